@@ -1,0 +1,131 @@
+/*
+ * ssd.h - C ABI of libssd, the MI355X (gfx950) implementation of the SSD
+ * (state space duality) core of a Mamba-2 layer.
+ *
+ * The operation. For every batch b and head h (B/C group g = floor(h*G/H)),
+ * token t = 0..T-1, with a P x N fp32 state s per (b, h):
+ *
+ *     a_t = exp(dt[b,t,h] * A[h])
+ *     s_t = a_t * s_{t-1} + dt[b,t,h] * x_t (outer) B[b,t,g,:]
+ *     y_t = s_t . C[b,t,g,:] + D[h] * x_t
+ *
+ * Sources (page title, section):
+ *  - "Transformers are SSMs" reading report (Mamba-2), section 2.2: the SSD
+ *    layer is a scalar-identity SSM, i.e. masked attention with the mask
+ *    L_ij = prod_{t=j+1..i} a_t (i >= j); section 3.1: the chunked (block)
+ *    algorithm, diagonal blocks as attention-like quadratic products, the
+ *    off-diagonal low-rank blocks through chunk states passed from each chunk
+ *    to the next.
+ *  - "Mamba 2 state space duality deep theory", section 4.1: the scan takes
+ *    (u, dt, C, A), with decay exp(dt * A) and input dt * u.
+ *  - "Mamba principles in depth", section 4.3: the scan's interface is
+ *    (x, delta, B, C, A, D); section 2.2: zero-order hold, Bbar = Delta * B.
+ *  - "SSM and Mamba survey", section 2: y = C h + D x.
+ *  - "Transformer vs Mamba/SSM: the next step of the architecture", core
+ *    concepts and why it matters: O(1)-per-token recurrent inference with a
+ *    fixed-size state (the decode step below).
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller. The library allocates
+ *    nothing and keeps no pointer after a call returns. All tensors are
+ *    contiguous, row-major, 16-byte aligned. Outputs must not alias inputs.
+ *  - A and D are float32 of shape (H). States are always float32.
+ *    X, dt, B, C and Y (x, y in the step) share one storage type `dtype`:
+ *    SSD_F32 (float32, computed in fp32) or SSD_BF16 (bfloat16 storage,
+ *    bf16 matrix-core products with fp32 accumulation and an fp32 state;
+ *    outputs rounded to nearest even).
+ *  - `stream` is a hipStream_t (NULL means the default stream). Work is
+ *    enqueued on it and the call returns without synchronising.
+ *  - Every argument check happens on the host before anything is enqueued;
+ *    a failed check returns its code and touches nothing. A HIP launch
+ *    error is returned as SSD_ERR_HIP; faults during execution surface at
+ *    the caller's next synchronisation. No call aborts, throws or prints.
+ *  - Calls are stateless and thread-safe.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+    SSD_ERR_SHAPE = 2,       /* a dimension is negative or zero where it may not be, or H % G != 0 */
+    SSD_ERR_UNSUPPORTED = 3, /* a valid shape this build has no kernel for (see below) */
+    SSD_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the query returns */
+    SSD_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
+    SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *ssd_status_string(ssd_status s);
+
+/*
+ * Workspace (device memory, caller-allocated) needed by ssd_chunk_scan_fwd
+ * for these arguments, in bytes. Returns 0 for an empty problem and
+ * (size_t)-1 if the arguments are invalid or unsupported.
+ */
+size_t ssd_chunk_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                          int64_t headdim, int64_t dstate, int64_t ngroups,
+                                          int64_t chunk, ssd_dtype dtype);
+
+/*
+ * Chunked forward over whole sequences, starting from a zero state.
+ *
+ *   X  (batch, seqlen, nheads, headdim)       dtype     input (the "value")
+ *   dt (batch, seqlen, nheads)                dtype     step sizes, already positive
+ *   A  (nheads)                               float32   per-head decay rate (A <= 0)
+ *   B  (batch, seqlen, ngroups, dstate)       dtype     input matrix (the "key")
+ *   C  (batch, seqlen, ngroups, dstate)       dtype     output matrix (the "query")
+ *   D  (nheads)                               float32   skip coefficient
+ *   chunk                                     chunk length Q of the block
+ *                                             decomposition: 64, 128 or 256
+ *   Y  (batch, seqlen, nheads, headdim)       dtype     output
+ *   final_state (batch, nheads, headdim, dstate) float32, or NULL to skip
+ *
+ * seqlen need not be a multiple of chunk (the last chunk is partial);
+ * seqlen == 0 writes a zero final state. When batch or seqlen is 0 nothing
+ * is read, and the input and Y pointers may be NULL. The result does not depend on
+ * chunk beyond rounding. Supported: headdim in {16, 32, 64, 128}, dstate in
+ * {16, 32, 64, 128, 256}, with the chunk's on-chip tiles fitting the 160 KB
+ * LDS of a compute unit (fp32 with headdim 128 and chunk 256 does not);
+ * other shapes return SSD_ERR_UNSUPPORTED. Each of X, Y, B, C per batch
+ * element and the workspace must be under 2 GiB.
+ */
+ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, int64_t chunk, void *Y,
+                              float *final_state, int64_t batch, int64_t seqlen,
+                              int64_t nheads, int64_t headdim, int64_t dstate,
+                              int64_t ngroups, ssd_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/*
+ * One recurrent decode step, updating `state` in place:
+ *
+ *   state (batch, nheads, headdim, dstate)    float32   in/out
+ *   x  (batch, nheads, headdim)               dtype
+ *   dt (batch, nheads)                        dtype
+ *   A, D (nheads)                             float32
+ *   B, C (batch, ngroups, dstate)             dtype
+ *   y  (batch, nheads, headdim)               dtype     output
+ *
+ * Supported: dstate in {4, 8, 16, 32, 64, 128, 256}. With batch == 0 nothing
+ * is read and the pointers may be NULL.
+ */
+ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,
+                    const void *C, const float *D, void *y, int64_t batch, int64_t nheads,
+                    int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                    void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

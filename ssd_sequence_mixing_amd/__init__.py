@@ -1,0 +1,176 @@
+"""Python binding of libssd, the gfx950 SSD core (argument marshalling only).
+
+Every function here forwards to the C ABI declared in include/ssd.h through
+ctypes: it checks that tensors are on the GPU and contiguous, allocates outputs
+and workspace with torch when the caller gives none, and passes raw device
+pointers plus the current HIP stream. All arithmetic runs in the library's
+kernels. There is no fallback: if libssd.so is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "SSD_F32", "SSD_BF16", "SSDError", "load", "lib_path", "ssd_status_string",
+    "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_step", "EXPORTS",
+]
+
+SSD_F32 = 0
+SSD_BF16 = 1
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libssd.so")
+_lib = None
+
+# Entry points include/ssd.h declares.
+EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_step")
+
+_V = ctypes.c_void_p
+_I = ctypes.c_int64
+
+
+class SSDError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ssd_status_string(code)} (status {code})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _hip_runtimes_mapped():
+    """Paths of every libamdhip64 mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def load():
+    """Loads libssd.so (built by ssd_sequence_mixing_amd.build); raises if absent.
+
+    torch is imported first on purpose: torch ships its own HIP runtime, whose
+    soname (libamdhip64.so.7) is the one libssd.so asks for, so loading torch
+    first makes libssd bind to that same runtime. Loading libssd first would
+    bring in a second HIP runtime (torch asks for its copy under another
+    name), and device memory and streams owned by one runtime are not valid
+    in the other."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FileNotFoundError(
+            f"{_LIB_PATH} is missing: build it with `python -m ssd_sequence_mixing_amd.build` "
+            "(or __graft_entry__.build()). There is no fallback path.")
+    import torch  # noqa: F401  (see the docstring: one HIP runtime per process)
+    lib = ctypes.CDLL(_LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are loaded in this process: {sorted(runtimes)}; "
+                           "import torch before loading libssd.so")
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_chunk_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_fwd_workspace_bytes.argtypes = [_I] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd.argtypes = [_V] * 6 + [_I, _V, _V] + [_I] * 6 + [ctypes.c_int, _V,
+                                                                          ctypes.c_size_t, _V]
+    lib.ssd_step.restype = ctypes.c_int
+    lib.ssd_step.argtypes = [_V] * 8 + [_I] * 5 + [ctypes.c_int, _V]
+    _lib = lib
+    return lib
+
+
+def ssd_status_string(code: int) -> str:
+    return load().ssd_status_string(int(code)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"unsupported storage dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                       dtype: int) -> int:
+    n = load().ssd_chunk_scan_fwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                                  chunk, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise SSDError(3, "ssd_chunk_scan_fwd_workspace_bytes")
+    return int(n)
+
+
+def ssd_chunk_scan_fwd(X, dt, A, B, C, D, chunk: int, Y=None, final_state=None, *,
+                       want_final: bool = True, workspace=None, stream=None):
+    """Chunked SSD forward. Shapes: X (b, T, H, P), dt (b, T, H), A/D (H,) fp32,
+    B/C (b, T, G, N); X/dt/B/C share one storage dtype (bf16 or fp32).
+
+    Returns (Y, final_state); final_state is None when want_final is False and
+    none was passed in."""
+    import torch
+    lib = load()
+    bsz, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=X.device)
+    need = ssd_chunk_scan_fwd_workspace_bytes(bsz, T, H, P, N, G, chunk, code)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_fwd(_ptr(X), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), chunk,
+                                _ptr(Y), _ptr(final_state), bsz, T, H, P, N, G, code,
+                                _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd")
+    return Y, final_state
+
+
+def ssd_step(state, x, dt, A, B, C, D, y=None, *, stream=None):
+    """One decode step; `state` (b, H, P, N) fp32 is updated in place. Returns y."""
+    import torch
+    lib = load()
+    bsz, H, P, N = state.shape
+    G = B.shape[1]
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.ssd_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(y),
+                      bsz, H, P, N, G, code, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_step")
+    return y
+
+
+def raw_call(name: str, *args) -> int:
+    """Calls a C entry point with raw integer/pointer arguments; returns its status."""
+    return int(getattr(load(), name)(*args))

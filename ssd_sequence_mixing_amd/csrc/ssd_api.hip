@@ -1,0 +1,160 @@
+// C ABI of libssd: argument checks, workspace layout and launch order.
+// Every check runs on the host before anything is enqueued.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssd_common.h"
+#include "ssd_internal.h"
+
+namespace {
+
+using ssd::FwdArgs;
+
+constexpr int64_t kTwoGiB = (int64_t)1 << 31;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t esize(ssd_dtype d) { return d == SSD_BF16 ? 2 : 4; }
+
+bool valid_dtype(int d) { return d == SSD_F32 || d == SSD_BF16; }
+
+bool in_set(int64_t v, std::initializer_list<int64_t> s) {
+    for (int64_t x : s)
+        if (v == x) return true;
+    return false;
+}
+
+int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+struct FwdLayout {
+    int64_t nC, Tpad, cs_bytes, g_bytes, total;
+};
+
+// Shape checks shared by the workspace query and the forward call.
+ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                           int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
+                           FwdLayout *lay) {
+    if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return SSD_ERR_SHAPE;
+    if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
+    if (!in_set(chunk, {64, 128, 256})) return SSD_ERR_UNSUPPORTED;
+    if (!in_set(headdim, {16, 32, 64, 128}) || !in_set(dstate, {16, 32, 64, 128, 256}))
+        return SSD_ERR_UNSUPPORTED;
+    const int lds = ssd::fwd_lds_bytes((ssd_dtype)dtype, chunk, headdim, dstate);
+    if (lds < 0 || lds > ssd::kMaxLds) return SSD_ERR_UNSUPPORTED;
+    const int64_t es = esize((ssd_dtype)dtype);
+    // 32-bit buffer offsets: every per-batch slab and the C B^T buffer stay under 2 GiB
+    if (seqlen > kTwoGiB || nheads > 65536) return SSD_ERR_UNSUPPORTED;
+    if (seqlen * nheads * headdim * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    if (seqlen * ngroups * dstate * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    if (seqlen * nheads * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    const int64_t nC = (seqlen + chunk - 1) / chunk;
+    const int64_t Tpad = nC * chunk;
+    const int64_t nt = chunk / 64, np = nt * (nt + 1) / 2;
+    lay->nC = nC;
+    lay->Tpad = Tpad;
+    lay->cs_bytes = align256(batch * nheads * Tpad * 4);
+    lay->g_bytes = align256(batch * ngroups * nC * np * 4096 * es);
+    if (lay->g_bytes >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    if (batch * nheads > (int64_t)INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
+    lay->total = (batch == 0 || seqlen == 0) ? 0 : 2 * lay->cs_bytes + lay->g_bytes;
+    return SSD_OK;
+}
+
+__global__ void k_fill_zero(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ssd_status_string(ssd_status s) {
+    switch (s) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: invalid dimensions";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: no kernel for this configuration";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+        case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer not 16-byte aligned";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime error at launch";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+size_t ssd_chunk_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                          int64_t headdim, int64_t dstate, int64_t ngroups,
+                                          int64_t chunk, ssd_dtype dtype) {
+    FwdLayout lay;
+    if (check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay) !=
+        SSD_OK)
+        return (size_t)-1;
+    return (size_t)lay.total;
+}
+
+ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, int64_t chunk, void *Y,
+                              float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
+                              int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    const bool empty = (batch == 0 || seqlen == 0);
+    // an empty problem reads no input, so its input pointers may be NULL
+    if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
+    FwdLayout lay;
+    const ssd_status st =
+        check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
+    if (st != SSD_OK) return st;
+    if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(D) || !aligned16(Y) || (final_state && !aligned16(final_state)))
+        return SSD_ERR_ALIGN;
+    if (lay.total > 0) {
+        if (!workspace || workspace_bytes < (size_t)lay.total) return SSD_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return SSD_ERR_ALIGN;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (batch == 0) return SSD_OK;
+    if (seqlen == 0) {
+        if (final_state) {
+            const int64_t n = batch * nheads * headdim * dstate;
+            if (ssd::launch(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), s, final_state,
+                            n) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
+        return SSD_OK;
+    }
+    FwdArgs f;
+    f.X = X; f.dt = dt; f.B = B; f.C = C; f.A = A; f.D = D; f.Y = Y; f.final_state = final_state;
+    f.batch = batch; f.T = seqlen; f.H = nheads; f.P = headdim; f.N = dstate; f.G = ngroups;
+    f.Q = chunk; f.nC = lay.nC; f.Tpad = lay.Tpad; f.dtype = dtype;
+    char *ws = static_cast<char *>(workspace);
+    f.cs2 = reinterpret_cast<float *>(ws);
+    f.dtf = reinterpret_cast<float *>(ws + lay.cs_bytes);
+    f.Gbuf = ws + 2 * lay.cs_bytes;
+    f.g_bytes = lay.g_bytes;
+    return ssd::launch_fwd(f, s);
+}
+
+ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,
+                    const void *C, const float *D, void *y, int64_t batch, int64_t nheads,
+                    int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                    void *stream) {
+    if (batch != 0 && (!state || !x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
+    if (!valid_dtype((int)dtype)) return SSD_ERR_UNSUPPORTED;
+    if (batch < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0) return SSD_ERR_SHAPE;
+    if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
+    if (!in_set(dstate, {4, 8, 16, 32, 64, 128, 256})) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(state) || !aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
+        !aligned16(C) || !aligned16(D) || !aligned16(y))
+        return SSD_ERR_ALIGN;
+    if (batch == 0) return SSD_OK;
+    const int64_t rows = batch * nheads * headdim;
+    if (rows / 16 > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;
+    ssd::StepArgs a;
+    a.state = state; a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
+    a.batch = batch; a.H = nheads; a.P = headdim; a.N = dstate; a.G = ngroups; a.dtype = dtype;
+    return ssd::launch_step(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+"""CPU tests of the C ABI: the library loads, exports every declared entry point,
+and every argument check returns its status before anything touches a GPU.
+
+The pointers below are fake (aligned integers): each call is chosen so that a
+host-side check fails first, so no kernel is ever launched from these tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import ssd_sequence_mixing_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, ENULL, ESHAPE, EUNSUP, EWS, EALIGN, EHIP = range(7)
+F32, BF16 = ssd.SSD_F32, ssd.SSD_BF16
+P16 = 0x10000  # a fake, 16-byte-aligned device address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(ssd.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ssd.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_library_exports_with_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", ssd.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared_functions():
+        assert name in syms, name
+
+
+def test_status_strings():
+    for code in range(7):
+        s = ssd.ssd_status_string(code)
+        assert s.startswith("SSD_OK" if code == 0 else "SSD_ERR")
+    assert "UNKNOWN" in ssd.ssd_status_string(99)
+
+
+def ws(*a):
+    return ssd.load().ssd_chunk_scan_fwd_workspace_bytes(*a)
+
+
+def test_workspace_query():
+    big = ctypes.c_size_t(-1).value
+    n = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
+    # two fp32 (b, H, Tpad) arrays plus the bf16 C B^T lower tiles (10 per chunk)
+    assert n == 2 * 4 * 64 * 2048 * 4 + 4 * 1 * 8 * 10 * 4096 * 2
+    assert ws(0, 2048, 64, 64, 128, 1, 256, BF16) == 0
+    assert ws(4, 0, 64, 64, 128, 1, 256, BF16) == 0
+    assert ws(4, 2048, 64, 64, 128, 3, 256, BF16) == big      # H % G
+    assert ws(4, 2048, 64, 64, 128, 1, 32, BF16) == big       # chunk
+    assert ws(4, 2048, 64, 48, 128, 1, 256, BF16) == big      # headdim
+    assert ws(4, 2048, 64, 64, 96, 1, 256, BF16) == big       # dstate
+    assert ws(1, 256, 2, 128, 256, 1, 256, F32) == big        # fp32 tiles exceed LDS
+    assert ws(4, 2048, 64, 64, 128, 1, 256, 7) == big         # dtype
+
+
+def fwd(X=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, chunk=256, Y=P16, fin=P16, batch=4, T=2048,
+        H=64, P=64, N=128, G=1, dtype=BF16, wsp=P16 * 16, wsb=1 << 40, stream=None):
+    return ssd.raw_call("ssd_chunk_scan_fwd", X, dt, A, B, C, D, chunk, Y, fin, batch, T, H, P, N,
+                        G, dtype, wsp, wsb, stream)
+
+
+@pytest.mark.parametrize("field", ["X", "dt", "A", "B", "C", "D", "Y"])
+def test_fwd_null(field):
+    assert fwd(**{field: None}) == ENULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ESHAPE), (dict(T=-5), ESHAPE), (dict(H=0), ESHAPE), (dict(P=0), ESHAPE),
+    (dict(N=-2), ESHAPE), (dict(G=0), ESHAPE), (dict(H=64, G=3), ESHAPE),
+    (dict(chunk=32), EUNSUP), (dict(chunk=100), EUNSUP), (dict(chunk=512), EUNSUP),
+    (dict(P=48), EUNSUP), (dict(N=100), EUNSUP), (dict(dtype=5), EUNSUP),
+    (dict(dtype=F32, P=128, N=256, chunk=256), EUNSUP),
+    (dict(T=1 << 40), EUNSUP),
+])
+def test_fwd_shape_checks(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("field", ["X", "dt", "A", "B", "C", "D", "Y", "fin"])
+def test_fwd_alignment(field):
+    assert fwd(**{field: P16 + 4}) == EALIGN
+
+
+def test_fwd_workspace_checks():
+    need = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
+    assert fwd(wsp=None) == EWS
+    assert fwd(wsb=need - 1) == EWS
+    assert fwd(wsp=P16 + 16, wsb=need) == EALIGN  # workspace wants 256-byte alignment
+
+
+def test_fwd_empty_batch_returns_ok_without_work():
+    assert fwd(batch=0, wsp=None, wsb=0) == OK
+
+
+def step(state=P16, x=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, y=P16, batch=256, H=64, P=64,
+         N=128, G=1, dtype=BF16, stream=None):
+    return ssd.raw_call("ssd_step", state, x, dt, A, B, C, D, y, batch, H, P, N, G, dtype, stream)
+
+
+@pytest.mark.parametrize("field", ["state", "x", "dt", "A", "B", "C", "D", "y"])
+def test_step_null(field):
+    assert step(**{field: None}) == ENULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ESHAPE), (dict(H=0), ESHAPE), (dict(P=0), ESHAPE), (dict(N=0), ESHAPE),
+    (dict(G=0), ESHAPE), (dict(H=6, G=4), ESHAPE), (dict(N=12), EUNSUP), (dict(N=512), EUNSUP),
+    (dict(dtype=9), EUNSUP),
+])
+def test_step_shape_checks(kw, code):
+    assert step(**kw) == code
+
+
+@pytest.mark.parametrize("field", ["state", "x", "dt", "A", "B", "C", "D", "y"])
+def test_step_alignment(field):
+    assert step(**{field: P16 + 2}) == EALIGN
+
+
+def test_step_empty_batch():
+    assert step(batch=0) == OK
+
+
+def test_single_hip_runtime_in_process():
+    # torch's HIP runtime and libssd's must be the same library
+    ssd.load()
+    assert len(ssd._hip_runtimes_mapped()) == 1, ssd._hip_runtimes_mapped()

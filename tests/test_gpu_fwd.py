@@ -1,0 +1,175 @@
+"""GPU parity of ssd_chunk_scan_fwd against the oracle (through the C ABI).
+
+Tolerances: max|GPU - oracle| / max|oracle| <= 2e-2 with bf16 storage and
+<= 1e-4 with fp32 storage, checked separately on Y, on Y with D = 0 (the SSM
+part alone, which the skip term would otherwise dominate) and on the final
+state.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+import ssd_inputs as si
+from tests.gpu_util import TOL, gpu_fwd, log, oracle_fwd, rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check_full(ssd, cfg, chunk=None, tag=""):
+    chunk = chunk or cfg.chunk
+    log(f"[fwd full] {cfg.name}{tag} chunk={chunk} shape=(b{cfg.batch},T{cfg.seqlen},H{cfg.nheads},"
+        f"P{cfg.headdim},N{cfg.dstate},G{cfg.ngroups}) {cfg.dtype}")
+    inp = si.make_fwd_inputs(cfg)
+    tol = TOL[cfg.dtype]
+    Yg, Fg = gpu_fwd(ssd, inp, chunk)
+    Yr, Fr = oracle_fwd(inp, cfg.ngroups)
+    Yg0, Fg0 = gpu_fwd(ssd, inp, chunk, D_zero=True)
+    Yr0, _ = oracle_fwd(inp, cfg.ngroups, D_zero=True)
+    e = (rel(Yg, Yr), rel(Yg0, Yr0), rel(Fg, Fr))
+    log(f"    rel err Y={e[0]:.2e} Y(D=0)={e[1]:.2e} final={e[2]:.2e} (tol {tol})")
+    assert np.all(np.isfinite(Yg)) and np.all(np.isfinite(Fg))
+    assert e[0] <= tol and e[1] <= tol and e[2] <= tol, e
+    assert np.array_equal(Fg, Fg0)  # the final state does not depend on D
+    return e
+
+
+def test_tiny_f32_workload(ssd):
+    check_full(ssd, si.CONFIGS["tiny_f32"])
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_f32_chunk_invariance_ragged(ssd, chunk):
+    cfg = dataclasses.replace(si.CONFIGS["tiny_f32"], name="f32_ragged", batch=2, seqlen=300,
+                              nheads=4, ngroups=2, seed=21)
+    check_full(ssd, cfg, chunk=chunk)
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_bf16_chunk_invariance_ragged(ssd, chunk):
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="bf16_ragged", batch=2, seqlen=600,
+                              nheads=4, seed=22)
+    check_full(ssd, cfg, chunk=chunk)
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (32, 32), (64, 64), (128, 128), (64, 256), (128, 64)])
+def test_bf16_head_and_state_sizes(ssd, P, N):
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name=f"bf16_P{P}_N{N}", batch=1,
+                              seqlen=320, nheads=4, headdim=P, dstate=N, ngroups=2, seed=23)
+    check_full(ssd, cfg, chunk=128)
+
+
+@pytest.mark.parametrize("P,N", [(32, 64), (64, 128)])
+def test_f32_head_and_state_sizes(ssd, P, N):
+    cfg = dataclasses.replace(si.CONFIGS["tiny_f32"], name=f"f32_P{P}_N{N}", batch=1, seqlen=200,
+                              nheads=2, headdim=P, dstate=N, seed=24)
+    check_full(ssd, cfg, chunk=64)
+
+
+@pytest.mark.parametrize("name", ["s2_a_zero", "s3_ragged", "s4_groups", "s5_large_dt"])
+def test_stress_workloads(ssd, name):
+    check_full(ssd, si.STRESS[name])
+
+
+def test_short_sequences(ssd):
+    for T in (1, 2, 63, 65):
+        cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name=f"T{T}", batch=3, seqlen=T,
+                                  nheads=2, seed=30 + T)
+        check_full(ssd, cfg, chunk=64)
+
+
+def check_sampled(ssd, cfg, batches, heads):
+    log(f"[fwd sampled] {cfg.name} full shape, (b,h) samples {[(b, h) for b in batches for h in heads]}")
+    inp = si.make_fwd_inputs(cfg)
+    Yg, Fg = gpu_fwd(ssd, inp, cfg.chunk)
+    Yg0, _ = gpu_fwd(ssd, inp, cfg.chunk, D_zero=True)
+    ref = oracle_fwd(inp, cfg.ngroups, batches=batches, heads=heads)
+    ref0 = oracle_fwd(inp, cfg.ngroups, D_zero=True, batches=batches, heads=heads)
+    tol = TOL[cfg.dtype]
+    worst = [0.0, 0.0, 0.0]
+    for (b, h), (Yr, Fr) in ref.items():
+        e = (rel(Yg[b, :, h], Yr), rel(Yg0[b, :, h], ref0[(b, h)][0]), rel(Fg[b, h], Fr))
+        worst = [max(x, y) for x, y in zip(worst, e)]
+        assert e[0] <= tol and e[1] <= tol and e[2] <= tol, ((b, h), e)
+    assert np.all(np.isfinite(Yg))
+    log(f"    worst rel err Y={worst[0]:.2e} Y(D=0)={worst[1]:.2e} final={worst[2]:.2e} (tol {tol})")
+
+
+def test_full_size_125m_layer(ssd):
+    check_sampled(ssd, si.CONFIGS["l125m_bf16"], batches=[0, 7], heads=[0, 11, 23])
+
+
+def test_full_size_1p3b_layer(ssd):
+    check_sampled(ssd, si.CONFIGS["l1p3b_bf16"], batches=[0, 3], heads=[0, 31, 63])
+
+
+def test_full_size_long_16k(ssd):
+    # heads from four different groups (G = 8, eight heads per group)
+    check_sampled(ssd, si.CONFIGS["long16k_bf16"], batches=[0], heads=[0, 9, 36, 63])
+
+
+def test_long_memory_stress_full_size(ssd):
+    check_sampled(ssd, si.STRESS["s1_long_memory"], batches=[1], heads=[5, 60])
+
+
+def test_group_mapping_probe(ssd):
+    """G = 8: B zero in every group but k, so only heads floor(h*G/H) == k get an
+    SSM term; the others must equal D x to the output's rounding."""
+    import torch
+    cfg = si.STRESS["s4_groups"]
+    inp = si.make_fwd_inputs(cfg)
+    H, G = cfg.nheads, cfg.ngroups
+    k = 5
+    Bm = inp["B"].copy()
+    Bm[:, :, [q for q in range(G) if q != k], :] = 0
+    X, dt, C = (to_dev(inp[n]) for n in ("X", "dt", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    Y, F = ssd.ssd_chunk_scan_fwd(X, dt, A, to_dev(Bm), C, D, cfg.chunk)
+    torch.cuda.synchronize()
+    Y = Y.float().cpu().numpy()
+    F = F.cpu().numpy()
+    skip = (inp["X32"] * inp["D"][None, None, :, None])
+    for h in range(H):
+        dev = np.max(np.abs(Y[:, :, h] - skip[:, :, h]))
+        if (h * G) // H == k:
+            assert dev > 1e-3 and np.max(np.abs(F[:, h])) > 1e-3, h
+        else:
+            assert not np.any(F[:, h]), h
+            assert dev <= 2.0 ** -8 * np.max(np.abs(skip[:, :, h])) + 1e-30, (h, dev)
+
+
+def test_determinism_and_causality(ssd):
+    import torch
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="det", batch=2, seqlen=1000, nheads=8,
+                              seed=40)
+    inp = si.make_fwd_inputs(cfg)
+    log("[fwd] determinism and causality, T=1000")
+    X, dt, B, C = (to_dev(inp[k]) for k in ("X", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    Y1, F1 = ssd.ssd_chunk_scan_fwd(X, dt, A, B, C, D, 256)
+    Y2, F2 = ssd.ssd_chunk_scan_fwd(X, dt, A, B, C, D, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(F1, F2)
+    t0 = 613
+    X2, B2 = X.clone(), B.clone()
+    X2[:, t0:] = X2[:, t0:] * -3 + 1
+    B2[:, t0:] = B2[:, t0:] * 2
+    Y3, _ = ssd.ssd_chunk_scan_fwd(X2, dt, A, B2, C, D, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1[:, :t0], Y3[:, :t0])
+    assert not torch.equal(Y1[:, t0:], Y3[:, t0:])
+
+
+def test_empty_sequence_zero_final_state(ssd):
+    import torch
+    X = torch.zeros((2, 0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    dt = torch.zeros((2, 0, 4), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((2, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    A = torch.full((4,), -1.0, device="cuda")
+    D = torch.ones(4, device="cuda")
+    F = torch.full((2, 4, 64, 128), 7.0, device="cuda")
+    Y, F = ssd.ssd_chunk_scan_fwd(X, dt, A, B, B, D, 256, final_state=F)
+    torch.cuda.synchronize()
+    assert Y.shape == X.shape and not torch.any(F)
