@@ -107,6 +107,38 @@ ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, con
                               size_t workspace_bytes, void *stream);
 
 /*
+ * The same forward in its two phases, for callers that time them apart or
+ * run several walks over one preparation. ssd_chunk_scan_fwd is exactly
+ * ssd_chunk_scan_prepare followed by ssd_chunk_scan_walk with no initial
+ * state. Arguments mean what they mean above; both calls must get the same
+ * dimensions, chunk, dtype and workspace, and the walk must see the B and C
+ * the preparation saw.
+ *
+ * ssd_chunk_scan_prepare: per chunk, the chunk-local prefix sums of
+ * dt*A (the log-decays of the mask L_ij = prod_{t=j+1..i} a_t, reading
+ * report section 2.2) and the products C B^T of its diagonal block, written
+ * to the workspace (section 3.1: the attention-like diagonal blocks).
+ *
+ * ssd_chunk_scan_walk: walks the chunks in order, passing the state from
+ * each chunk to the next (section 3.1), and writes Y and final_state.
+ * initial_state (batch, nheads, headdim, dstate) float32 is the state before
+ * token 0, or NULL for zero; it lets a sequence be resumed from a carried
+ * state (the final state of an earlier call, or a decode state).
+ */
+ssd_status ssd_chunk_scan_prepare(const void *dt, const float *A, const void *B, const void *C,
+                                  int64_t chunk, int64_t batch, int64_t seqlen, int64_t nheads,
+                                  int64_t headdim, int64_t dstate, int64_t ngroups,
+                                  ssd_dtype dtype, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+ssd_status ssd_chunk_scan_walk(const void *X, const void *B, const void *C, const float *D,
+                               const float *initial_state, int64_t chunk, void *Y,
+                               float *final_state, int64_t batch, int64_t seqlen,
+                               int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                               ssd_dtype dtype, const void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * One recurrent decode step, updating `state` in place:
  *
  *   state (batch, nheads, headdim, dstate)    float32   in/out

@@ -14,7 +14,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "load", "lib_path", "ssd_status_string",
-    "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_step", "EXPORTS",
+    "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_chunk_scan_prepare",
+    "ssd_chunk_scan_walk", "ssd_step", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -24,7 +25,8 @@ _LIB_PATH = os.path.join(_PKG, "libssd.so")
 _lib = None
 
 # Entry points include/ssd.h declares.
-EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_step")
+EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd",
+           "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step")
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -82,6 +84,11 @@ def load():
     lib.ssd_chunk_scan_fwd.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd.argtypes = [_V] * 6 + [_I, _V, _V] + [_I] * 6 + [ctypes.c_int, _V,
                                                                           ctypes.c_size_t, _V]
+    lib.ssd_chunk_scan_prepare.restype = ctypes.c_int
+    lib.ssd_chunk_scan_prepare.argtypes = [_V] * 4 + [_I] * 7 + [ctypes.c_int, _V, ctypes.c_size_t, _V]
+    lib.ssd_chunk_scan_walk.restype = ctypes.c_int
+    lib.ssd_chunk_scan_walk.argtypes = [_V] * 5 + [_I, _V, _V] + [_I] * 6 + [ctypes.c_int, _V,
+                                                                           ctypes.c_size_t, _V]
     lib.ssd_step.restype = ctypes.c_int
     lib.ssd_step.argtypes = [_V] * 8 + [_I] * 5 + [ctypes.c_int, _V]
     _lib = lib
@@ -152,6 +159,50 @@ def ssd_chunk_scan_fwd(X, dt, A, B, C, D, chunk: int, Y=None, final_state=None, 
                                 _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd")
+    return Y, final_state
+
+
+def _workspace(workspace, need, device):
+    import torch
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def ssd_chunk_scan_prepare(dt, A, B, C, chunk: int, headdim: int, *, workspace=None, stream=None):
+    """Phase 1 of the forward: fills and returns the workspace."""
+    lib = load()
+    bsz, T, H = dt.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(dt)
+    need = ssd_chunk_scan_fwd_workspace_bytes(bsz, T, H, headdim, N, G, chunk, code)
+    workspace, nbytes = _workspace(workspace, need, dt.device)
+    st = lib.ssd_chunk_scan_prepare(_ptr(dt), _ptr(A), _ptr(B), _ptr(C), chunk, bsz, T, H, headdim,
+                                    N, G, code, _ptr(workspace), nbytes, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_prepare")
+    return workspace
+
+
+def ssd_chunk_scan_walk(X, B, C, D, workspace, chunk: int, initial_state=None, Y=None,
+                        final_state=None, *, want_final: bool = True, stream=None):
+    """Phase 2 of the forward: the chunk walk over a prepared workspace."""
+    import torch
+    lib = load()
+    bsz, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=X.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.ssd_chunk_scan_walk(_ptr(X), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state), chunk,
+                                 _ptr(Y), _ptr(final_state), bsz, T, H, P, N, G, code,
+                                 _ptr(workspace), nbytes, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_walk")
     return Y, final_state
 
 

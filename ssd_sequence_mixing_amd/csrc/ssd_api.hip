@@ -3,6 +3,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "ssd_common.h"
 #include "ssd_internal.h"
 
@@ -30,7 +32,7 @@ struct FwdLayout {
     int64_t nC, Tpad, cs_bytes, g_bytes, total;
 };
 
-// Shape checks shared by the workspace query and the forward call.
+// Shape checks shared by the workspace query and the forward entry points.
 ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
                            FwdLayout *lay) {
@@ -62,9 +64,40 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     return SSD_OK;
 }
 
-__global__ void k_fill_zero(float *p, int64_t n) {
+ssd_status check_workspace(const FwdLayout &lay, const void *workspace, size_t workspace_bytes) {
+    if (lay.total > 0) {
+        if (!workspace || workspace_bytes < (size_t)lay.total) return SSD_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return SSD_ERR_ALIGN;
+    }
+    return SSD_OK;
+}
+
+FwdArgs make_args(const FwdLayout &lay, int64_t batch, int64_t seqlen, int64_t nheads,
+                  int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, ssd_dtype dtype,
+                  const void *workspace) {
+    FwdArgs f = {};
+    f.batch = batch; f.T = seqlen; f.H = nheads; f.P = headdim; f.N = dstate; f.G = ngroups;
+    f.Q = chunk; f.nC = lay.nC; f.Tpad = lay.Tpad; f.dtype = dtype;
+    char *ws = static_cast<char *>(const_cast<void *>(workspace));
+    f.cs2 = reinterpret_cast<float *>(ws);
+    f.dtf = reinterpret_cast<float *>(ws + lay.cs_bytes);
+    f.Gbuf = ws + 2 * lay.cs_bytes;
+    f.g_bytes = lay.g_bytes;
+    return f;
+}
+
+__global__ void k_fill_state(float *dst, const float *src, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.f;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+// Empty sequence: the final state is the initial state (zero when none).
+ssd_status empty_final_state(float *final_state, const float *init, int64_t n, hipStream_t s) {
+    if (!final_state || n == 0) return SSD_OK;
+    return ssd::launch(k_fill_state, dim3((unsigned)((n + 255) / 256)), dim3(256), s, final_state,
+                       init, n) == hipSuccess
+               ? SSD_OK
+               : SSD_ERR_HIP;
 }
 
 }  // namespace
@@ -94,6 +127,50 @@ size_t ssd_chunk_scan_fwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t
     return (size_t)lay.total;
 }
 
+ssd_status ssd_chunk_scan_prepare(const void *dt, const float *A, const void *B, const void *C,
+                                  int64_t chunk, int64_t batch, int64_t seqlen, int64_t nheads,
+                                  int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    const bool empty = (batch == 0 || seqlen == 0);
+    if (!empty && (!dt || !A || !B || !C)) return SSD_ERR_NULL;
+    FwdLayout lay;
+    ssd_status st =
+        check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
+    if (st != SSD_OK) return st;
+    if (!aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C)) return SSD_ERR_ALIGN;
+    if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
+    if (empty) return SSD_OK;
+    FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          workspace);
+    f.dt = dt; f.A = A; f.B = B; f.C = C;
+    return ssd::launch_prepare(f, reinterpret_cast<hipStream_t>(stream));
+}
+
+ssd_status ssd_chunk_scan_walk(const void *X, const void *B, const void *C, const float *D,
+                               const float *initial_state, int64_t chunk, void *Y,
+                               float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
+                               int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                               const void *workspace, size_t workspace_bytes, void *stream) {
+    const bool empty = (batch == 0 || seqlen == 0);
+    if (!empty && (!X || !B || !C || !D || !Y)) return SSD_ERR_NULL;
+    FwdLayout lay;
+    ssd_status st =
+        check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
+    if (st != SSD_OK) return st;
+    if (!aligned16(X) || !aligned16(B) || !aligned16(C) || !aligned16(D) || !aligned16(Y) ||
+        !aligned16(initial_state) || !aligned16(final_state))
+        return SSD_ERR_ALIGN;
+    if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (batch == 0) return SSD_OK;
+    if (seqlen == 0)
+        return empty_final_state(final_state, initial_state, batch * nheads * headdim * dstate, s);
+    FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          workspace);
+    f.X = X; f.B = B; f.C = C; f.D = D; f.Y = Y; f.init = initial_state; f.final_state = final_state;
+    return ssd::launch_walk(f, s);
+}
+
 ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, const void *B,
                               const void *C, const float *D, int64_t chunk, void *Y,
                               float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
@@ -103,37 +180,22 @@ ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, con
     // an empty problem reads no input, so its input pointers may be NULL
     if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
     FwdLayout lay;
-    const ssd_status st =
+    ssd_status st =
         check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
     if (st != SSD_OK) return st;
     if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
-        !aligned16(D) || !aligned16(Y) || (final_state && !aligned16(final_state)))
+        !aligned16(D) || !aligned16(Y) || !aligned16(final_state))
         return SSD_ERR_ALIGN;
-    if (lay.total > 0) {
-        if (!workspace || workspace_bytes < (size_t)lay.total) return SSD_ERR_WORKSPACE;
-        if (((uintptr_t)workspace & 255u) != 0) return SSD_ERR_ALIGN;
-    }
+    if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (batch == 0) return SSD_OK;
-    if (seqlen == 0) {
-        if (final_state) {
-            const int64_t n = batch * nheads * headdim * dstate;
-            if (ssd::launch(k_fill_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), s, final_state,
-                            n) != hipSuccess)
-                return SSD_ERR_HIP;
-        }
-        return SSD_OK;
-    }
-    FwdArgs f;
-    f.X = X; f.dt = dt; f.B = B; f.C = C; f.A = A; f.D = D; f.Y = Y; f.final_state = final_state;
-    f.batch = batch; f.T = seqlen; f.H = nheads; f.P = headdim; f.N = dstate; f.G = ngroups;
-    f.Q = chunk; f.nC = lay.nC; f.Tpad = lay.Tpad; f.dtype = dtype;
-    char *ws = static_cast<char *>(workspace);
-    f.cs2 = reinterpret_cast<float *>(ws);
-    f.dtf = reinterpret_cast<float *>(ws + lay.cs_bytes);
-    f.Gbuf = ws + 2 * lay.cs_bytes;
-    f.g_bytes = lay.g_bytes;
-    return ssd::launch_fwd(f, s);
+    if (seqlen == 0)
+        return empty_final_state(final_state, nullptr, batch * nheads * headdim * dstate, s);
+    FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          workspace);
+    f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y; f.final_state = final_state;
+    if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
+    return ssd::launch_walk(f, s);
 }
 
 ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A, const void *B,

@@ -473,29 +473,33 @@ __global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// host-side launch of the three kernels for one instantiation
+// host-side launches for one instantiation
 // ---------------------------------------------------------------------------
+template <typename TI, int Q, int N>
+static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
+    const int nC = (int)f.nC;
+    const int hblocks = (int)((f.H + kCumsumHeads - 1) / kCumsumHeads);
+    if (launch(k_dt_cumsum<TI, Q>, dim3((unsigned)(f.batch * hblocks * nC)), dim3(256), s,
+               (const TI *)f.dt, f.A, f.cs2, f.dtf, (int)f.T, (int)f.H, nC, (int)f.Tpad) != hipSuccess)
+        return SSD_ERR_HIP;
+    constexpr int NT = Q / 64;
+    if (launch(k_chunk_cb<TI, Q, N>, dim3((unsigned)(f.batch * nC * f.G * NT)), dim3(256), s,
+               (const TI *)f.B, (const TI *)f.C, (TI *)f.Gbuf, (int)f.T, (int)f.G, nC,
+               (uint32_t)f.g_bytes) != hipSuccess)
+        return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
 template <typename TI, int Q, int P, int N>
-static ssd_status run_fwd(const FwdArgs &f, hipStream_t s) {
+static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
     using Cfg = WalkCfg<TI, Q, P, N>;
     if constexpr (!Cfg::kFits) {
         return SSD_ERR_UNSUPPORTED;
     } else {
-        const int nC = (int)f.nC;
-        const int hblocks = (int)((f.H + kCumsumHeads - 1) / kCumsumHeads);
-        if (launch(k_dt_cumsum<TI, Q>, dim3((unsigned)(f.batch * hblocks * nC)), dim3(256), s,
-                   (const TI *)f.dt, f.A, f.cs2, f.dtf, (int)f.T, (int)f.H, nC,
-                   (int)f.Tpad) != hipSuccess)
-            return SSD_ERR_HIP;
-        constexpr int NT = Q / 64;
-        if (launch(k_chunk_cb<TI, Q, N>, dim3((unsigned)(f.batch * nC * f.G * NT)), dim3(256), s,
-                   (const TI *)f.B, (const TI *)f.C, (TI *)f.Gbuf, (int)f.T, (int)f.G, nC,
-                   (uint32_t)f.g_bytes) != hipSuccess)
-            return SSD_ERR_HIP;
         WalkArgs wa;
         wa.X = f.X; wa.B = f.B; wa.C = f.C; wa.Y = f.Y; wa.Gbuf = f.Gbuf;
-        wa.cs2 = f.cs2; wa.dtf = f.dtf; wa.D = f.D; wa.init = nullptr; wa.final_state = f.final_state;
-        wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = nC;
+        wa.cs2 = f.cs2; wa.dtf = f.dtf; wa.D = f.D; wa.init = f.init; wa.final_state = f.final_state;
+        wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
         wa.Tpad = (int)f.Tpad; wa.g_bytes = (uint32_t)f.g_bytes;
         return launch(k_chunk_walk<TI, Q, P, N>, dim3((unsigned)(f.batch * f.H)), dim3(256), s, wa) ==
                        hipSuccess
@@ -505,40 +509,56 @@ static ssd_status run_fwd(const FwdArgs &f, hipStream_t s) {
 }
 
 template <typename TI, int Q, int P>
-static ssd_status dispatch_n(const FwdArgs &f, hipStream_t s) {
+static ssd_status walk_n(const FwdArgs &f, hipStream_t s) {
     switch (f.N) {
-        case 16: return run_fwd<TI, Q, P, 16>(f, s);
-        case 32: return run_fwd<TI, Q, P, 32>(f, s);
-        case 64: return run_fwd<TI, Q, P, 64>(f, s);
-        case 128: return run_fwd<TI, Q, P, 128>(f, s);
-        case 256: return run_fwd<TI, Q, P, 256>(f, s);
+        case 16: return run_walk<TI, Q, P, 16>(f, s);
+        case 32: return run_walk<TI, Q, P, 32>(f, s);
+        case 64: return run_walk<TI, Q, P, 64>(f, s);
+        case 128: return run_walk<TI, Q, P, 128>(f, s);
+        case 256: return run_walk<TI, Q, P, 256>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
 template <typename TI, int Q>
-static ssd_status dispatch_p(const FwdArgs &f, hipStream_t s) {
+static ssd_status walk_p(const FwdArgs &f, hipStream_t s) {
     switch (f.P) {
-        case 16: return dispatch_n<TI, Q, 16>(f, s);
-        case 32: return dispatch_n<TI, Q, 32>(f, s);
-        case 64: return dispatch_n<TI, Q, 64>(f, s);
-        case 128: return dispatch_n<TI, Q, 128>(f, s);
+        case 16: return walk_n<TI, Q, 16>(f, s);
+        case 32: return walk_n<TI, Q, 32>(f, s);
+        case 64: return walk_n<TI, Q, 64>(f, s);
+        case 128: return walk_n<TI, Q, 128>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
-template <typename TI>
+template <typename TI, int Q>
+static ssd_status prepare_n(const FwdArgs &f, hipStream_t s) {
+    switch (f.N) {
+        case 16: return run_prepare<TI, Q, 16>(f, s);
+        case 32: return run_prepare<TI, Q, 32>(f, s);
+        case 64: return run_prepare<TI, Q, 64>(f, s);
+        case 128: return run_prepare<TI, Q, 128>(f, s);
+        case 256: return run_prepare<TI, Q, 256>(f, s);
+        default: return SSD_ERR_UNSUPPORTED;
+    }
+}
+
+template <typename TI, bool kWalk>
 static ssd_status dispatch_q(const FwdArgs &f, hipStream_t s) {
     switch (f.Q) {
-        case 64: return dispatch_p<TI, 64>(f, s);
-        case 128: return dispatch_p<TI, 128>(f, s);
-        case 256: return dispatch_p<TI, 256>(f, s);
+        case 64: return kWalk ? walk_p<TI, 64>(f, s) : prepare_n<TI, 64>(f, s);
+        case 128: return kWalk ? walk_p<TI, 128>(f, s) : prepare_n<TI, 128>(f, s);
+        case 256: return kWalk ? walk_p<TI, 256>(f, s) : prepare_n<TI, 256>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
-ssd_status launch_fwd(const FwdArgs &f, hipStream_t s) {
-    return f.dtype == SSD_BF16 ? dispatch_q<bf16>(f, s) : dispatch_q<float>(f, s);
+ssd_status launch_prepare(const FwdArgs &f, hipStream_t s) {
+    return f.dtype == SSD_BF16 ? dispatch_q<bf16, false>(f, s) : dispatch_q<float, false>(f, s);
+}
+
+ssd_status launch_walk(const FwdArgs &f, hipStream_t s) {
+    return f.dtype == SSD_BF16 ? dispatch_q<bf16, true>(f, s) : dispatch_q<float, true>(f, s);
 }
 
 template <typename TI, int Q, int P, int N>

@@ -14,6 +14,7 @@ struct FwdArgs {
     const float *A, *D;
     void *Y;
     float *final_state;        // may be null
+    const float *init;         // (batch, H, P, N) initial state, or null for zero
     int64_t batch, T, H, P, N, G, Q, nC, Tpad;
     ssd_dtype dtype;
     float *cs2, *dtf;          // workspace: (batch, H, Tpad) each
@@ -42,7 +43,10 @@ struct StepArgs {
     ssd_dtype dtype;
 };
 
-ssd_status launch_fwd(const FwdArgs &f, hipStream_t s);
+// Phase 1: chunk-local log-decay prefix sums and C B^T tiles into the workspace.
+ssd_status launch_prepare(const FwdArgs &f, hipStream_t s);
+// Phase 2: the chunk walk (reads the prepared workspace).
+ssd_status launch_walk(const FwdArgs &f, hipStream_t s);
 // LDS bytes one chunk-walk work-group needs, or -1 if there is no kernel.
 int fwd_lds_bytes(ssd_dtype dt, int64_t Q, int64_t P, int64_t N);
 ssd_status launch_step(const StepArgs &a, hipStream_t s);

@@ -145,3 +145,44 @@ def test_single_hip_runtime_in_process():
     # torch's HIP runtime and libssd's must be the same library
     ssd.load()
     assert len(ssd._hip_runtimes_mapped()) == 1, ssd._hip_runtimes_mapped()
+
+
+def prep(dt=P16, A=P16, B=P16, C=P16, chunk=256, batch=4, T=2048, H=64, P=64, N=128, G=1,
+         dtype=BF16, wsp=P16 * 16, wsb=1 << 40, stream=None):
+    return ssd.raw_call("ssd_chunk_scan_prepare", dt, A, B, C, chunk, batch, T, H, P, N, G, dtype,
+                        wsp, wsb, stream)
+
+
+def walk(X=P16, B=P16, C=P16, D=P16, init=None, chunk=256, Y=P16, fin=P16, batch=4, T=2048, H=64,
+         P=64, N=128, G=1, dtype=BF16, wsp=P16 * 16, wsb=1 << 40, stream=None):
+    return ssd.raw_call("ssd_chunk_scan_walk", X, B, C, D, init, chunk, Y, fin, batch, T, H, P, N,
+                        G, dtype, wsp, wsb, stream)
+
+
+@pytest.mark.parametrize("field", ["dt", "A", "B", "C"])
+def test_prepare_null_and_align(field):
+    assert prep(**{field: None}) == ENULL
+    assert prep(**{field: P16 + 8}) == EALIGN
+
+
+@pytest.mark.parametrize("field", ["X", "B", "C", "D", "Y"])
+def test_walk_null(field):
+    assert walk(**{field: None}) == ENULL
+
+
+@pytest.mark.parametrize("field", ["X", "B", "C", "D", "Y", "init", "fin"])
+def test_walk_alignment(field):
+    assert walk(**{field: P16 + 4}) == EALIGN
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=64, G=3), ESHAPE), (dict(chunk=48), EUNSUP), (dict(N=24), EUNSUP), (dict(wsp=None), EWS),
+])
+def test_prepare_and_walk_shape_checks(kw, code):
+    assert prep(**kw) == code
+    assert walk(**kw) == code
+
+
+def test_prepare_and_walk_empty():
+    assert prep(batch=0, wsp=None, wsb=0) == OK
+    assert walk(batch=0, wsp=None, wsb=0) == OK

@@ -173,3 +173,74 @@ def test_empty_sequence_zero_final_state(ssd):
     Y, F = ssd.ssd_chunk_scan_fwd(X, dt, A, B, B, D, 256, final_state=F)
     torch.cuda.synchronize()
     assert Y.shape == X.shape and not torch.any(F)
+
+
+def test_prepare_then_walk_is_the_forward(ssd):
+    import torch
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="split", batch=2, seqlen=700, nheads=8,
+                              seed=70)
+    inp = si.make_fwd_inputs(cfg)
+    log("[fwd] prepare + walk == fwd (bitwise)")
+    X, dt, B, C = (to_dev(inp[k]) for k in ("X", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    Y1, F1 = ssd.ssd_chunk_scan_fwd(X, dt, A, B, C, D, 256)
+    ws = ssd.ssd_chunk_scan_prepare(dt, A, B, C, 256, cfg.headdim)
+    Y2, F2 = ssd.ssd_chunk_scan_walk(X, B, C, D, ws, 256)
+    # a second walk over the same preparation with another X: the map is linear
+    # in X (skip term included) and scaling by 2 is exact in floating point
+    Y3, F3 = ssd.ssd_chunk_scan_walk(X * 2, B, C, D, ws, 256)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(F1, F2)
+    assert torch.allclose(Y3.float(), 2 * Y1.float(), rtol=2 ** -7, atol=0)
+    assert torch.allclose(F3, 2 * F1, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 256), ("bf16", 64), ("f32", 128)])
+def test_walk_from_initial_state(ssd, dtype, chunk):
+    """A walk from a given initial state matches the oracle run from that state."""
+    import torch
+    base = si.CONFIGS["l1p3b_bf16"] if dtype == "bf16" else si.CONFIGS["tiny_f32"]
+    cfg = dataclasses.replace(base, name=f"init_{dtype}", batch=2, seqlen=333, nheads=4, ngroups=2,
+                              seed=71)
+    inp = si.make_fwd_inputs(cfg)
+    rng = np.random.default_rng(72)
+    h0 = rng.standard_normal((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate)).astype(np.float32)
+    log(f"[fwd] walk from initial state {dtype} chunk {chunk}")
+    X, dt, B, C = (to_dev(inp[k]) for k in ("X", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    ws = ssd.ssd_chunk_scan_prepare(dt, A, B, C, chunk, cfg.headdim)
+    Y, F = ssd.ssd_chunk_scan_walk(X, B, C, D, ws, chunk, initial_state=to_dev(h0))
+    Y0, _ = ssd.ssd_chunk_scan_walk(X, B, C, torch.zeros_like(D), ws, chunk, initial_state=to_dev(h0))
+    torch.cuda.synchronize()
+    import oracle
+    Yr, Fr, _ = oracle.fwd(inp["X32"], inp["dt32"], inp["A"], inp["B32"], inp["C32"], inp["D"],
+                           cfg.ngroups, init_state=h0)
+    Yr0, _, _ = oracle.fwd(inp["X32"], inp["dt32"], inp["A"], inp["B32"], inp["C32"],
+                           np.zeros_like(inp["D"]), cfg.ngroups, init_state=h0)
+    e = (rel(Y.float().cpu().numpy(), Yr), rel(Y0.float().cpu().numpy(), Yr0), rel(F.cpu().numpy(), Fr))
+    log(f"    rel err Y={e[0]:.2e} Y(D=0)={e[1]:.2e} final={e[2]:.2e}")
+    tol = TOL[cfg.dtype]
+    assert max(e) <= tol, e
+
+
+def test_resume_across_calls(ssd):
+    """Forward over [0, T1), then a walk over [T1, T) from the carried final
+    state, reproduces one forward over [0, T) to the bf16 tolerance."""
+    import torch
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="resume", batch=2, seqlen=900, nheads=4,
+                              seed=73)
+    inp = si.make_fwd_inputs(cfg)
+    X, dt, B, C = (to_dev(inp[k]) for k in ("X", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    Yf, Ff = ssd.ssd_chunk_scan_fwd(X, dt, A, B, C, D, 256)
+    T1 = 389
+    Ya, Fa = ssd.ssd_chunk_scan_fwd(X[:, :T1].contiguous(), dt[:, :T1].contiguous(), A,
+                                    B[:, :T1].contiguous(), C[:, :T1].contiguous(), D, 256)
+    Xb, dtb, Bb, Cb = (t[:, T1:].contiguous() for t in (X, dt, B, C))
+    ws = ssd.ssd_chunk_scan_prepare(dtb, A, Bb, Cb, 256, cfg.headdim)
+    Yb, Fb = ssd.ssd_chunk_scan_walk(Xb, Bb, Cb, D, ws, 256, initial_state=Fa)
+    torch.cuda.synchronize()
+    Ys = torch.cat([Ya, Yb], 1).float().cpu().numpy()
+    e = (rel(Ys, Yf.float().cpu().numpy()), rel(Fb.cpu().numpy(), Ff.cpu().numpy()))
+    log(f"[fwd] resume across calls: rel Y={e[0]:.2e} final={e[1]:.2e}")
+    assert max(e) <= TOL["bf16"], e
