@@ -212,7 +212,7 @@ ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A,
         return SSD_ERR_ALIGN;
     if (batch == 0) return SSD_OK;
     const int64_t rows = batch * nheads * headdim;
-    if (rows / 16 > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;
+    if (rows > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;  // grid size bound
     ssd::StepArgs a;
     a.state = state; a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
     a.batch = batch; a.H = nheads; a.P = headdim; a.N = dstate; a.G = ngroups; a.dtype = dtype;

@@ -29,6 +29,13 @@ constexpr int kRsrcWord3 = 0x00020000;
 // An offset beyond every range a kernel builds: loads return 0, stores drop.
 constexpr uint32_t kOOB = 0x80000000u;
 
+// Offset `off`, or one past every range when `bad`: bit 31 is set, and every
+// range a kernel builds is under 2 GiB. Arithmetic rather than a select, so
+// the compiler keeps one load instead of branching around two.
+__device__ __forceinline__ uint32_t oob_if(bool bad, uint32_t off) {
+    return off | ((uint32_t)bad << 31);
+}
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              kRsrcWord3);

@@ -32,15 +32,17 @@
 // row factor is applied to the 16x16 accumulators. On the diagonal tile the
 // mask is built per element in registers, with j > i selected to zero before
 // the exponential is used.
+#include <utility>
+
 #include "ssd_common.h"
 #include "ssd_internal.h"
 
 namespace ssd {
 
 // ---------------------------------------------------------------------------
-// k_dt_cumsum
+// k_dt_cumsum: one work-group per (batch, chunk, block of 16 heads)
 // ---------------------------------------------------------------------------
-constexpr int kCumsumHeads = 64;  // heads per work-group
+constexpr int kCumsumHeads = 16;
 
 template <typename TI, int Q>
 __global__ __launch_bounds__(256) void k_dt_cumsum(const TI *__restrict__ dt,
@@ -51,25 +53,32 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(const TI *__restrict__ dt,
     constexpr int ES = Traits<TI>::kBytes;
     constexpr int LD = Q + 1;
     __shared__ float tile[kCumsumHeads * LD];
-    const int c = blockIdx.x % nC;
-    const int hb = (blockIdx.x / nC) % ((H + kCumsumHeads - 1) / kCumsumHeads);
-    const int b = blockIdx.x / (nC * ((H + kCumsumHeads - 1) / kCumsumHeads));
+    const int hblocks = (H + kCumsumHeads - 1) / kCumsumHeads;
+    int x = blockIdx.x;
+    const int c = x % nC;
+    x /= nC;
+    const int hb = x % hblocks;
+    const int b = x / hblocks;
     const int h0 = hb * kCumsumHeads;
     const int Hb = min(kCumsumHeads, H - h0);
     const int t0 = c * Q;
     const rsrc_t r = make_rsrc(reinterpret_cast<const char *>(dt) + (size_t)b * T * H * ES,
                                (uint32_t)((size_t)T * H * ES));
-    // coalesced load: consecutive threads read consecutive heads of one token
-    for (int idx = threadIdx.x; idx < Q * Hb; idx += 256) {
-        const int t = idx / Hb, hl = idx - t * Hb;
-        const uint32_t off = (t0 + t < T) ? (uint32_t)(((t0 + t) * H + h0 + hl) * ES) : kOOB;
-        float v;
-        if constexpr (ES == 2) {
-            v = (float)__builtin_bit_cast(bf16, buf_ld16(r, off));
-        } else {
-            v = __builtin_bit_cast(float, buf_ld32(r, off));
+    // one token row per thread: all of its loads are issued before any is used
+    for (int t = threadIdx.x; t < Q; t += 256) {
+        float v[kCumsumHeads];
+#pragma unroll
+        for (int hl = 0; hl < kCumsumHeads; ++hl) {
+            const uint32_t off =
+                (hl < Hb && t0 + t < T) ? (uint32_t)(((t0 + t) * H + h0 + hl) * ES) : kOOB;
+            if constexpr (ES == 2) {
+                v[hl] = (float)__builtin_bit_cast(bf16, buf_ld16(r, off));
+            } else {
+                v[hl] = __builtin_bit_cast(float, buf_ld32(r, off));
+            }
         }
-        tile[hl * LD + t] = v;
+#pragma unroll
+        for (int hl = 0; hl < kCumsumHeads; ++hl) tile[hl * LD + t] = v[hl];
     }
     __syncthreads();
     constexpr int PER = Q / 64;  // tokens per lane
@@ -104,7 +113,8 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(const TI *__restrict__ dt,
 }
 
 // ---------------------------------------------------------------------------
-// k_chunk_cb: G[b, g, c, pair(I, J)] = C_I B_J^T, J <= I, 64 x 64 tiles
+// k_chunk_cb: G[b, g, c, pair(I, J)] = C_I B_J^T, J <= I, one 64 x 64 tile
+// per work-group; every operand load is issued before the first product.
 // ---------------------------------------------------------------------------
 __host__ __device__ constexpr int pair_index(int I, int J) { return I * (I + 1) / 2 + J; }
 
@@ -113,15 +123,21 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const TI *__restrict__ Bm,
                                                   const TI *__restrict__ Cm, TI *__restrict__ Gout,
                                                   int T, int G, int nC, uint32_t g_bytes) {
     using Tr = Traits<TI>;
+    using frag = typename Tr::frag;
     constexpr int ES = Tr::kBytes;
     constexpr int NT = Q / 64;
     constexpr int NP = NT * (NT + 1) / 2;
     constexpr int NK = (N + 31) / 32;
     int x = blockIdx.x;
-    const int I = x % NT; x /= NT;
-    const int g = x % G; x /= G;
+    const int pr = x % NP;
+    x /= NP;
+    const int g = x % G;
+    x /= G;
     const int c = x % nC;
     const int b = x / nC;
+    int I = 0;
+    while ((I + 1) * (I + 2) / 2 <= pr) ++I;
+    const int J = pr - I * (I + 1) / 2;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, kg = lane >> 4;
     const size_t slab = (size_t)T * G * N * ES;
@@ -130,44 +146,39 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const TI *__restrict__ Bm,
     const rsrc_t rg = make_rsrc(Gout, g_bytes);
     const int t0 = c * Q;
     const int ti = t0 + I * 64 + 16 * w + r;  // this lane's A row (token)
-    typename Tr::frag ca[NK];
+    frag ca[NK], bb[4][NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
         const int n0 = kk * 32 + 8 * kg;
-        const uint32_t off = (ti < T && n0 < N) ? (uint32_t)(((ti * G + g) * N + n0) * ES) : kOOB;
-        ca[kk] = Tr::load_frag(rc, off);
-    }
-    for (int J = 0; J <= I; ++J) {
-        f32x4 acc[4];
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            const int n0 = kk * 32 + 8 * kg;
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const int tj = t0 + J * 64 + 16 * cb + r;
-                const uint32_t off =
-                    (tj < T && n0 < N) ? (uint32_t)(((tj * G + g) * N + n0) * ES) : kOOB;
-                const typename Tr::frag bb = Tr::load_frag(rb, off);
-                acc[cb] = Tr::mma(ca[kk], bb, acc[cb]);
-            }
-        }
-        const size_t tile = ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, J)) * 4096;
+        ca[kk] = Tr::load_frag(rc, (ti < T && n0 < N) ? (uint32_t)(((ti * G + g) * N + n0) * ES) : kOOB);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
+            const int tj = t0 + J * 64 + 16 * cb + r;
+            bb[cb][kk] =
+                Tr::load_frag(rb, (tj < T && n0 < N) ? (uint32_t)(((tj * G + g) * N + n0) * ES) : kOOB);
+        }
+    }
+    f32x4 acc[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * w + 4 * kg + i, col = 16 * cb + r;
-                const uint32_t off = (uint32_t)((tile + row * 64 + col) * ES);
-                // copy the element out first: a bit_cast taken directly on a
-                // vector-element lvalue reads element 0 with this compiler
-                const float v = acc[cb][i];
-                if constexpr (ES == 2) {
-                    buf_st16(__builtin_bit_cast(uint16_t, Tr::from_f32(v)), rg, off);
-                } else {
-                    buf_st32(__builtin_bit_cast(uint32_t, v), rg, off);
-                }
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[cb] = Tr::mma(ca[kk], bb[cb][kk], acc[cb]);
+    const size_t tile = ((((size_t)b * G + g) * nC + c) * NP + pr) * 4096;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * w + 4 * kg + i, col = 16 * cb + r;
+            const uint32_t off = (uint32_t)((tile + row * 64 + col) * ES);
+            // copy the element out first: a bit_cast taken directly on a
+            // vector-element lvalue reads element 0 with this compiler
+            const float v = acc[cb][i];
+            if constexpr (ES == 2) {
+                buf_st16(__builtin_bit_cast(uint16_t, Tr::from_f32(v)), rg, off);
+            } else {
+                buf_st32(__builtin_bit_cast(uint32_t, v), rg, off);
             }
         }
     }
@@ -183,14 +194,22 @@ struct WalkCfg {
     static constexpr int NP = NT * (NT + 1) / 2;
     static constexpr int PB = P / 16;
     static constexpr int NB = N / 16;
-    static constexpr int NW = 4;
-    static constexpr int NBW = (NB + NW - 1) / NW;
+    static constexpr int NW = 4;                  // wavefronts per work-group
+    static constexpr int NTH = 64 * NW;
+    static constexpr int NBW = (NB + NW - 1) / NW;  // state n-blocks per wave
+    static constexpr int WPR = NW / 4;              // waves sharing one 16-row output block
+    static constexpr int PBW = (PB + WPR - 1) / WPR;  // output p-blocks per wave
     static constexpr int NK = (N + 31) / 32;
     static constexpr int PAD = 16 / ES;
-    static constexpr int XT_LD = Q + PAD;     // X^T rows (p), token-contiguous
-    static constexpr int BT_LD = 64 + PAD;    // B^T rows (n), token-contiguous, one tile
+    static constexpr int XT_LD = Q + PAD;        // X^T rows (p), token-contiguous, whole chunk
+    static constexpr int BT_LD = 64 + PAD;       // B^T rows (n), token-contiguous, one tile
     static constexpr int HS_LD = NK * 32 + PAD;  // state rows (p), n-contiguous
-    static constexpr int YS_LD = P + PAD;     // output staging rows (token)
+    static constexpr int YS_LD = P + PAD;        // output staging rows (token)
+    // staging units per 64-token tile: 4 consecutive tokens x 8 consecutive columns
+    static constexpr int UX = 16 * (P / 8);
+    static constexpr int UB = 16 * (N / 8);
+    static constexpr int RX = (UX + NTH - 1) / NTH;
+    static constexpr int RB = (UB + NTH - 1) / NTH;
     static constexpr int XT_OFF = 0;
     static constexpr int XT_BYTES = P * XT_LD * ES;
     static constexpr int XH_OFF = XT_OFF + XT_BYTES;
@@ -200,19 +219,52 @@ struct WalkCfg {
     static constexpr int HS_BYTES = P * HS_LD * ES;
     static constexpr int YS_OFF = HS_OFF + HS_BYTES;
     static constexpr int YS_BYTES = 64 * YS_LD * ES;
-    static constexpr int CS_OFF = YS_OFF + YS_BYTES;
-    static constexpr int DT_OFF = CS_OFF + Q * 4;
-    static constexpr int LDS = DT_OFF + Q * 4;
+    static constexpr int CS_OFF = YS_OFF + YS_BYTES;  // 2 buffers x (cs2[Q], dt[Q]) fp32
+    static constexpr int LDS = CS_OFF + 2 * 2 * Q * 4;
     static constexpr bool kFits = LDS <= 160 * 1024;
 };
 
+// Global data one 64-token tile needs, held in registers so that the next
+// tile's loads are in flight while the current tile computes.
 template <typename TI, int Q, int P, int N>
-__global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
+struct WalkRegs {
+    using Cfg = WalkCfg<TI, Q, P, N>;
+    using frag = typename Traits<TI>::frag;
+    frag xr[Cfg::RX][4];   // X: 4 tokens x 8 columns per staging unit
+    frag br[Cfg::RB][4];   // B: 4 tokens x 8 columns per staging unit
+    frag cf[Cfg::NK];      // C rows of this lane's A row (state -> output)
+    frag gf[Cfg::NT][2];   // C B^T rows of tiles J <= I (two 32-wide k-steps each)
+};
+
+template <int... Is, typename F>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int Count, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, Count>{});
+}
+
+template <typename TI>
+__device__ __forceinline__ void lds_store4(TI *p, TI v0, TI v1, TI v2, TI v3) {
+    if constexpr (sizeof(TI) == 2) {
+        bf16x4 v = {v0, v1, v2, v3};
+        *reinterpret_cast<bf16x4 *>(p) = v;
+    } else {
+        f32x4 v = {v0, v1, v2, v3};
+        *reinterpret_cast<f32x4 *>(p) = v;
+    }
+}
+
+template <typename TI, int Q, int P, int N>
+__global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(WalkArgs a) {
     using Tr = Traits<TI>;
     using Cfg = WalkCfg<TI, Q, P, N>;
+    using Regs = WalkRegs<TI, Q, P, N>;
     using frag = typename Tr::frag;
     constexpr int ES = Cfg::ES, NT = Cfg::NT, NP = Cfg::NP, PB = Cfg::PB, NB = Cfg::NB;
-    constexpr int NW = Cfg::NW, NBW = Cfg::NBW, NK = Cfg::NK;
+    constexpr int NW = Cfg::NW, NTH = Cfg::NTH, NBW = Cfg::NBW, PBW = Cfg::PBW, NK = Cfg::NK;
+    constexpr int WPR = Cfg::WPR;
     constexpr int XT_LD = Cfg::XT_LD, BT_LD = Cfg::BT_LD, HS_LD = Cfg::HS_LD, YS_LD = Cfg::YS_LD;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
     TI *XT = reinterpret_cast<TI *>(smem + Cfg::XT_OFF);
@@ -220,8 +272,7 @@ __global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
     TI *BT = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);
     TI *HS = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);
     TI *YS = reinterpret_cast<TI *>(smem + Cfg::YS_OFF);
-    float *CSL = reinterpret_cast<float *>(smem + Cfg::CS_OFF);
-    float *DTL = reinterpret_cast<float *>(smem + Cfg::DT_OFF);
+    float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);  // [buf][cs2 Q | dt Q]
 
     const int H = a.H, G = a.G, T = a.T, nC = a.nC;
     // blockIdx -> (b, h): consecutive logical indices share an XCD (dispatch
@@ -233,19 +284,67 @@ __global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
     const int b = L / H, h = L - b * H;
     const int g = (h * G) / H;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
     const int r = lane & 15, kg = lane >> 4;
+    const int rb = w & 3;   // output row block (16 tokens) of this wave
+    const int ph = w >> 2;  // output p-blocks ph, ph + WPR, ... of this wave
+    // X staging units go to threads 0.., B staging units to threads ..NTH-1
+    const int xu0 = tid, bu0 = NTH - 1 - tid;
 
     const size_t xslab = (size_t)T * H * P * ES;
     const size_t bslab = (size_t)T * G * N * ES;
     const rsrc_t rx = make_rsrc(reinterpret_cast<const char *>(a.X) + b * xslab, (uint32_t)xslab);
     const rsrc_t ry = make_rsrc(reinterpret_cast<char *>(a.Y) + b * xslab, (uint32_t)xslab);
-    const rsrc_t rb = make_rsrc(reinterpret_cast<const char *>(a.B) + b * bslab, (uint32_t)bslab);
+    const rsrc_t rbm = make_rsrc(reinterpret_cast<const char *>(a.B) + b * bslab, (uint32_t)bslab);
     const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(a.C) + b * bslab, (uint32_t)bslab);
     const rsrc_t rg = make_rsrc(a.Gbuf, a.g_bytes);
     const float *cs_row = a.cs2 + ((size_t)b * H + h) * a.Tpad;
     const float *dt_row = a.dtf + ((size_t)b * H + h) * a.Tpad;
     const float Dh = a.D[h];
+
+    // issue every global load tile (c, I) needs, into registers
+    auto load_tile = [&](Regs &R, int c, auto Ic) {
+        constexpr int I = decltype(Ic)::value;
+        const int t0 = c * Q, tile0 = I * 64;
+#pragma unroll
+        for (int k = 0; k < Cfg::RX; ++k) {
+            const int u = xu0 + NTH * k;
+            const int tq = u % 16, po = (u / 16) % (P / 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + tile0 + 4 * tq + i;
+                R.xr[k][i] = Tr::load_frag(
+                    rx, oob_if(u >= Cfg::UX || t >= T, (uint32_t)(((t * H + h) * P + 8 * po) * ES)));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < Cfg::RB; ++k) {
+            const int u = bu0 + NTH * k;
+            const int tq = u % 16, no = (u / 16) % (N / 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = t0 + tile0 + 4 * tq + i;
+                R.br[k][i] = Tr::load_frag(
+                    rbm, oob_if(u >= Cfg::UB || t >= T, (uint32_t)(((t * G + g) * N + 8 * no) * ES)));
+            }
+        }
+        const int ti = t0 + tile0 + 16 * rb + r;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * kg;
+            R.cf[kk] = Tr::load_frag(
+                rc, oob_if(ti >= T || n0 >= N, (uint32_t)(((ti * G + g) * N + n0) * ES)));
+        }
+#pragma unroll
+        for (int J = 0; J <= I; ++J) {
+            const size_t gt = ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, J)) * 4096;
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+                R.gf[J][k2] =
+                    Tr::load_frag(rg, (uint32_t)((gt + (16 * rb + r) * 64 + 32 * k2 + 8 * kg) * ES));
+        }
+    };
 
     // state accumulators: tile (pb, nb = w + NW*j), rows p = 16pb + 4kg + i, col n = 16nb + r
     f32x4 hacc[PB][NBW];
@@ -265,111 +364,141 @@ __global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
             hacc[pb][j] = v;
         }
 
+    Regs R[2];
+    for (int k = tid; k < Q; k += NTH) {
+        CSB[k] = cs_row[k];
+        CSB[Q + k] = dt_row[k];
+    }
+    load_tile(R[0], 0, std::integral_constant<int, 0>{});
+
     for (int c = 0; c < nC; ++c) {
         const int t0 = c * Q;
-        for (int k = tid; k < Q; k += 256) {
-            CSL[k] = cs_row[t0 + k];
-            DTL[k] = dt_row[t0 + k];
-        }
-        // state entering this chunk -> matrix-core operand copy
+        const float *CSL = CSB + (c & 1) * 2 * Q;
+        const float *DTL = CSL + Q;
+        float *CSN = CSB + ((c + 1) & 1) * 2 * Q;  // next chunk's slot
+        float csn = 0.f, dtn = 0.f;
+        static_for<NT>([&](auto Ic) {
+            constexpr int I = decltype(Ic)::value;
+            constexpr int cur = (NT == 1) ? 0 : (I & 1);
+            constexpr int nxt = cur ^ 1;
+            Regs &RC = R[cur];
+            const int tile0 = I * 64;
+            if constexpr (I == 0) {
+                // state entering this chunk -> matrix-core operand copy
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb)
+                for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-                const int nb = w + NW * j;
-                if (nb < NB) {
+                    for (int j = 0; j < NBW; ++j) {
+                        const int nb = w + NW * j;
+                        if (nb < NB) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        HS[(16 * pb + 4 * kg + i) * HS_LD + 16 * nb + r] = Tr::from_f32(hacc[pb][j][i]);
+                            for (int i = 0; i < 4; ++i)
+                                HS[(16 * pb + 4 * kg + i) * HS_LD + 16 * nb + r] =
+                                    Tr::from_f32(hacc[pb][j][i]);
+                        }
+                    }
+                if constexpr (N % 32 != 0) {
+                    for (int k = tid; k < P * (NK * 32 - N); k += NTH) {
+                        const int p = k / (NK * 32 - N), n = N + k % (NK * 32 - N);
+                        HS[p * HS_LD + n] = Tr::from_f32(0.f);
+                    }
                 }
             }
-        if constexpr (N % 32 != 0) {
-            // zero the K-padding columns of the state copy (read by the last fragment)
-            for (int k = tid; k < P * (NK * 32 - N); k += 256) {
-                const int p = k / (NK * 32 - N), n = N + k % (NK * 32 - N);
-                HS[p * HS_LD + n] = Tr::from_f32(0.f);
-            }
-        }
-        __syncthreads();
-
-        for (int I = 0; I < NT; ++I) {
-            const int tile0 = I * 64;            // chunk-local first token of the tile
             const float cs_e = CSL[tile0 + 63];  // tile's last token
-            // ---- stage X tile (unscaled and column-scaled copies) and B tile
-            for (int u = tid; u < 32 * (P / 8); u += 256) {
-                const int jp = u / (P / 8), po = u - jp * (P / 8);
-                const int jl = 2 * jp, jc = tile0 + jl, t = t0 + jc;
-                const uint32_t o0 = (t < T) ? (uint32_t)(((t * H + h) * P + 8 * po) * ES) : kOOB;
-                const uint32_t o1 = (t + 1 < T) ? o0 + (uint32_t)(H * P * ES) : kOOB;
-                const frag x0 = Tr::load_frag(rx, o0), x1 = Tr::load_frag(rx, o1);
-                const float s0 = DTL[jc] * fast_exp2(cs_e - CSL[jc]);
-                const float s1 = DTL[jc + 1] * fast_exp2(cs_e - CSL[jc + 1]);
+            // ---- stage the prefetched X tile (unscaled and column-scaled) and B tile
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = (8 * po + e);
-                    const float v0 = Tr::frag_get(x0, e), v1 = Tr::frag_get(x1, e);
-                    XT[row * XT_LD + jc] = Tr::from_f32(v0);
-                    XT[row * XT_LD + jc + 1] = Tr::from_f32(v1);
-                    XH[row * XT_LD + jc] = Tr::from_f32(v0 * s0);
-                    XH[row * XT_LD + jc + 1] = Tr::from_f32(v1 * s1);
+            for (int k = 0; k < Cfg::RX; ++k) {
+                const int u = xu0 + NTH * k;
+                // wave-uniform whenever UX is a multiple of 64
+                if ((Cfg::UX % 64 == 0) ? (64 * w + NTH * k < Cfg::UX) : (u < Cfg::UX)) {
+                    const int tq = u % 16, po = u / 16;
+                    const int jc = tile0 + 4 * tq;
+                    float sc[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sc[i] = DTL[jc + i] * fast_exp2(cs_e - CSL[jc + i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = 8 * po + e;
+                        lds_store4<TI>(XT + row * XT_LD + jc, RC.xr[k][0][e], RC.xr[k][1][e],
+                                       RC.xr[k][2][e], RC.xr[k][3][e]);
+                        lds_store4<TI>(XH + row * XT_LD + jc,
+                                       Tr::from_f32(Tr::frag_get(RC.xr[k][0], e) * sc[0]),
+                                       Tr::from_f32(Tr::frag_get(RC.xr[k][1], e) * sc[1]),
+                                       Tr::from_f32(Tr::frag_get(RC.xr[k][2], e) * sc[2]),
+                                       Tr::from_f32(Tr::frag_get(RC.xr[k][3], e) * sc[3]));
+                    }
                 }
             }
-            for (int u = tid; u < 32 * (N / 8); u += 256) {
-                const int jp = u / (N / 8), no = u - jp * (N / 8);
-                const int jl = 2 * jp, t = t0 + tile0 + jl;
-                const uint32_t o0 = (t < T) ? (uint32_t)(((t * G + g) * N + 8 * no) * ES) : kOOB;
-                const uint32_t o1 = (t + 1 < T) ? o0 + (uint32_t)(G * N * ES) : kOOB;
-                const frag b0 = Tr::load_frag(rb, o0), b1 = Tr::load_frag(rb, o1);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    BT[(8 * no + e) * BT_LD + jl] = Tr::from_f32(Tr::frag_get(b0, e));
-                    BT[(8 * no + e) * BT_LD + jl + 1] = Tr::from_f32(Tr::frag_get(b1, e));
+            for (int k = 0; k < Cfg::RB; ++k) {
+                const int u = bu0 + NTH * k;
+                if ((Cfg::UB % 64 == 0) ? (64 * (NW - 1 - w) + NTH * k < Cfg::UB) : (u < Cfg::UB)) {
+                    const int tq = u % 16, no = u / 16;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq, RC.br[k][0][e],
+                                       RC.br[k][1][e], RC.br[k][2][e], RC.br[k][3][e]);
                 }
             }
             __syncthreads();
 
-            // ---- output rows tile0 + 16w .. +15 (A-operand row r), all P columns
-            const int irow = tile0 + 16 * w + r;  // chunk-local token of this lane's A row
-            const int ti = t0 + irow;
-            f32x4 acc[PB];
+            // ---- prefetch the next tile while this one computes
+            // (past the last chunk the loads fall outside every range and return 0)
+            if constexpr (I + 1 < NT) {
+                load_tile(R[nxt], c, std::integral_constant<int, I + 1>{});
+            } else {
+                load_tile(R[nxt], c + 1, std::integral_constant<int, 0>{});
+            }
+            if constexpr (I == 0) {
+                if (c + 1 < nC && tid < Q) {  // Q <= NTH: one value per thread
+                    csn = cs_row[t0 + Q + tid];
+                    dtn = dt_row[t0 + Q + tid];
+                }
+            }
+
+            // ---- output rows tile0 + 16rb .. +15 (A-operand row r), p-blocks ph, ph + 2, ...
+            const int irow = tile0 + 16 * rb + r;  // chunk-local token of this lane's A row
+            f32x4 acc[PBW];
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < PBW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
             // state -> output: C_i . h_in
 #pragma unroll
             for (int kk = 0; kk < NK; ++kk) {
                 const int n0 = kk * 32 + 8 * kg;
-                const uint32_t off =
-                    (ti < T && n0 < N) ? (uint32_t)(((ti * G + g) * N + n0) * ES) : kOOB;
-                const frag ca = Tr::load_frag(rc, off);
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const frag hb = Tr::lds_frag(HS + (16 * pb + r) * HS_LD + n0);
-                    acc[pb] = Tr::mma(ca, hb, acc[pb]);
+                for (int j = 0; j < PBW; ++j) {
+                    const int pb = ph + WPR * j;
+                    if (pb < PB) {
+                        const frag hb = Tr::lds_frag(HS + (16 * pb + r) * HS_LD + n0);
+                        acc[j] = Tr::mma(RC.cf[kk], hb, acc[j]);
+                    }
                 }
             }
             float cs_rows[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cs_rows[i] = CSL[tile0 + 16 * w + 4 * kg + i];
+            for (int i = 0; i < 4; ++i) cs_rows[i] = CSL[tile0 + 16 * rb + 4 * kg + i];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float f = fast_exp2(cs_rows[i]);
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) acc[pb][i] *= f;
+                for (int j = 0; j < PBW; ++j) acc[j][i] *= f;
             }
             // earlier tiles of this chunk: G_IJ (unmasked, J < I) times the scaled X copy
+#pragma unroll
             for (int J = 0; J < I; ++J) {
-                f32x4 tmp[PB];
+                f32x4 tmp[PBW];
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) tmp[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const size_t gt = ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, J)) * 4096;
+                for (int j = 0; j < PBW; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k0 = 0; k0 < 64; k0 += 32) {
-                    const frag ga =
-                        Tr::load_frag(rg, (uint32_t)((gt + (16 * w + r) * 64 + k0 + 8 * kg) * ES));
+                for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) {
-                        const frag xb = Tr::lds_frag(XH + (16 * pb + r) * XT_LD + J * 64 + k0 + 8 * kg);
-                        tmp[pb] = Tr::mma(ga, xb, tmp[pb]);
+                    for (int j = 0; j < PBW; ++j) {
+                        const int pb = ph + WPR * j;
+                        if (pb < PB) {
+                            const frag xb =
+                                Tr::lds_frag(XH + (16 * pb + r) * XT_LD + J * 64 + 32 * k2 + 8 * kg);
+                            tmp[j] = Tr::mma(RC.gf[J][k2], xb, tmp[j]);
+                        }
                     }
                 }
                 const float cs_je = CSL[J * 64 + 63];
@@ -377,52 +506,58 @@ __global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
                 for (int i = 0; i < 4; ++i) {
                     const float f = fast_exp2(cs_rows[i] - cs_je);
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) acc[pb][i] += f * tmp[pb][i];
+                    for (int j = 0; j < PBW; ++j) acc[j][i] += f * tmp[j][i];
                 }
             }
             // diagonal tile: mask built per element, j > i selected to zero
             {
-                const size_t gt = ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, I)) * 4096;
                 const float cs_i = CSL[irow];
 #pragma unroll
-                for (int k0 = 0; k0 < 64; k0 += 32) {
-                    if (k0 > 16 * w + 15) continue;  // wave-uniform: block entirely above the diagonal
-                    const frag gr =
-                        Tr::load_frag(rg, (uint32_t)((gt + (16 * w + r) * 64 + k0 + 8 * kg) * ES));
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    if (32 * k2 > 16 * rb + 15) continue;  // wave-uniform: block above the diagonal
                     frag ma;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const int jc = tile0 + k0 + 8 * kg + e;
-                        const float v = Tr::frag_get(gr, e) * fast_exp2(cs_i - CSL[jc]) * DTL[jc];
+                        const int jc = tile0 + 32 * k2 + 8 * kg + e;
+                        const float v =
+                            Tr::frag_get(RC.gf[I][k2], e) * fast_exp2(cs_i - CSL[jc]) * DTL[jc];
                         Tr::frag_set(ma, e, (jc <= irow) ? v : 0.f);
                     }
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) {
-                        const frag xb = Tr::lds_frag(XT + (16 * pb + r) * XT_LD + tile0 + k0 + 8 * kg);
-                        acc[pb] = Tr::mma(ma, xb, acc[pb]);
+                    for (int j = 0; j < PBW; ++j) {
+                        const int pb = ph + WPR * j;
+                        if (pb < PB) {
+                            const frag xb =
+                                Tr::lds_frag(XT + (16 * pb + r) * XT_LD + tile0 + 32 * k2 + 8 * kg);
+                            acc[j] = Tr::mma(ma, xb, acc[j]);
+                        }
                     }
                 }
             }
             // skip term and output staging
 #pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
+            for (int j = 0; j < PBW; ++j) {
+                const int pb = ph + WPR * j;
+                if (pb < PB) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rl = 16 * w + 4 * kg + i;  // tile-local token
-                    const float xv = Tr::to_f32(XT[(16 * pb + r) * XT_LD + tile0 + rl]);
-                    YS[rl * YS_LD + 16 * pb + r] = Tr::from_f32(acc[pb][i] + Dh * xv);
+                    for (int i = 0; i < 4; ++i) {
+                        const int rl = 16 * rb + 4 * kg + i;  // tile-local token
+                        const float xv = Tr::to_f32(XT[(16 * pb + r) * XT_LD + tile0 + rl]);
+                        YS[rl * YS_LD + 16 * pb + r] = Tr::from_f32(acc[j][i] + Dh * xv);
+                    }
                 }
+            }
             __syncthreads();
             {
                 constexpr int VPR = P * ES / 16;  // 16-byte vectors per row
-                for (int v = lane; v < 16 * VPR; v += 64) {
-                    const int rl = 16 * w + v / VPR, cv = v % VPR;
+#pragma unroll
+                for (int v = tid; v < 64 * VPR; v += NTH) {
+                    const int rl = v / VPR, cv = v % VPR;
                     const int t = t0 + tile0 + rl;
                     const u32x4 d =
                         *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
                                                          rl * YS_LD * ES + cv * 16);
-                    const uint32_t off = (t < T) ? (uint32_t)((t * H + h) * P * ES + cv * 16) : kOOB;
-                    buf_st128(d, ry, off);
+                    buf_st128(d, ry, oob_if(t >= T, (uint32_t)((t * H + h) * P * ES + cv * 16)));
                 }
             }
 
@@ -435,24 +570,31 @@ __global__ __launch_bounds__(256, 1) void k_chunk_walk(WalkArgs a) {
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) hacc[pb][j] *= dec;
 #pragma unroll
-                for (int k0 = 0; k0 < 64; k0 += 32) {
+                for (int k2 = 0; k2 < 2; ++k2) {
                     frag xa[PB];
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb)
-                        xa[pb] = Tr::lds_frag(XH + (16 * pb + r) * XT_LD + tile0 + k0 + 8 * kg);
+                        xa[pb] = Tr::lds_frag(XH + (16 * pb + r) * XT_LD + tile0 + 32 * k2 + 8 * kg);
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) {
                         const int nb = w + NW * j;
                         if (nb < NB) {
-                            const frag bb = Tr::lds_frag(BT + (16 * nb + r) * BT_LD + k0 + 8 * kg);
+                            const frag bb = Tr::lds_frag(BT + (16 * nb + r) * BT_LD + 32 * k2 + 8 * kg);
 #pragma unroll
                             for (int pb = 0; pb < PB; ++pb) hacc[pb][j] = Tr::mma(xa[pb], bb, hacc[pb][j]);
                         }
                     }
                 }
             }
+            if constexpr (I == NT - 1) {
+                if (c + 1 < nC && tid < Q) {  // Q <= NTH
+                    CSN[tid] = csn;
+                    CSN[Q + tid] = dtn;
+                }
+            }
+            if constexpr (NT == 1) R[0] = R[1];
             __syncthreads();
-        }
+        });
     }
 
     if (a.final_state) {
@@ -482,8 +624,8 @@ static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
     if (launch(k_dt_cumsum<TI, Q>, dim3((unsigned)(f.batch * hblocks * nC)), dim3(256), s,
                (const TI *)f.dt, f.A, f.cs2, f.dtf, (int)f.T, (int)f.H, nC, (int)f.Tpad) != hipSuccess)
         return SSD_ERR_HIP;
-    constexpr int NT = Q / 64;
-    if (launch(k_chunk_cb<TI, Q, N>, dim3((unsigned)(f.batch * nC * f.G * NT)), dim3(256), s,
+    constexpr int NT = Q / 64, NP = NT * (NT + 1) / 2;
+    if (launch(k_chunk_cb<TI, Q, N>, dim3((unsigned)(f.batch * nC * f.G * NP)), dim3(256), s,
                (const TI *)f.B, (const TI *)f.C, (TI *)f.Gbuf, (int)f.T, (int)f.G, nC,
                (uint32_t)f.g_bytes) != hipSuccess)
         return SSD_ERR_HIP;
@@ -501,7 +643,7 @@ static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
         wa.cs2 = f.cs2; wa.dtf = f.dtf; wa.D = f.D; wa.init = f.init; wa.final_state = f.final_state;
         wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
         wa.Tpad = (int)f.Tpad; wa.g_bytes = (uint32_t)f.g_bytes;
-        return launch(k_chunk_walk<TI, Q, P, N>, dim3((unsigned)(f.batch * f.H)), dim3(256), s, wa) ==
+        return launch(k_chunk_walk<TI, Q, P, N>, dim3((unsigned)(f.batch * f.H)), dim3(Cfg::NTH), s, wa) ==
                        hipSuccess
                    ? SSD_OK
                    : SSD_ERR_HIP;

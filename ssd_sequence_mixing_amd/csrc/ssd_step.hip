@@ -6,58 +6,68 @@
 //   y[p] = sum_n s[p,n] C[g,n] + D[h] x[p]
 //
 // The state is the only large operand: the kernel streams it once in and
-// once out with 16-byte accesses. A row of N fp32 values is split over N/4
-// lanes; the dot product with C is reduced across those lanes with
-// cross-lane shuffles. Each thread keeps UNROLL rows' loads in flight.
+// once out with 16-byte non-temporal accesses (it is not reused by this
+// step, so it should not displace anything in the caches). A row of N fp32
+// values is split over N/4 lanes; the dot product with C is reduced across
+// those lanes with cross-lane shuffles. Each work-group covers RPB rows of
+// one (batch, head), so the head's scalars (dt, A, D, group) are uniform
+// and every lane keeps two rows' loads in flight.
 #include "ssd_common.h"
 #include "ssd_internal.h"
 
 namespace ssd {
 
-template <typename TI, int N, int UNROLL>
-__global__ __launch_bounds__(256) void k_step(StepArgs a, int64_t rows) {
+constexpr int kStepThreads = 256;
+constexpr int kStepUnroll = 2;
+
+template <typename TI, int N>
+struct StepShape {
+    static constexpr int TPR = N / 4;                 // lanes per state row
+    static constexpr int RPW = 64 / TPR;              // rows per wavefront per pass
+    static constexpr int RPB = (kStepThreads / 64) * RPW * kStepUnroll;  // rows per work-group
+};
+
+template <typename TI, int N>
+__global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a, int pblocks) {
     using Tr = Traits<TI>;
-    constexpr int ES = Tr::kBytes;
-    constexpr int TPR = N / 4;          // lanes per state row
-    constexpr int RPW = 64 / TPR;       // rows per wavefront per pass
-    constexpr int RPB = 4 * RPW * UNROLL;
+    using S = StepShape<TI, N>;
+    constexpr int TPR = S::TPR, RPW = S::RPW, RPB = S::RPB;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int sub = lane / TPR, c4 = lane % TPR;
     const int P = (int)a.P, H = (int)a.H, G = (int)a.G;
-    const int64_t row0 = (int64_t)blockIdx.x * RPB;
+    // work-group -> (batch*head, block of rows); all of it scalar
+    const int64_t bh = blockIdx.x / pblocks;
+    const int pb = blockIdx.x - (int)(bh * pblocks);
+    const int64_t bb = bh / H;
+    const int h = (int)(bh - bb * H);
+    const int g = (h * G) / H;
+    const float dtv = Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[bh]);
+    const float dec = fast_exp2(dtv * a.A[h] * kLog2e);
+    const float Dh = a.D[h];
+    float *srow = a.state + bh * P * N;
 
-    f32x4 s[UNROLL];
-    int64_t rr[UNROLL];
+    int p[kStepUnroll];
+    f32x4 s[kStepUnroll];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-        rr[u] = row0 + (int64_t)(u * 4 + w) * RPW + sub;
-        if (rr[u] < rows)
-            s[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.state + rr[u] * N) + c4);
-        else
-            s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kStepUnroll; ++u) {
+        p[u] = pb * RPB + (u * (kStepThreads / 64) + w) * RPW + sub;
+        s[u] = (p[u] < P)
+                   ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(srow + (int64_t)p[u] * N) + c4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const TI *bp = reinterpret_cast<const TI *>(a.B) + (bb * G + g) * N + 4 * c4;
+    const TI *cp = reinterpret_cast<const TI *>(a.C) + (bb * G + g) * N + 4 * c4;
+    float bv[4], cv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        bv[e] = Tr::to_f32(bp[e]);
+        cv[e] = Tr::to_f32(cp[e]);
     }
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-        const int64_t R = rr[u];
-        const bool ok = R < rows;
-        const int64_t Rc = ok ? R : 0;
-        const int64_t bh = Rc / P;
-        const int p = (int)(Rc - bh * P);
-        const int64_t bb = bh / H;
-        const int h = (int)(bh - bb * H);
-        const int g = (h * G) / H;
-        const float dtv = Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[bh]);
-        const float xv = Tr::to_f32(reinterpret_cast<const TI *>(a.x)[bh * P + p]);
-        const float dec = fast_exp2(dtv * a.A[h] * kLog2e);
+    for (int u = 0; u < kStepUnroll; ++u) {
+        const bool ok = p[u] < P;
+        const float xv = ok ? Tr::to_f32(reinterpret_cast<const TI *>(a.x)[bh * P + p[u]]) : 0.f;
         const float uin = dtv * xv;
-        const TI *bp = reinterpret_cast<const TI *>(a.B) + (bb * G + g) * N + 4 * c4;
-        const TI *cp = reinterpret_cast<const TI *>(a.C) + (bb * G + g) * N + 4 * c4;
-        float bv[4], cv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bv[e] = Tr::to_f32(bp[e]);
-            cv[e] = Tr::to_f32(cp[e]);
-        }
         f32x4 sn;
         float part = 0.f;
 #pragma unroll
@@ -65,23 +75,20 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a, int64_t rows) {
             sn[e] = dec * s[u][e] + uin * bv[e];
             part += sn[e] * cv[e];
         }
-        if (ok) __builtin_nontemporal_store(sn, reinterpret_cast<f32x4 *>(a.state + R * N) + c4);
+        if (ok) __builtin_nontemporal_store(sn, reinterpret_cast<f32x4 *>(srow + (int64_t)p[u] * N) + c4);
 #pragma unroll
         for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (ok && c4 == 0) {
-            const float yv = part + a.D[h] * xv;
-            reinterpret_cast<TI *>(a.y)[bh * P + p] = Tr::from_f32(yv);
-        }
+        if (ok && c4 == 0) reinterpret_cast<TI *>(a.y)[bh * P + p[u]] = Tr::from_f32(part + Dh * xv);
     }
 }
 
 template <typename TI, int N>
 static ssd_status run_step(const StepArgs &a, hipStream_t s) {
-    constexpr int UNROLL = 4;
-    constexpr int RPB = 4 * (64 / (N / 4)) * UNROLL;
-    const int64_t rows = a.batch * a.H * a.P;
-    const int64_t blocks = (rows + RPB - 1) / RPB;
-    return launch(k_step<TI, N, UNROLL>, dim3((unsigned)blocks), dim3(256), s, a, rows) == hipSuccess
+    constexpr int RPB = StepShape<TI, N>::RPB;
+    const int pblocks = (int)((a.P + RPB - 1) / RPB);
+    const int64_t blocks = a.batch * a.H * pblocks;
+    return launch(k_step<TI, N>, dim3((unsigned)blocks), dim3(kStepThreads), s, a, pblocks) ==
+                   hipSuccess
                ? SSD_OK
                : SSD_ERR_HIP;
 }
