@@ -46,13 +46,15 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     const int lds = ssd::fwd_lds_bytes((ssd_dtype)dtype, chunk, headdim, dstate);
     if (lds < 0 || lds > ssd::kMaxLds) return SSD_ERR_UNSUPPORTED;
     const int64_t es = esize((ssd_dtype)dtype);
-    // 32-bit buffer offsets: every per-batch slab and the C B^T buffer stay under 2 GiB
+    // 32-bit buffer offsets: every per-batch slab, padded to whole chunks, and
+    // the C B^T buffer stay under 2 GiB, so an offset past the end of a slab
+    // (a token past T) can never wrap back into range
     if (seqlen > kTwoGiB || nheads > 65536) return SSD_ERR_UNSUPPORTED;
-    if (seqlen * nheads * headdim * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    if (seqlen * ngroups * dstate * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    if (seqlen * nheads * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     const int64_t nC = (seqlen + chunk - 1) / chunk;
     const int64_t Tpad = nC * chunk;
+    if (Tpad * nheads * headdim * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    if (Tpad * ngroups * dstate * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    if (Tpad * nheads * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     const int64_t nt = chunk / 64, np = nt * (nt + 1) / 2;
     lay->nC = nC;
     lay->Tpad = Tpad;

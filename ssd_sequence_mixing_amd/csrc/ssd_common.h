@@ -53,6 +53,13 @@ __device__ __forceinline__ uint32_t buf_ld32(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint16_t buf_ld16(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
+// The same with a scalar (wave-uniform) offset added: voff per lane, soff per wave.
+__device__ __forceinline__ u32x4 buf_ld128s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st128s(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
 __device__ __forceinline__ void buf_st128(u32x4 v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
@@ -94,6 +101,9 @@ template <> struct Traits<bf16> {
     __device__ static __forceinline__ frag load_frag(rsrc_t r, uint32_t off) {
         return __builtin_bit_cast(bf16x8, buf_ld128(r, off));
     }
+    __device__ static __forceinline__ frag load_frag_s(rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __builtin_bit_cast(bf16x8, buf_ld128s(r, voff, soff));
+    }
     __device__ static __forceinline__ frag lds_frag(const bf16 *p) {
         return *reinterpret_cast<const bf16x8 *>(p);
     }
@@ -112,6 +122,15 @@ template <> struct Traits<float> {
     __device__ static __forceinline__ frag load_frag(rsrc_t r, uint32_t off) {
         u32x4 lo = buf_ld128(r, off);
         u32x4 hi = buf_ld128(r, off + 16);
+        f32x4 a = __builtin_bit_cast(f32x4, lo), b = __builtin_bit_cast(f32x4, hi);
+        frag f;
+        f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];
+        f[4] = b[0]; f[5] = b[1]; f[6] = b[2]; f[7] = b[3];
+        return f;
+    }
+    __device__ static __forceinline__ frag load_frag_s(rsrc_t r, uint32_t voff, uint32_t soff) {
+        u32x4 lo = buf_ld128s(r, voff, soff);
+        u32x4 hi = buf_ld128s(r, voff + 16, soff);
         f32x4 a = __builtin_bit_cast(f32x4, lo), b = __builtin_bit_cast(f32x4, hi);
         frag f;
         f[0] = a[0]; f[1] = a[1]; f[2] = a[2]; f[3] = a[3];

@@ -9,8 +9,10 @@
 //
 // Three kernels, launched in this order on the caller's stream:
 //   k_dt_cumsum   per (batch, chunk, head block): dt -> chunk-local inclusive
-//                 prefix sum of dt*A in base 2 (cs2), plus dt re-laid out as
-//                 (batch, head, token) fp32, both read contiguously later.
+//                 prefix sum of dt*A in base 2 (cs2), and cs' = cs2 - log2(dt),
+//                 both laid out (batch, head, token) fp32. With cs', the
+//                 weight dt_j exp2(cs_i - cs_j) of token j seen from token i is
+//                 one exponential, exp2(cs_i - cs'_j).
 //   k_chunk_cb    per (batch, chunk, group, row tile): G = C B^T for the lower
 //                 64 x 64 tiles of each chunk's Q x Q block (matrix cores).
 //                 C B^T depends on the group only, so it is formed once and
@@ -107,7 +109,9 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(const TI *__restrict__ dt,
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             o[k] = s[k] + excl;
-            od[k] = d[k];
+            // log2(0) = -inf, so a zero step (or a padded token) gets cs' = +inf
+            // and every factor exp2(x - cs') built from it is exactly 0
+            od[k] = s[k] + excl - __builtin_amdgcn_logf(d[k]);
         }
     }
 }
@@ -186,6 +190,24 @@ __global__ __launch_bounds__(256) void k_chunk_cb(const TI *__restrict__ Bm,
 
 // ---------------------------------------------------------------------------
 // k_chunk_walk
+//
+// One work-group per (batch, head) walks the chunks in order, 64-token tile by
+// tile, with the P x N fp32 state in matrix-core accumulators. Its 8
+// wavefronts take two roles that run side by side on every SIMD:
+//   output waves (0-3), 16 output rows each: load this tile's C rows and C B^T
+//     rows; form exp2(cs_i) C_i h_in^T (h_in fragments held in registers for
+//     the chunk) + the chunk's earlier tiles through C B^T and the scaled X
+//     copy (factorised decay) + the masked diagonal block + D x; store Y.
+//   state waves (4-7), a quarter of the state's columns each: issue the next
+//     tile's X, B and log-decay loads; update h <- decay h + Xs^T B with this
+//     tile (Xs: X scaled by exp2(cs_e - cs'_j), e = the tile's last token);
+//     at a chunk's end write h as the next chunk's h_in copy; stage the next
+//     tile into the other LDS slots.
+// One barrier per tile (two where a buffer cannot be doubled).
+// LDS: a ring of NT+1 scaled-X tile slots (a chunk's earlier tiles stay
+// readable while the next is staged), two unscaled-X slots, B^T and h_in
+// copies (doubled when they fit), per-wave output rows, and two chunk-sized
+// log-decay buffers.
 // ---------------------------------------------------------------------------
 template <typename TI, int Q, int P, int N>
 struct WalkCfg {
@@ -194,46 +216,38 @@ struct WalkCfg {
     static constexpr int NP = NT * (NT + 1) / 2;
     static constexpr int PB = P / 16;
     static constexpr int NB = N / 16;
-    static constexpr int NW = 4;                  // wavefronts per work-group
-    static constexpr int NTH = 64 * NW;
-    static constexpr int NBW = (NB + NW - 1) / NW;  // state n-blocks per wave
-    static constexpr int WPR = NW / 4;              // waves sharing one 16-row output block
-    static constexpr int PBW = (PB + WPR - 1) / WPR;  // output p-blocks per wave
-    static constexpr int NK = (N + 31) / 32;
+    static constexpr int NTH = 512;                  // 4 output + 4 state wavefronts
+    static constexpr int NBW = (NB + 3) / 4;         // state n-blocks per state wave
+    static constexpr int NK = (N + 31) / 32;         // 32-wide k-steps over N
     static constexpr int PAD = 16 / ES;
-    static constexpr int XT_LD = Q + PAD;        // X^T rows (p), token-contiguous, whole chunk
-    static constexpr int BT_LD = 64 + PAD;       // B^T rows (n), token-contiguous, one tile
-    static constexpr int HS_LD = NK * 32 + PAD;  // state rows (p), n-contiguous
-    static constexpr int YS_LD = P + PAD;        // output staging rows (token)
-    // staging units per 64-token tile: 4 consecutive tokens x 8 consecutive columns
-    static constexpr int UX = 16 * (P / 8);
+    static constexpr int XS = NT + 1;                // scaled-X tile slots (ring)
+    static constexpr int XH_LD = XS * 64 + PAD;
+    static constexpr int XT_LD = 2 * 64 + PAD;       // unscaled X: two tile slots
+    static constexpr int BT_LD = 64 + PAD;
+    static constexpr int HS_LD = NK * 32 + PAD;
+    static constexpr int YS_LD = P + PAD;
+    static constexpr int UX = 16 * (P / 8);          // staging units: 4 tokens x 8 columns
     static constexpr int UB = 16 * (N / 8);
-    static constexpr int RX = (UX + NTH - 1) / NTH;
-    static constexpr int RB = (UB + NTH - 1) / NTH;
-    static constexpr int XT_OFF = 0;
+    static constexpr int RX = (UX + 255) / 256;      // units per state-wave thread
+    static constexpr int RB = (UB + 255) / 256;
+    static constexpr bool kHSReg = PB * NK * ES <= 32;  // h_in fragments kept in registers
+    static constexpr int XH_OFF = 0;
+    static constexpr int XH_BYTES = P * XH_LD * ES;
+    static constexpr int XT_OFF = XH_OFF + XH_BYTES;
     static constexpr int XT_BYTES = P * XT_LD * ES;
-    static constexpr int XH_OFF = XT_OFF + XT_BYTES;
-    static constexpr int BT_OFF = XH_OFF + XT_BYTES;
-    static constexpr int BT_BYTES = N * BT_LD * ES;
-    static constexpr int HS_OFF = BT_OFF + BT_BYTES;
-    static constexpr int HS_BYTES = P * HS_LD * ES;
-    static constexpr int YS_OFF = HS_OFF + HS_BYTES;
+    static constexpr int YS_OFF = XT_OFF + XT_BYTES;
     static constexpr int YS_BYTES = 64 * YS_LD * ES;
-    static constexpr int CS_OFF = YS_OFF + YS_BYTES;  // 2 buffers x (cs2[Q], dt[Q]) fp32
-    static constexpr int LDS = CS_OFF + 2 * 2 * Q * 4;
+    static constexpr int CS_OFF = YS_OFF + YS_BYTES;  // 2 x (cs2[Q], cs'[Q]) fp32
+    static constexpr int CS_BYTES = 2 * 2 * Q * 4;
+    static constexpr int HS_OFF = CS_OFF + CS_BYTES;
+    static constexpr int HS_BYTES = P * HS_LD * ES;
+    static constexpr int BT_BYTES = N * BT_LD * ES;
+    static constexpr int BASE = HS_OFF + HS_BYTES + BT_BYTES;
+    static constexpr bool kBT2 = BASE + BT_BYTES <= 160 * 1024;             // double B^T
+    static constexpr bool kHS2 = BASE + (kBT2 ? BT_BYTES : 0) + HS_BYTES <= 160 * 1024;
+    static constexpr int BT_OFF = HS_OFF + (kHS2 ? 2 : 1) * HS_BYTES;
+    static constexpr int LDS = BT_OFF + (kBT2 ? 2 : 1) * BT_BYTES;
     static constexpr bool kFits = LDS <= 160 * 1024;
-};
-
-// Global data one 64-token tile needs, held in registers so that the next
-// tile's loads are in flight while the current tile computes.
-template <typename TI, int Q, int P, int N>
-struct WalkRegs {
-    using Cfg = WalkCfg<TI, Q, P, N>;
-    using frag = typename Traits<TI>::frag;
-    frag xr[Cfg::RX][4];   // X: 4 tokens x 8 columns per staging unit
-    frag br[Cfg::RB][4];   // B: 4 tokens x 8 columns per staging unit
-    frag cf[Cfg::NK];      // C rows of this lane's A row (state -> output)
-    frag gf[Cfg::NT][2];   // C B^T rows of tiles J <= I (two 32-wide k-steps each)
 };
 
 template <int... Is, typename F>
@@ -256,28 +270,44 @@ __device__ __forceinline__ void lds_store4(TI *p, TI v0, TI v1, TI v2, TI v3) {
     }
 }
 
+template <typename TI>
+__device__ __forceinline__ void lds_load4(TI *d, const TI *p) {
+    if constexpr (sizeof(TI) == 2) {
+        *reinterpret_cast<uint64_t *>(d) = *reinterpret_cast<const uint64_t *>(p);
+    } else {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
+    }
+}
+
+// A compiler-level ordering point for LDS traffic within one wavefront: LDS
+// operations of a wavefront execute in order, so a read issued after a write
+// sees it once the compiler keeps them in that order.
+__device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
 template <typename TI, int Q, int P, int N>
 __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(WalkArgs a) {
     using Tr = Traits<TI>;
     using Cfg = WalkCfg<TI, Q, P, N>;
-    using Regs = WalkRegs<TI, Q, P, N>;
     using frag = typename Tr::frag;
     constexpr int ES = Cfg::ES, NT = Cfg::NT, NP = Cfg::NP, PB = Cfg::PB, NB = Cfg::NB;
-    constexpr int NW = Cfg::NW, NTH = Cfg::NTH, NBW = Cfg::NBW, PBW = Cfg::PBW, NK = Cfg::NK;
-    constexpr int WPR = Cfg::WPR;
-    constexpr int XT_LD = Cfg::XT_LD, BT_LD = Cfg::BT_LD, HS_LD = Cfg::HS_LD, YS_LD = Cfg::YS_LD;
+    constexpr int NBW = Cfg::NBW, NK = Cfg::NK, XS = Cfg::XS;
+    constexpr int RX = Cfg::RX, RB = Cfg::RB, UX = Cfg::UX, UB = Cfg::UB;
+    constexpr int XH_LD = Cfg::XH_LD, XT_LD = Cfg::XT_LD, BT_LD = Cfg::BT_LD, HS_LD = Cfg::HS_LD;
+    constexpr int YS_LD = Cfg::YS_LD;
+    constexpr bool kHSReg = Cfg::kHSReg, kBT2 = Cfg::kBT2, kHS2 = Cfg::kHS2;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
-    TI *XT = reinterpret_cast<TI *>(smem + Cfg::XT_OFF);
     TI *XH = reinterpret_cast<TI *>(smem + Cfg::XH_OFF);
-    TI *BT = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);
-    TI *HS = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);
+    TI *XT = reinterpret_cast<TI *>(smem + Cfg::XT_OFF);
     TI *YS = reinterpret_cast<TI *>(smem + Cfg::YS_OFF);
-    float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);  // [buf][cs2 Q | dt Q]
+    float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);  // [buf][cs2 Q | cs' Q]
+    TI *HSB = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);
+    TI *BTB = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);
 
     const int H = a.H, G = a.G, T = a.T, nC = a.nC;
     // blockIdx -> (b, h): consecutive logical indices share an XCD (dispatch
     // goes round-robin over the 8 XCDs), so the heads of one batch element,
-    // which read the same B, C and G, share one L2.
+    // which read the same B, C and C B^T, share one L2.
     const int W = a.batch * H;
     int L = blockIdx.x;
     if ((W & 7) == 0) L = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
@@ -285,12 +315,11 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     const int g = (h * G) / H;
 
     const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+    const bool out_wave = wv < 4;
+    const int w = wv & 3;              // index within the role
+    const int st = tid & 255;          // thread index within the role
     const int r = lane & 15, kg = lane >> 4;
-    const int rb = w & 3;   // output row block (16 tokens) of this wave
-    const int ph = w >> 2;  // output p-blocks ph, ph + WPR, ... of this wave
-    // X staging units go to threads 0.., B staging units to threads ..NTH-1
-    const int xu0 = tid, bu0 = NTH - 1 - tid;
 
     const size_t xslab = (size_t)T * H * P * ES;
     const size_t bslab = (size_t)T * G * N * ES;
@@ -300,269 +329,304 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(a.C) + b * bslab, (uint32_t)bslab);
     const rsrc_t rg = make_rsrc(a.Gbuf, a.g_bytes);
     const float *cs_row = a.cs2 + ((size_t)b * H + h) * a.Tpad;
-    const float *dt_row = a.dtf + ((size_t)b * H + h) * a.Tpad;
+    const float *cp_row = a.dtf + ((size_t)b * H + h) * a.Tpad;  // cs' = cs2 - log2(dt)
     const float Dh = a.D[h];
+    const uint32_t x_tok = (uint32_t)(H * P * ES), b_tok = (uint32_t)(G * N * ES);
 
-    // issue every global load tile (c, I) needs, into registers
-    auto load_tile = [&](Regs &R, int c, auto Ic) {
-        constexpr int I = decltype(Ic)::value;
-        const int t0 = c * Q, tile0 = I * 64;
+    // ---- state-wave data: staging offsets and registers ----
+    uint32_t vx[RX], vb[RB];
 #pragma unroll
-        for (int k = 0; k < Cfg::RX; ++k) {
-            const int u = xu0 + NTH * k;
-            const int tq = u % 16, po = (u / 16) % (P / 8);
+    for (int k = 0; k < RX; ++k) {
+        const int u = st + 256 * k;
+        vx[k] = (uint32_t)(4 * (u % 16)) * x_tok + (uint32_t)(8 * ((u / 16) % (P / 8)) * ES);
+    }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + tile0 + 4 * tq + i;
-                R.xr[k][i] = Tr::load_frag(
-                    rx, oob_if(u >= Cfg::UX || t >= T, (uint32_t)(((t * H + h) * P + 8 * po) * ES)));
+    for (int k = 0; k < RB; ++k) {
+        const int u = st + 256 * k;
+        vb[k] = (uint32_t)(4 * (u % 16)) * b_tok + (uint32_t)(8 * ((u / 16) % (N / 8)) * ES);
+    }
+    // staging units are wave-uniform whenever their count is a multiple of 64
+    auto x_unit = [&](int k) { return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (st + 256 * k < UX); };
+    auto b_unit = [&](int k) { return (UB % 64 == 0) ? (64 * w + 256 * k < UB) : (st + 256 * k < UB); };
+    frag xr[RX][4], br[RB][4];
+    f32x4 xcp[RX];    // cs' of the unit's 4 tokens
+    float xce = 0.f;  // cs2 of the staged tile's last token
+    auto issue_stage = [&](int tt) {  // X, B and log-decays of the tile starting at token tt
+        const uint32_t sx = (uint32_t)(tt * H + h) * (uint32_t)(P * ES);
+        const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
+#pragma unroll
+        for (int k = 0; k < RX; ++k)
+            if (x_unit(k)) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xr[k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
+                xcp[k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % 16));
             }
-        }
+        xce = cs_row[tt + 63];
 #pragma unroll
-        for (int k = 0; k < Cfg::RB; ++k) {
-            const int u = bu0 + NTH * k;
-            const int tq = u % 16, no = (u / 16) % (N / 8);
+        for (int k = 0; k < RB; ++k)
+            if (b_unit(k)) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = t0 + tile0 + 4 * tq + i;
-                R.br[k][i] = Tr::load_frag(
-                    rbm, oob_if(u >= Cfg::UB || t >= T, (uint32_t)(((t * G + g) * N + 8 * no) * ES)));
+                for (int i = 0; i < 4; ++i) br[k][i] = Tr::load_frag_s(rbm, vb[k] + i * b_tok, sb);
             }
-        }
-        const int ti = t0 + tile0 + 16 * rb + r;
+    };
+    auto stage = [&](int xslot, int tslot) {
+        TI *BT = BTB + (kBT2 ? tslot : 0) * N * BT_LD;
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            const int n0 = kk * 32 + 8 * kg;
-            R.cf[kk] = Tr::load_frag(
-                rc, oob_if(ti >= T || n0 >= N, (uint32_t)(((ti * G + g) * N + n0) * ES)));
-        }
+        for (int k = 0; k < RX; ++k)
+            if (x_unit(k)) {
+                const int u = st + 256 * k;
+                const int tq = u % 16, po = (u / 16) % (P / 8);
+                float sc[4];
 #pragma unroll
-        for (int J = 0; J <= I; ++J) {
-            const size_t gt = ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, J)) * 4096;
+                for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce - xcp[k][i]);
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-                R.gf[J][k2] =
-                    Tr::load_frag(rg, (uint32_t)((gt + (16 * rb + r) * 64 + 32 * k2 + 8 * kg) * ES));
-        }
+                for (int e = 0; e < 8; ++e) {
+                    const int row = 8 * po + e;
+                    lds_store4<TI>(XT + row * XT_LD + tslot * 64 + 4 * tq, xr[k][0][e], xr[k][1][e],
+                                   xr[k][2][e], xr[k][3][e]);
+                    lds_store4<TI>(XH + row * XH_LD + xslot * 64 + 4 * tq,
+                                   Tr::from_f32(Tr::frag_get(xr[k][0], e) * sc[0]),
+                                   Tr::from_f32(Tr::frag_get(xr[k][1], e) * sc[1]),
+                                   Tr::from_f32(Tr::frag_get(xr[k][2], e) * sc[2]),
+                                   Tr::from_f32(Tr::frag_get(xr[k][3], e) * sc[3]));
+                }
+            }
+#pragma unroll
+        for (int k = 0; k < RB; ++k)
+            if (b_unit(k)) {
+                const int u = st + 256 * k;
+                const int tq = u % 16, no = (u / 16) % (N / 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq, br[k][0][e], br[k][1][e],
+                                   br[k][2][e], br[k][3][e]);
+            }
+    };
+    // state accumulators (state waves): tile (pb, nb = w + 4j), rows p = 16pb + 4kg + i, col n = 16nb + r
+    f32x4 hacc[PB][NBW];
+    auto write_hs = [&](TI *HSw) {
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                const int nb = w + 4 * j;
+                if (nb < NB) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        HSw[(16 * pb + 4 * kg + i) * HS_LD + 16 * nb + r] = Tr::from_f32(hacc[pb][j][i]);
+                }
+            }
     };
 
-    // state accumulators: tile (pb, nb = w + NW*j), rows p = 16pb + 4kg + i, col n = 16nb + r
-    f32x4 hacc[PB][NBW];
+    // ---- output-wave data ----
+    uint32_t vc[NK], vg[2];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            const int nb = w + NW * j;
-            f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (a.init && nb < NB) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int p = 16 * pb + 4 * kg + i, n = 16 * nb + r;
-                    v[i] = a.init[(((size_t)b * H + h) * P + p) * N + n];
-                }
-            }
-            hacc[pb][j] = v;
-        }
-
-    Regs R[2];
-    for (int k = tid; k < Q; k += NTH) {
-        CSB[k] = cs_row[k];
-        CSB[Q + k] = dt_row[k];
+    for (int kk = 0; kk < NK; ++kk) {
+        const int n0 = kk * 32 + 8 * kg;
+        vc[kk] = oob_if(n0 >= N, (uint32_t)(16 * w + r) * b_tok + (uint32_t)(n0 * ES));
     }
-    load_tile(R[0], 0, std::integral_constant<int, 0>{});
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) vg[k2] = (uint32_t)(((16 * w + r) * 64 + 32 * k2 + 8 * kg) * ES);
+    frag hsf[kHSReg ? PB : 1][kHSReg ? NK : 1];
 
-    for (int c = 0; c < nC; ++c) {
-        const int t0 = c * Q;
-        const float *CSL = CSB + (c & 1) * 2 * Q;
-        const float *DTL = CSL + Q;
-        float *CSN = CSB + ((c + 1) & 1) * 2 * Q;  // next chunk's slot
-        float csn = 0.f, dtn = 0.f;
-        static_for<NT>([&](auto Ic) {
-            constexpr int I = decltype(Ic)::value;
-            constexpr int cur = (NT == 1) ? 0 : (I & 1);
-            constexpr int nxt = cur ^ 1;
-            Regs &RC = R[cur];
-            const int tile0 = I * 64;
-            if constexpr (I == 0) {
-                // state entering this chunk -> matrix-core operand copy
+    // ---- prologue ----
+    if (!out_wave) {
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb)
+        for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-                    for (int j = 0; j < NBW; ++j) {
-                        const int nb = w + NW * j;
-                        if (nb < NB) {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                HS[(16 * pb + 4 * kg + i) * HS_LD + 16 * nb + r] =
-                                    Tr::from_f32(hacc[pb][j][i]);
-                        }
-                    }
-                if constexpr (N % 32 != 0) {
-                    for (int k = tid; k < P * (NK * 32 - N); k += NTH) {
-                        const int p = k / (NK * 32 - N), n = N + k % (NK * 32 - N);
-                        HS[p * HS_LD + n] = Tr::from_f32(0.f);
-                    }
-                }
-            }
-            const float cs_e = CSL[tile0 + 63];  // tile's last token
-            // ---- stage the prefetched X tile (unscaled and column-scaled) and B tile
-#pragma unroll
-            for (int k = 0; k < Cfg::RX; ++k) {
-                const int u = xu0 + NTH * k;
-                // wave-uniform whenever UX is a multiple of 64
-                if ((Cfg::UX % 64 == 0) ? (64 * w + NTH * k < Cfg::UX) : (u < Cfg::UX)) {
-                    const int tq = u % 16, po = u / 16;
-                    const int jc = tile0 + 4 * tq;
-                    float sc[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) sc[i] = DTL[jc + i] * fast_exp2(cs_e - CSL[jc + i]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int row = 8 * po + e;
-                        lds_store4<TI>(XT + row * XT_LD + jc, RC.xr[k][0][e], RC.xr[k][1][e],
-                                       RC.xr[k][2][e], RC.xr[k][3][e]);
-                        lds_store4<TI>(XH + row * XT_LD + jc,
-                                       Tr::from_f32(Tr::frag_get(RC.xr[k][0], e) * sc[0]),
-                                       Tr::from_f32(Tr::frag_get(RC.xr[k][1], e) * sc[1]),
-                                       Tr::from_f32(Tr::frag_get(RC.xr[k][2], e) * sc[2]),
-                                       Tr::from_f32(Tr::frag_get(RC.xr[k][3], e) * sc[3]));
-                    }
-                }
-            }
-#pragma unroll
-            for (int k = 0; k < Cfg::RB; ++k) {
-                const int u = bu0 + NTH * k;
-                if ((Cfg::UB % 64 == 0) ? (64 * (NW - 1 - w) + NTH * k < Cfg::UB) : (u < Cfg::UB)) {
-                    const int tq = u % 16, no = u / 16;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq, RC.br[k][0][e],
-                                       RC.br[k][1][e], RC.br[k][2][e], RC.br[k][3][e]);
-                }
-            }
-            __syncthreads();
-
-            // ---- prefetch the next tile while this one computes
-            // (past the last chunk the loads fall outside every range and return 0)
-            if constexpr (I + 1 < NT) {
-                load_tile(R[nxt], c, std::integral_constant<int, I + 1>{});
-            } else {
-                load_tile(R[nxt], c + 1, std::integral_constant<int, 0>{});
-            }
-            if constexpr (I == 0) {
-                if (c + 1 < nC && tid < Q) {  // Q <= NTH: one value per thread
-                    csn = cs_row[t0 + Q + tid];
-                    dtn = dt_row[t0 + Q + tid];
-                }
-            }
-
-            // ---- output rows tile0 + 16rb .. +15 (A-operand row r), p-blocks ph, ph + 2, ...
-            const int irow = tile0 + 16 * rb + r;  // chunk-local token of this lane's A row
-            f32x4 acc[PBW];
-#pragma unroll
-            for (int j = 0; j < PBW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // state -> output: C_i . h_in
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const int n0 = kk * 32 + 8 * kg;
-#pragma unroll
-                for (int j = 0; j < PBW; ++j) {
-                    const int pb = ph + WPR * j;
-                    if (pb < PB) {
-                        const frag hb = Tr::lds_frag(HS + (16 * pb + r) * HS_LD + n0);
-                        acc[j] = Tr::mma(RC.cf[kk], hb, acc[j]);
-                    }
-                }
-            }
-            float cs_rows[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) cs_rows[i] = CSL[tile0 + 16 * rb + 4 * kg + i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float f = fast_exp2(cs_rows[i]);
-#pragma unroll
-                for (int j = 0; j < PBW; ++j) acc[j][i] *= f;
-            }
-            // earlier tiles of this chunk: G_IJ (unmasked, J < I) times the scaled X copy
-#pragma unroll
-            for (int J = 0; J < I; ++J) {
-                f32x4 tmp[PBW];
-#pragma unroll
-                for (int j = 0; j < PBW; ++j) tmp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-                    for (int j = 0; j < PBW; ++j) {
-                        const int pb = ph + WPR * j;
-                        if (pb < PB) {
-                            const frag xb =
-                                Tr::lds_frag(XH + (16 * pb + r) * XT_LD + J * 64 + 32 * k2 + 8 * kg);
-                            tmp[j] = Tr::mma(RC.gf[J][k2], xb, tmp[j]);
-                        }
-                    }
-                }
-                const float cs_je = CSL[J * 64 + 63];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float f = fast_exp2(cs_rows[i] - cs_je);
-#pragma unroll
-                    for (int j = 0; j < PBW; ++j) acc[j][i] += f * tmp[j][i];
-                }
-            }
-            // diagonal tile: mask built per element, j > i selected to zero
-            {
-                const float cs_i = CSL[irow];
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    if (32 * k2 > 16 * rb + 15) continue;  // wave-uniform: block above the diagonal
-                    frag ma;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int jc = tile0 + 32 * k2 + 8 * kg + e;
-                        const float v =
-                            Tr::frag_get(RC.gf[I][k2], e) * fast_exp2(cs_i - CSL[jc]) * DTL[jc];
-                        Tr::frag_set(ma, e, (jc <= irow) ? v : 0.f);
-                    }
-#pragma unroll
-                    for (int j = 0; j < PBW; ++j) {
-                        const int pb = ph + WPR * j;
-                        if (pb < PB) {
-                            const frag xb =
-                                Tr::lds_frag(XT + (16 * pb + r) * XT_LD + tile0 + 32 * k2 + 8 * kg);
-                            acc[j] = Tr::mma(ma, xb, acc[j]);
-                        }
-                    }
-                }
-            }
-            // skip term and output staging
-#pragma unroll
-            for (int j = 0; j < PBW; ++j) {
-                const int pb = ph + WPR * j;
-                if (pb < PB) {
+            for (int j = 0; j < NBW; ++j) {
+                const int nb = w + 4 * j;
+                f32x4 v = {0.f, 0.f, 0.f, 0.f};
+                if (a.init && nb < NB) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int rl = 16 * rb + 4 * kg + i;  // tile-local token
-                        const float xv = Tr::to_f32(XT[(16 * pb + r) * XT_LD + tile0 + rl]);
-                        YS[rl * YS_LD + 16 * pb + r] = Tr::from_f32(acc[j][i] + Dh * xv);
+                        const int p = 16 * pb + 4 * kg + i, n = 16 * nb + r;
+                        v[i] = a.init[(((size_t)b * H + h) * P + p) * N + n];
                     }
                 }
+                hacc[pb][j] = v;
             }
-            __syncthreads();
-            {
-                constexpr int VPR = P * ES / 16;  // 16-byte vectors per row
-#pragma unroll
-                for (int v = tid; v < 64 * VPR; v += NTH) {
-                    const int rl = v / VPR, cv = v % VPR;
-                    const int t = t0 + tile0 + rl;
-                    const u32x4 d =
-                        *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
-                                                         rl * YS_LD * ES + cv * 16);
-                    buf_st128(d, ry, oob_if(t >= T, (uint32_t)((t * H + h) * P * ES + cv * 16)));
-                }
-            }
+        write_hs(HSB);
+        issue_stage(0);
+        stage(0, 0);
+    }
+    for (int k = tid; k < Q; k += Cfg::NTH) {
+        CSB[k] = cs_row[k];
+        CSB[Q + k] = cp_row[k];
+    }
+    if constexpr (N % 32 != 0) {
+        for (int k = tid; k < (kHS2 ? 2 : 1) * P * (NK * 32 - N); k += Cfg::NTH) {
+            const int q = k / (P * (NK * 32 - N)), kr = k % (P * (NK * 32 - N));
+            const int p = kr / (NK * 32 - N), n = N + kr % (NK * 32 - N);
+            HSB[q * P * HS_LD + p * HS_LD + n] = Tr::from_f32(0.f);
+        }
+    }
+    __syncthreads();
 
-            // ---- state update for this tile: h <- decay * h + (scaled X)^T B
-            {
+    // Each wavefront runs one role for the whole walk (the role is uniform
+    // over the wavefront); both loops reach the same barriers, one per tile
+    // (two where kMidSync), so the work-group stays in step.
+    constexpr bool kMidSync = !kBT2 || (!kHS2 && (NT == 1 || !kHSReg));
+    if (out_wave) {
+        for (int c = 0; c < nC; ++c) {
+            const int t0 = c * Q;
+            const float *CSL = CSB + (c & 1) * 2 * Q;  // cs2 of this chunk
+            const float *CPL = CSL + Q;                // cs' of this chunk
+            const TI *HSr = HSB + (kHS2 ? (c & 1) : 0) * P * HS_LD;
+            static_for<NT>([&](auto Ic) {
+                constexpr int I = decltype(Ic)::value;
+                const int tile0 = I * 64;
+                const int tau = c * NT + I;
+                const TI *XTc = XT + (tau & 1) * 64;
+                // ================= output rows tile0 + 16w .. +15 =================
+                frag cf[NK], gf[I + 1][2];
+                {
+                    const uint32_t sb = (uint32_t)((t0 + tile0) * G + g) * (uint32_t)(N * ES);
+#pragma unroll
+                    for (int kk = 0; kk < NK; ++kk) cf[kk] = Tr::load_frag_s(rc, vc[kk], sb);
+#pragma unroll
+                    for (int J = 0; J <= I; ++J) {
+                        const uint32_t sg = (uint32_t)(
+                            ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, J)) * 4096 * ES);
+#pragma unroll
+                        for (int k2 = 0; k2 < 2; ++k2) gf[J][k2] = Tr::load_frag_s(rg, vg[k2], sg);
+                    }
+                }
+                if constexpr (I == 0 && kHSReg) {
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                        for (int kk = 0; kk < NK; ++kk)
+                            hsf[pb][kk] = Tr::lds_frag(HSr + (16 * pb + r) * HS_LD + kk * 32 + 8 * kg);
+                }
+                const int irow = tile0 + 16 * w + r;  // chunk-local token of this lane's A row
+                float cs_rows[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) cs_rows[i] = CSL[tile0 + 16 * w + 4 * kg + i];
+                f32x4 acc[PB];
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                // state -> output
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) {
+                        frag hb;
+                        if constexpr (kHSReg) {
+                            hb = hsf[pb][kk];
+                        } else {
+                            hb = Tr::lds_frag(HSr + (16 * pb + r) * HS_LD + kk * 32 + 8 * kg);
+                        }
+                        acc[pb] = Tr::mma(cf[kk], hb, acc[pb]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float f = fast_exp2(cs_rows[i]);
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) acc[pb][i] *= f;
+                }
+                // earlier tiles of this chunk
+#pragma unroll
+                for (int J = 0; J < I; ++J) {
+                    const int js = (tau - I + J) % XS;
+                    f32x4 tmp[PB];
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) tmp[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+                        for (int pb = 0; pb < PB; ++pb) {
+                            const frag xb =
+                                Tr::lds_frag(XH + (16 * pb + r) * XH_LD + js * 64 + 32 * k2 + 8 * kg);
+                            tmp[pb] = Tr::mma(gf[J][k2], xb, tmp[pb]);
+                        }
+                    }
+                    const float cs_je = CSL[J * 64 + 63];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = fast_exp2(cs_rows[i] - cs_je);
+#pragma unroll
+                        for (int pb = 0; pb < PB; ++pb) acc[pb][i] += f * tmp[pb][i];
+                    }
+                }
+                // diagonal tile: weight exp2(cs_i - cs'_j) per element, j > i selected to zero
+                {
+                    const float cs_i = CSL[irow];
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) {
+                        if (32 * k2 > 16 * w + 15) continue;  // wave-uniform: above the diagonal
+                        const int j0 = tile0 + 32 * k2 + 8 * kg;
+                        const f32x4 cpa = *reinterpret_cast<const f32x4 *>(CPL + j0);
+                        const f32x4 cpb = *reinterpret_cast<const f32x4 *>(CPL + j0 + 4);
+                        frag ma;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float cpj = e < 4 ? cpa[e] : cpb[e - 4];
+                            const float v = Tr::frag_get(gf[I][k2], e) * fast_exp2(cs_i - cpj);
+                            Tr::frag_set(ma, e, (j0 + e <= irow) ? v : 0.f);
+                        }
+#pragma unroll
+                        for (int pb = 0; pb < PB; ++pb) {
+                            const frag xb = Tr::lds_frag(XTc + (16 * pb + r) * XT_LD + 32 * k2 + 8 * kg);
+                            acc[pb] = Tr::mma(ma, xb, acc[pb]);
+                        }
+                    }
+                }
+                // skip term, staging through this wave's own rows, store
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    TI xs4[4];
+                    lds_load4<TI>(xs4, XTc + (16 * pb + r) * XT_LD + 16 * w + 4 * kg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rl = 16 * w + 4 * kg + i;  // tile-local token
+                        YS[rl * YS_LD + 16 * pb + r] = Tr::from_f32(acc[pb][i] + Dh * Tr::to_f32(xs4[i]));
+                    }
+                }
+                wave_lds_order();
+                {
+                    constexpr int VPR = P * ES / 16;  // 16-byte vectors per row
+                    const uint32_t sy = (uint32_t)((t0 + tile0 + 16 * w) * H + h) * (uint32_t)(P * ES);
+#pragma unroll
+                    for (int v = lane; v < 16 * VPR; v += 64) {
+                        const int rl = v / VPR, cv = v % VPR;
+                        const u32x4 d =
+                            *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
+                                                             (16 * w + rl) * YS_LD * ES + cv * 16);
+                        buf_st128s(d, ry, (uint32_t)rl * x_tok + (uint32_t)(cv * 16), sy);
+                    }
+                }
+                // a single B^T slot, or a single h_in copy that the output waves
+                // still read this tile, must be read before it is overwritten
+                if constexpr (kMidSync) __syncthreads();
+                __syncthreads();
+            });
+        }
+    } else {
+        float csn = 0.f, cpn = 0.f;
+        for (int c = 0; c < nC; ++c) {
+            const int t0 = c * Q;
+            const float *CSL = CSB + (c & 1) * 2 * Q;  // cs2 of this chunk
+            static_for<NT>([&](auto Ic) {
+                constexpr int I = decltype(Ic)::value;
+                const int tile0 = I * 64;
+                const int tau = c * NT + I;
+                const int xslot = tau % XS, tslot = tau & 1;
+                // ================= state update and staging =================
+                if constexpr (I + 1 < NT) {
+                    issue_stage(t0 + tile0 + 64);
+                } else {
+                    if (c + 1 < nC) issue_stage(t0 + Q);
+                }
+                if constexpr (I == 0) {
+                    if (c + 1 < nC && st < Q) {  // Q <= 256: one value per thread
+                        csn = cs_row[t0 + Q + st];
+                        cpn = cp_row[t0 + Q + st];
+                    }
+                }
+                const TI *BT = BTB + (kBT2 ? tslot : 0) * N * BT_LD;
+                const float cs_e = CSL[tile0 + 63];
                 const float prev = (I > 0) ? CSL[tile0 - 1] : 0.f;
                 const float dec = fast_exp2(cs_e - prev);
 #pragma unroll
@@ -574,10 +638,10 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                     frag xa[PB];
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb)
-                        xa[pb] = Tr::lds_frag(XH + (16 * pb + r) * XT_LD + tile0 + 32 * k2 + 8 * kg);
+                        xa[pb] = Tr::lds_frag(XH + (16 * pb + r) * XH_LD + xslot * 64 + 32 * k2 + 8 * kg);
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) {
-                        const int nb = w + NW * j;
+                        const int nb = w + 4 * j;
                         if (nb < NB) {
                             const frag bb = Tr::lds_frag(BT + (16 * nb + r) * BT_LD + 32 * k2 + 8 * kg);
 #pragma unroll
@@ -585,32 +649,36 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                         }
                     }
                 }
-            }
-            if constexpr (I == NT - 1) {
-                if (c + 1 < nC && tid < Q) {  // Q <= NTH
-                    CSN[tid] = csn;
-                    CSN[Q + tid] = dtn;
+                // a single B^T slot, or a single h_in copy that the output waves
+                // still read this tile, must be read before it is overwritten
+                if constexpr (kMidSync) __syncthreads();
+                if constexpr (I == 0) {
+                if (c + 1 < nC && st < Q) {
+                    float *CSN = CSB + ((c + 1) & 1) * 2 * Q;
+                    CSN[st] = csn;
+                    CSN[Q + st] = cpn;
                 }
-            }
-            if constexpr (NT == 1) R[0] = R[1];
-            __syncthreads();
-        });
-    }
-
-    if (a.final_state) {
+                }
+                if constexpr (I == NT - 1) write_hs(HSB + (kHS2 ? ((c + 1) & 1) : 0) * P * HS_LD);
+                if (I + 1 < NT || c + 1 < nC) stage((tau + 1) % XS, (tau + 1) & 1);
+                __syncthreads();
+            });
+        }
+        if (a.final_state) {
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb)
+            for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-                const int nb = w + NW * j;
-                if (nb < NB) {
+                for (int j = 0; j < NBW; ++j) {
+                    const int nb = w + 4 * j;
+                    if (nb < NB) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int p = 16 * pb + 4 * kg + i, n = 16 * nb + r;
-                        a.final_state[(((size_t)b * H + h) * P + p) * N + n] = hacc[pb][j][i];
+                        for (int i = 0; i < 4; ++i) {
+                            const int p = 16 * pb + 4 * kg + i, n = 16 * nb + r;
+                            a.final_state[(((size_t)b * H + h) * P + p) * N + n] = hacc[pb][j][i];
+                        }
                     }
                 }
-            }
+        }
     }
 }
 
