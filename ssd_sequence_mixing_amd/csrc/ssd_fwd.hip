@@ -334,42 +334,51 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     const uint32_t x_tok = (uint32_t)(H * P * ES), b_tok = (uint32_t)(G * N * ES);
 
     // ---- state-wave data: staging offsets and registers ----
+    // staging units are wave-uniform whenever their count is a multiple of 64
+    auto x_unit = [&](int k) { return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (st + 256 * k < UX); };
+    auto b_unit = [&](int k) { return (UB % 64 == 0) ? (64 * w + 256 * k < UB) : (st + 256 * k < UB); };
+    // Every state-wave lane issues every load, a lane without a unit at an
+    // out-of-range offset (it reads zeros and moves no data), and tiles past
+    // the end reload the last one: with no load under a branch, the
+    // compiler's wait counts stay exact and loads two tiles ahead stay in
+    // flight.
     uint32_t vx[RX], vb[RB];
 #pragma unroll
     for (int k = 0; k < RX; ++k) {
         const int u = st + 256 * k;
-        vx[k] = (uint32_t)(4 * (u % 16)) * x_tok + (uint32_t)(8 * ((u / 16) % (P / 8)) * ES);
+        vx[k] = oob_if(!x_unit(k), (uint32_t)(4 * (u % 16)) * x_tok + (uint32_t)(8 * ((u / 16) % (P / 8)) * ES));
     }
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
         const int u = st + 256 * k;
-        vb[k] = (uint32_t)(4 * (u % 16)) * b_tok + (uint32_t)(8 * ((u / 16) % (N / 8)) * ES);
+        vb[k] = oob_if(!b_unit(k), (uint32_t)(4 * (u % 16)) * b_tok + (uint32_t)(8 * ((u / 16) % (N / 8)) * ES));
     }
-    // staging units are wave-uniform whenever their count is a multiple of 64
-    auto x_unit = [&](int k) { return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (st + 256 * k < UX); };
-    auto b_unit = [&](int k) { return (UB % 64 == 0) ? (64 * w + 256 * k < UB) : (st + 256 * k < UB); };
-    frag xr[RX][4], br[RB][4];
-    f32x4 xcp[RX];    // cs' of the unit's 4 tokens
-    float xce = 0.f;  // cs2 of the staged tile's last token
-    auto issue_stage = [&](int tt) {  // X, B and log-decays of the tile starting at token tt
+    // Loads run kDepth tiles ahead of the staging; with two register sets the
+    // set of tile t is t % 2, which is static when a chunk has an even number
+    // of tiles.
+    constexpr int kDepth = (NT % 2 == 0) ? 2 : 1;
+    frag xr[kDepth][RX][4], br[kDepth][RB][4];
+    f32x4 xcp[kDepth][RX];   // cs' of the unit's 4 tokens
+    float xce[kDepth] = {};  // cs2 of the staged tile's last token
+    auto issue_stage = [&](int tt, auto Sc) {  // X, B and log-decays of the tile at token tt
+        constexpr int S = decltype(Sc)::value;
         const uint32_t sx = (uint32_t)(tt * H + h) * (uint32_t)(P * ES);
         const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
 #pragma unroll
-        for (int k = 0; k < RX; ++k)
-            if (x_unit(k)) {
+        for (int k = 0; k < RX; ++k) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) xr[k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
-                xcp[k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % 16));
-            }
-        xce = cs_row[tt + 63];
+            for (int i = 0; i < 4; ++i) xr[S][k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
+            xcp[S][k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % 16));
+        }
+        xce[S] = cs_row[tt + 63];
 #pragma unroll
-        for (int k = 0; k < RB; ++k)
-            if (b_unit(k)) {
+        for (int k = 0; k < RB; ++k) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) br[k][i] = Tr::load_frag_s(rbm, vb[k] + i * b_tok, sb);
-            }
+            for (int i = 0; i < 4; ++i) br[S][k][i] = Tr::load_frag_s(rbm, vb[k] + i * b_tok, sb);
+        }
     };
-    auto stage = [&](int xslot, int tslot) {
+    auto stage = [&](auto Sc, int xslot, int tslot) {
+        constexpr int S = decltype(Sc)::value;
         TI *BT = BTB + (kBT2 ? tslot : 0) * N * BT_LD;
 #pragma unroll
         for (int k = 0; k < RX; ++k)
@@ -378,17 +387,17 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 const int tq = u % 16, po = (u / 16) % (P / 8);
                 float sc[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce - xcp[k][i]);
+                for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce[S] - xcp[S][k][i]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int row = 8 * po + e;
-                    lds_store4<TI>(XT + row * XT_LD + tslot * 64 + 4 * tq, xr[k][0][e], xr[k][1][e],
-                                   xr[k][2][e], xr[k][3][e]);
+                    lds_store4<TI>(XT + row * XT_LD + tslot * 64 + 4 * tq, xr[S][k][0][e], xr[S][k][1][e],
+                                   xr[S][k][2][e], xr[S][k][3][e]);
                     lds_store4<TI>(XH + row * XH_LD + xslot * 64 + 4 * tq,
-                                   Tr::from_f32(Tr::frag_get(xr[k][0], e) * sc[0]),
-                                   Tr::from_f32(Tr::frag_get(xr[k][1], e) * sc[1]),
-                                   Tr::from_f32(Tr::frag_get(xr[k][2], e) * sc[2]),
-                                   Tr::from_f32(Tr::frag_get(xr[k][3], e) * sc[3]));
+                                   Tr::from_f32(Tr::frag_get(xr[S][k][0], e) * sc[0]),
+                                   Tr::from_f32(Tr::frag_get(xr[S][k][1], e) * sc[1]),
+                                   Tr::from_f32(Tr::frag_get(xr[S][k][2], e) * sc[2]),
+                                   Tr::from_f32(Tr::frag_get(xr[S][k][3], e) * sc[3]));
                 }
             }
 #pragma unroll
@@ -398,8 +407,8 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 const int tq = u % 16, no = (u / 16) % (N / 8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq, br[k][0][e], br[k][1][e],
-                                   br[k][2][e], br[k][3][e]);
+                    lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq, br[S][k][0][e], br[S][k][1][e],
+                                   br[S][k][2][e], br[S][k][3][e]);
             }
     };
     // state accumulators (state waves): tile (pb, nb = w + 4j), rows p = 16pb + 4kg + i, col n = 16nb + r
@@ -447,8 +456,11 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 hacc[pb][j] = v;
             }
         write_hs(HSB);
-        issue_stage(0);
-        stage(0, 0);
+        issue_stage(0, std::integral_constant<int, 0>{});
+        stage(std::integral_constant<int, 0>{}, 0, 0);
+        if constexpr (kDepth == 2) {
+            issue_stage(nC * NT > 1 ? 64 : 0, std::integral_constant<int, 1>{});
+        }
     }
     for (int k = tid; k < Q; k += Cfg::NTH) {
         CSB[k] = cs_row[k];
@@ -468,6 +480,29 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     // (two where kMidSync), so the work-group stays in step.
     constexpr bool kMidSync = !kBT2 || (!kHS2 && (NT == 1 || !kHSReg));
     if (out_wave) {
+        // C rows and C B^T blocks of the next tile are loaded while this one
+        // is computed: C right after its last use, C B^T after the diagonal.
+        frag cf[NK], gf[NT][2];
+        auto load_c = [&](int tt) {  // C rows of the tile at token tt
+            const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) cf[kk] = Tr::load_frag_s(rc, vc[kk], sb);
+        };
+        auto load_g = [&](int cc, auto Ic) {  // C B^T blocks (I, J <= I) of chunk cc
+            constexpr int I = decltype(Ic)::value;
+            const size_t base = (((size_t)b * G + g) * nC + cc) * NP;
+#pragma unroll
+            for (int J = 0; J <= I; ++J) {
+                const uint32_t sg = (uint32_t)((base + pair_index(I, J)) * 4096 * ES);
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) gf[J][k2] = Tr::load_frag_s(rg, vg[k2], sg);
+            }
+        };
+        // same issue order as inside the loop (C rows first), so that the
+        // compiler's wait counts at the loop head fit both ways in
+        load_c(0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_g(0, std::integral_constant<int, 0>{});
         for (int c = 0; c < nC; ++c) {
             const int t0 = c * Q;
             const float *CSL = CSB + (c & 1) * 2 * Q;  // cs2 of this chunk
@@ -479,19 +514,6 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 const int tau = c * NT + I;
                 const TI *XTc = XT + (tau & 1) * 64;
                 // ================= output rows tile0 + 16w .. +15 =================
-                frag cf[NK], gf[I + 1][2];
-                {
-                    const uint32_t sb = (uint32_t)((t0 + tile0) * G + g) * (uint32_t)(N * ES);
-#pragma unroll
-                    for (int kk = 0; kk < NK; ++kk) cf[kk] = Tr::load_frag_s(rc, vc[kk], sb);
-#pragma unroll
-                    for (int J = 0; J <= I; ++J) {
-                        const uint32_t sg = (uint32_t)(
-                            ((((size_t)b * G + g) * nC + c) * NP + pair_index(I, J)) * 4096 * ES);
-#pragma unroll
-                        for (int k2 = 0; k2 < 2; ++k2) gf[J][k2] = Tr::load_frag_s(rg, vg[k2], sg);
-                    }
-                }
                 if constexpr (I == 0 && kHSReg) {
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb)
@@ -519,6 +541,11 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                         }
                         acc[pb] = Tr::mma(cf[kk], hb, acc[pb]);
                     }
+                }
+                if constexpr (I + 1 < NT) {
+                    load_c(t0 + tile0 + 64);
+                } else {
+                    load_c(c + 1 < nC ? t0 + Q : t0);  // past the end: a harmless reload
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -573,6 +600,11 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                         }
                     }
                 }
+                if constexpr (I + 1 < NT) {
+                    load_g(c, std::integral_constant<int, I + 1>{});
+                } else {
+                    load_g(c + 1 < nC ? c + 1 : c, std::integral_constant<int, 0>{});
+                }
                 // skip term, staging through this wave's own rows, store
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb) {
@@ -614,17 +646,15 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 const int tau = c * NT + I;
                 const int xslot = tau % XS, tslot = tau & 1;
                 // ================= state update and staging =================
-                if constexpr (I + 1 < NT) {
-                    issue_stage(t0 + tile0 + 64);
-                } else {
-                    if (c + 1 < nC) issue_stage(t0 + Q);
-                }
                 if constexpr (I == 0) {
-                    if (c + 1 < nC && st < Q) {  // Q <= 256: one value per thread
-                        csn = cs_row[t0 + Q + st];
-                        cpn = cp_row[t0 + Q + st];
-                    }
+                    // the next chunk's log-decays (Q <= 256: one per thread),
+                    // issued first and written at the chunk's last tile
+                    const int kn = (c + 1 < nC ? t0 + Q : t0) + min(st, Q - 1);
+                    csn = cs_row[kn];
+                    cpn = cp_row[kn];
                 }
+                issue_stage(min(tau + kDepth, nC * NT - 1) * 64,
+                            std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
                 const TI *BT = BTB + (kBT2 ? tslot : 0) * N * BT_LD;
                 const float cs_e = CSL[tile0 + 63];
                 const float prev = (I > 0) ? CSL[tile0 - 1] : 0.f;
@@ -652,15 +682,16 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 // a single B^T slot, or a single h_in copy that the output waves
                 // still read this tile, must be read before it is overwritten
                 if constexpr (kMidSync) __syncthreads();
-                if constexpr (I == 0) {
-                if (c + 1 < nC && st < Q) {
-                    float *CSN = CSB + ((c + 1) & 1) * 2 * Q;
-                    CSN[st] = csn;
-                    CSN[Q + st] = cpn;
-                }
+                if constexpr (I == NT - 1) {
+                    if (c + 1 < nC && st < Q) {
+                        float *CSN = CSB + ((c + 1) & 1) * 2 * Q;
+                        CSN[st] = csn;
+                        CSN[Q + st] = cpn;
+                    }
                 }
                 if constexpr (I == NT - 1) write_hs(HSB + (kHS2 ? ((c + 1) & 1) : 0) * P * HS_LD);
-                if (I + 1 < NT || c + 1 < nC) stage((tau + 1) % XS, (tau + 1) & 1);
+                // (after the last tile this stages a reload into slots nobody reads)
+                stage(std::integral_constant<int, kDepth == 2 ? ((I + 1) & 1) : 0>{}, (tau + 1) % XS, (tau + 1) & 1);
                 __syncthreads();
             });
         }
