@@ -55,11 +55,11 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     if (Tpad * nheads * headdim * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (Tpad * ngroups * dstate * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (Tpad * nheads * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    const int64_t nt = chunk / 64, np = nt * (nt + 1) / 2;
+    const int64_t ntiles = Tpad / 64;
     lay->nC = nC;
     lay->Tpad = Tpad;
     lay->cs_bytes = align256(batch * nheads * Tpad * 4);
-    lay->g_bytes = align256(batch * ngroups * nC * np * 4096 * es);
+    lay->g_bytes = align256(batch * ngroups * ntiles * 4096 * es);
     if (lay->g_bytes >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (batch * nheads > (int64_t)INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
     lay->total = (batch == 0 || seqlen == 0) ? 0 : 2 * lay->cs_bytes + lay->g_bytes;

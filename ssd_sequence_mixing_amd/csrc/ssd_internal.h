@@ -18,7 +18,7 @@ struct FwdArgs {
     int64_t batch, T, H, P, N, G, Q, nC, Tpad;
     ssd_dtype dtype;
     float *cs2, *dtf;          // workspace: (batch, H, Tpad) each
-    void *Gbuf;                // workspace: (batch, G, nC, pairs, 64, 64) in the storage type
+    void *Gbuf;                // workspace: (batch, G, tiles, 64, 64) in the storage type
     int64_t g_bytes;
 };
 

@@ -62,8 +62,8 @@ def ws(*a):
 def test_workspace_query():
     big = ctypes.c_size_t(-1).value
     n = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
-    # two fp32 (b, H, Tpad) arrays plus the bf16 C B^T lower tiles (10 per chunk)
-    assert n == 2 * 4 * 64 * 2048 * 4 + 4 * 1 * 8 * 10 * 4096 * 2
+    # two fp32 (b, H, Tpad) arrays plus the bf16 C B^T of every 64-token tile
+    assert n == 2 * 4 * 64 * 2048 * 4 + 4 * 1 * 32 * 4096 * 2
     assert ws(0, 2048, 64, 64, 128, 1, 256, BF16) == 0
     assert ws(4, 0, 64, 64, 128, 1, 256, BF16) == 0
     assert ws(4, 2048, 64, 64, 128, 3, 256, BF16) == big      # H % G
