@@ -60,6 +60,9 @@ __device__ __forceinline__ u32x4 buf_ld128s(rsrc_t r, uint32_t voff, uint32_t so
 __device__ __forceinline__ void buf_st128s(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
 }
+__device__ __forceinline__ void buf_st64s(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
 __device__ __forceinline__ void buf_st128(u32x4 v, rsrc_t r, uint32_t off) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }

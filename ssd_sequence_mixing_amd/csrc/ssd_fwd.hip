@@ -202,11 +202,11 @@ __global__ __launch_bounds__(256) void k_tile_cb(const TI *__restrict__ Bm, cons
 // four consecutive n of one row p: the LDS copy and the final state are
 // written four elements at a time.
 // ---------------------------------------------------------------------------
-template <typename TI, int Q, int P, int N>
+template <typename TI, int Q, int PW, int N>
 struct WalkCfg {
     static constexpr int ES = Traits<TI>::kBytes;
     static constexpr int NT = Q / 64;
-    static constexpr int PB = P / 16;
+    static constexpr int PB = PW / 16;
     static constexpr int NB = N / 16;
     static constexpr int NTH = 512;                  // 4 output + 4 state wavefronts
     static constexpr int NBW = (NB + 3) / 4;         // state n-blocks per state wave
@@ -215,21 +215,21 @@ struct WalkCfg {
     static constexpr int X_LD = 2 * 64 + PAD;        // X tiles (plain and scaled): two slots each
     static constexpr int BT_LD = 64 + PAD;
     static constexpr int HS_LD = NK * 32 + PAD;
-    static constexpr int YS_LD = P + PAD;
-    static constexpr int UX = 16 * (P / 8);          // staging units: 4 tokens x 8 columns
+    static constexpr int YS_LD = PW + PAD;
+    static constexpr int UX = 16 * (PW / 8);         // staging units: 4 tokens x 8 columns
     static constexpr int UB = 16 * (N / 8);
     static constexpr int RX = (UX + 255) / 256;      // units per state-wave thread
     static constexpr int RB = (UB + 255) / 256;
     static constexpr bool kHSReg = PB * NK * ES <= 32;  // state fragments held in registers
     static constexpr int XT_OFF = 0;
-    static constexpr int X_BYTES = P * X_LD * ES;
+    static constexpr int X_BYTES = PW * X_LD * ES;
     static constexpr int XH_OFF = XT_OFF + X_BYTES;
     static constexpr int YS_OFF = XH_OFF + X_BYTES;
     static constexpr int YS_BYTES = 64 * YS_LD * ES;
     static constexpr int CS_OFF = YS_OFF + YS_BYTES;  // 2 x (cs2[Q], cs'[Q]) fp32
     static constexpr int CS_BYTES = 2 * 2 * Q * 4;
     static constexpr int HS_OFF = CS_OFF + CS_BYTES;
-    static constexpr int HS_BYTES = P * HS_LD * ES;
+    static constexpr int HS_BYTES = PW * HS_LD * ES;
     static constexpr int BT_BYTES = N * BT_LD * ES;
     static constexpr int BASE = HS_OFF + HS_BYTES + BT_BYTES;
     static constexpr bool kBT2 = BASE + BT_BYTES <= 160 * 1024;             // double B^T
@@ -275,10 +275,10 @@ __device__ __forceinline__ void lds_load4(TI *d, const TI *p) {
 // sees it once the compiler keeps them in that order.
 __device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-template <typename TI, int Q, int P, int N>
-__global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(WalkArgs a) {
+template <typename TI, int Q, int PW, int N>
+__global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(WalkArgs a) {
     using Tr = Traits<TI>;
-    using Cfg = WalkCfg<TI, Q, P, N>;
+    using Cfg = WalkCfg<TI, Q, PW, N>;
     using frag = typename Tr::frag;
     constexpr int ES = Cfg::ES, NT = Cfg::NT, PB = Cfg::PB, NB = Cfg::NB;
     constexpr int NBW = Cfg::NBW, NK = Cfg::NK;
@@ -293,16 +293,19 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     TI *HSB = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);        // [copy][p][n]
     TI *BTB = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);        // [copy][n][token]
 
-    const int H = a.H, G = a.G, T = a.T, nC = a.nC;
+    const int H = a.H, G = a.G, T = a.T, nC = a.nC, P = a.P, NS = a.NS;
     const int ntiles = nC * NT;
-    // blockIdx -> (b, h): consecutive logical indices share an XCD (dispatch
-    // goes round-robin over the 8 XCDs), so the heads of one batch element,
-    // which read the same B, C and C B^T, share one L2.
-    const int W = a.batch * H;
+    // blockIdx -> (b, h, slice of PW columns): consecutive logical indices
+    // share an XCD (dispatch goes round-robin over the 8 XCDs), so the slices
+    // of a head and the heads of one batch element, which read the same B, C
+    // and C B^T, share one L2.
+    const int W = a.batch * H * NS;
     int L = blockIdx.x;
     if ((W & 7) == 0) L = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
-    const int b = L / H, h = L - b * H;
+    const int ps = L % NS;
+    const int b = (L / NS) / H, h = (L / NS) - b * H;
     const int g = (h * G) / H;
+    const int p0 = ps * PW;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
@@ -322,6 +325,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     const float *cp_row = a.dtf + ((size_t)b * H + h) * a.Tpad;  // cs' = cs2 - log2(dt)
     const float Dh = a.D[h];
     const uint32_t x_tok = (uint32_t)(H * P * ES), b_tok = (uint32_t)(G * N * ES);
+    const uint32_t hp0 = (uint32_t)((h * P + p0) * ES);  // this slice's columns within a token row
     const size_t bh = (size_t)b * H + h;
 
     // ---- prologue: the log-decays of chunk 0, zero padding of the state copies ----
@@ -331,9 +335,9 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
     }
     if constexpr (N % 32 != 0) {
         constexpr int PADN = NK * 32 - N;
-        for (int k = tid; k < (kHS2 ? 2 : 1) * P * PADN; k += Cfg::NTH) {
-            const int q = k / (P * PADN), kr = k % (P * PADN);
-            HSB[q * P * HS_LD + (kr / PADN) * HS_LD + N + kr % PADN] = Tr::from_f32(0.f);
+        for (int k = tid; k < (kHS2 ? 2 : 1) * PW * PADN; k += Cfg::NTH) {
+            const int q = k / (PW * PADN), kr = k % (PW * PADN);
+            HSB[q * PW * HS_LD + (kr / PADN) * HS_LD + N + kr % PADN] = Tr::from_f32(0.f);
         }
     }
 
@@ -376,7 +380,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 constexpr int I = decltype(Ic)::value;
                 const int tile0 = I * 64;  // chunk-local
                 const int tau = c * NT + I;
-                const TI *HSr = HSB + (kHS2 ? (tau & 1) : 0) * P * HS_LD;
+                const TI *HSr = HSB + (kHS2 ? (tau & 1) : 0) * PW * HS_LD;
                 const TI *XTc = XT + (tau & 1) * 64;
                 if constexpr (kHSReg) {
 #pragma unroll
@@ -454,8 +458,8 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 }
                 wave_lds_order();
                 {
-                    constexpr int VPR = P * ES / 16;  // 16-byte vectors per row
-                    const uint32_t sy = (uint32_t)((t0 + tile0 + 16 * w) * H + h) * (uint32_t)(P * ES);
+                    constexpr int VPR = PW * ES / 16;  // 16-byte vectors per row
+                    const uint32_t sy = (uint32_t)(t0 + tile0 + 16 * w) * x_tok + hp0;
 #pragma unroll
                     for (int v = lane; v < 16 * VPR; v += 64) {
                         const int rl = v / VPR, cv = v % VPR;
@@ -482,7 +486,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
 #pragma unroll
         for (int k = 0; k < RX; ++k) {
             const int u = st + 256 * k;
-            vx[k] = oob_if(!x_unit(k), (uint32_t)(4 * (u % 16)) * x_tok + (uint32_t)(8 * ((u / 16) % (P / 8)) * ES));
+            vx[k] = oob_if(!x_unit(k), (uint32_t)(4 * (u % 16)) * x_tok + (uint32_t)(8 * ((u / 16) % (PW / 8)) * ES));
         }
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
@@ -496,9 +500,10 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
         frag xr[kDepth][RX][4], br[kDepth][RB][4];
         f32x4 xcp[kDepth][RX];   // cs' of the unit's 4 tokens
         float xce[kDepth] = {};  // cs2 of the tile's last token
+        const rsrc_t rcs = make_rsrc(cs_row, (uint32_t)a.Tpad * 4u);
         auto issue_stage = [&](int tt, auto Sc) {  // X, B and log-decays of the tile at token tt
             constexpr int S = decltype(Sc)::value;
-            const uint32_t sx = (uint32_t)(tt * H + h) * (uint32_t)(P * ES);
+            const uint32_t sx = (uint32_t)tt * x_tok + hp0;
             const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
 #pragma unroll
             for (int k = 0; k < RX; ++k) {
@@ -506,7 +511,9 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 for (int i = 0; i < 4; ++i) xr[S][k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
                 xcp[S][k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % 16));
             }
-            xce[S] = cs_row[tt + 63];
+            // a vector load: a scalar one would hold up every LDS wait (both
+            // count in lgkmcnt) until it returns
+            xce[S] = __builtin_bit_cast(float, buf_ld32(rcs, (uint32_t)(tt + 63) * 4u));
 #pragma unroll
             for (int k = 0; k < RB; ++k) {
 #pragma unroll
@@ -520,7 +527,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
             for (int k = 0; k < RX; ++k)
                 if (x_unit(k)) {
                     const int u = st + 256 * k;
-                    const int tq = u % 16, po = (u / 16) % (P / 8);
+                    const int tq = u % 16, po = (u / 16) % (PW / 8);
                     float sc[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce[S] - xcp[S][k][i]);
@@ -568,7 +575,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 const int nb = w + 4 * j;
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
                 if (a.init && nb < NB)
-                    v = *reinterpret_cast<const f32x4 *>(a.init + (bh * P + 16 * pb + r) * N + 16 * nb + 4 * kg);
+                    v = *reinterpret_cast<const f32x4 *>(a.init + (bh * P + p0 + 16 * pb + r) * N + 16 * nb + 4 * kg);
                 hacc[pb][j] = v;
             }
         write_hs(HSB);
@@ -626,7 +633,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                         CSN[Q + st] = cpn;
                     }
                 }
-                write_hs(HSB + (kHS2 ? ((tau + 1) & 1) : 0) * P * HS_LD);
+                write_hs(HSB + (kHS2 ? ((tau + 1) & 1) : 0) * PW * HS_LD);
                 // (after the last tile this stages a reload into slots nobody reads)
                 stage(std::integral_constant<int, kDepth == 2 ? ((I + 1) & 1) : 0>{}, (tau + 1) & 1);
                 __syncthreads();
@@ -639,7 +646,7 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, P, N>::NTH), 1) void k_chunk_walk(W
                 for (int j = 0; j < NBW; ++j) {
                     const int nb = w + 4 * j;
                     if (nb < NB)
-                        *reinterpret_cast<f32x4 *>(a.final_state + (bh * P + 16 * pb + r) * N + 16 * nb + 4 * kg) =
+                        *reinterpret_cast<f32x4 *>(a.final_state + (bh * P + p0 + 16 * pb + r) * N + 16 * nb + 4 * kg) =
                             hacc[pb][j];
                 }
         }
@@ -663,9 +670,9 @@ static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
     return SSD_OK;
 }
 
-template <typename TI, int Q, int P, int N>
-static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
-    using Cfg = WalkCfg<TI, Q, P, N>;
+template <typename TI, int Q, int PW, int N>
+static ssd_status run_walk(const FwdArgs &f, int ns, hipStream_t s) {
+    using Cfg = WalkCfg<TI, Q, PW, N>;
     if constexpr (!Cfg::kFits) {
         return SSD_ERR_UNSUPPORTED;
     } else {
@@ -673,33 +680,48 @@ static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
         wa.X = f.X; wa.B = f.B; wa.C = f.C; wa.Y = f.Y; wa.Gbuf = f.Gbuf;
         wa.cs2 = f.cs2; wa.dtf = f.dtf; wa.D = f.D; wa.init = f.init; wa.final_state = f.final_state;
         wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
-        wa.Tpad = (int)f.Tpad; wa.g_bytes = (uint32_t)f.g_bytes;
-        return launch(k_chunk_walk<TI, Q, P, N>, dim3((unsigned)(f.batch * f.H)), dim3(Cfg::NTH), s, wa) ==
-                       hipSuccess
+        wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = ns; wa.g_bytes = (uint32_t)f.g_bytes;
+        return launch(k_chunk_walk<TI, Q, PW, N>, dim3((unsigned)(f.batch * f.H * ns)), dim3(Cfg::NTH), s,
+                      wa) == hipSuccess
                    ? SSD_OK
                    : SSD_ERR_HIP;
     }
 }
 
-template <typename TI, int Q, int P>
-static ssd_status walk_n(const FwdArgs &f, hipStream_t s) {
+template <typename TI, int Q, int PW>
+static ssd_status walk_n(const FwdArgs &f, int ns, hipStream_t s) {
     switch (f.N) {
-        case 16: return run_walk<TI, Q, P, 16>(f, s);
-        case 32: return run_walk<TI, Q, P, 32>(f, s);
-        case 64: return run_walk<TI, Q, P, 64>(f, s);
-        case 128: return run_walk<TI, Q, P, 128>(f, s);
-        case 256: return run_walk<TI, Q, P, 256>(f, s);
+        case 16: return run_walk<TI, Q, PW, 16>(f, ns, s);
+        case 32: return run_walk<TI, Q, PW, 32>(f, ns, s);
+        case 64: return run_walk<TI, Q, PW, 64>(f, ns, s);
+        case 128: return run_walk<TI, Q, PW, 128>(f, ns, s);
+        case 256: return run_walk<TI, Q, PW, 256>(f, ns, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
+// Work-groups per head, each taking P / ns of the head's columns (and the
+// matching rows of the state). One work-group fills a CU, so heads are split
+// only while there are fewer walks than CUs; a slice keeps at least 16
+// columns. Splitting further was measured slower: the slices of a head each
+// stage the whole B tile and build the whole masked C B^T block.
+constexpr int kCUs = 256;
+
+static int walk_split(const FwdArgs &f) {
+    const int64_t walks = f.batch * f.H;
+    int ns = 1;
+    while (ns < 4 && walks * ns < kCUs && f.P % (2 * ns) == 0 && f.P / (2 * ns) >= 16) ns *= 2;
+    return ns;
+}
+
 template <typename TI, int Q>
 static ssd_status walk_p(const FwdArgs &f, hipStream_t s) {
-    switch (f.P) {
-        case 16: return walk_n<TI, Q, 16>(f, s);
-        case 32: return walk_n<TI, Q, 32>(f, s);
-        case 64: return walk_n<TI, Q, 64>(f, s);
-        case 128: return walk_n<TI, Q, 128>(f, s);
+    const int ns = walk_split(f);
+    switch (f.P / ns) {
+        case 16: return walk_n<TI, Q, 16>(f, ns, s);
+        case 32: return walk_n<TI, Q, 32>(f, ns, s);
+        case 64: return walk_n<TI, Q, 64>(f, ns, s);
+        case 128: return walk_n<TI, Q, 128>(f, ns, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }

@@ -31,6 +31,7 @@ struct WalkArgs {
     const float *init;         // (batch, H, P, N) or null for a zero state
     float *final_state;        // may be null
     int batch, T, H, G, nC, Tpad;
+    int P, NS;                 // head dimension, and the work-groups sharing each head's P columns
     uint32_t g_bytes;
 };
 
