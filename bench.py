@@ -125,6 +125,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="for counter runs: 5 walk launches, then 5 element-wise negations of a "
+                         "512 MiB bf16 buffer (a copy of known size, to calibrate the counters); "
+                         "prints one line and exits")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -172,6 +176,23 @@ def main():
         t["walk"] = (p["X"], p["B"], p["C"], p["D"], None, chunk, p["Y"], p["F"], Bz, T, H, P, N, G, code,
                      p["W"], need, sptr)
         sets.append(t)
+
+    if args.traffic_probe:
+        for i in range(5):
+            t = sets[i % len(sets)]
+            if lib.ssd_chunk_scan_prepare(*t["prep"]) or lib.ssd_chunk_scan_walk(*t["walk"]):
+                raise RuntimeError("forward failed")
+        torch.cuda.synchronize()
+        n_copy = 512 * 2 ** 20
+        src = torch.ones(n_copy // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "walk_launches": 5, "copy_bytes_read": n_copy,
+                          "copy_bytes_written": n_copy,
+                          "walk_algorithmic_bytes": fwd_accounting(cfg, chunk)["walk_bytes"]}), flush=True)
+        return
 
     def step(t):
         st = lib.ssd_chunk_scan_prepare(*t["prep"])
