@@ -16,13 +16,14 @@
 // length still fixes the segment sums: log-decays are accumulated from each
 // chunk's first token.
 //
-// Three kernels, launched in this order on the caller's stream:
-//   k_dt_cumsum   per (batch, chunk, head block): dt -> chunk-local inclusive
+// Two kernels on the caller's stream. k_prepare does two independent jobs in
+// one launch:
+//   dt_cumsum     per (batch, chunk, head block): dt -> chunk-local inclusive
 //                 prefix sum of dt*A in base 2 (cs2), and cs' = cs2 - log2(dt),
 //                 both laid out (batch, head, token) fp32. With cs', the
 //                 weight dt_j exp2(cs_i - cs_j) of token j seen from token i is
 //                 one exponential, exp2(cs_i - cs'_j).
-//   k_tile_cb     per (batch, tile, group): G = C B^T of the tile's 64 tokens
+//   tile_cb       per (batch, tile, group): G = C B^T of the tile's 64 tokens
 //                 (matrix cores). It depends on the group only, so it is
 //                 formed once and shared by every head of the group.
 //   k_chunk_walk  per (batch, head): walks the tiles in order with the state
@@ -47,21 +48,19 @@
 namespace ssd {
 
 // ---------------------------------------------------------------------------
-// k_dt_cumsum: one work-group per (batch, chunk, block of 16 heads)
+// dt_cumsum: one work-group per (batch, chunk, block of 16 heads)
 // ---------------------------------------------------------------------------
 constexpr int kCumsumHeads = 16;
 
 template <typename TI, int Q>
-__global__ __launch_bounds__(256) void k_dt_cumsum(const TI *__restrict__ dt,
-                                                   const float *__restrict__ A,
-                                                   float *__restrict__ cs2,
-                                                   float *__restrict__ dtf, int T, int H,
-                                                   int nC, int Tpad) {
+__device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, const float *__restrict__ A,
+                                          float *__restrict__ cs2, float *__restrict__ dtf, int T, int H,
+                                          int nC, int Tpad) {
     constexpr int ES = Traits<TI>::kBytes;
     constexpr int LD = Q + 1;
     __shared__ float tile[kCumsumHeads * LD];
     const int hblocks = (H + kCumsumHeads - 1) / kCumsumHeads;
-    int x = blockIdx.x;
+    int x = blk;
     const int c = x % nC;
     x /= nC;
     const int hb = x % hblocks;
@@ -122,21 +121,20 @@ __global__ __launch_bounds__(256) void k_dt_cumsum(const TI *__restrict__ dt,
 }
 
 // ---------------------------------------------------------------------------
-// k_tile_cb: G[b, g, tile] = C_tile B_tile^T (64 x 64, row = query token i,
+// tile_cb: G[b, g, tile] = C_tile B_tile^T (64 x 64, row = query token i,
 // column = key token j), one tile per work-group, wave w owning rows
 // 16w..16w+15. The product is formed transposed (B rows as the A operand) so
 // that each lane holds four consecutive columns of one row: one 4-element
 // store each. Every operand load is issued before the first product.
 // ---------------------------------------------------------------------------
 template <typename TI, int N>
-__global__ __launch_bounds__(256) void k_tile_cb(const TI *__restrict__ Bm, const TI *__restrict__ Cm,
-                                                 TI *__restrict__ Gout, int T, int G, int ntiles,
-                                                 uint32_t g_bytes) {
+__device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, const TI *__restrict__ Cm,
+                                        TI *__restrict__ Gout, int T, int G, int ntiles, uint32_t g_bytes) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
     constexpr int ES = Tr::kBytes;
     constexpr int NK = (N + 31) / 32;
-    int x = blockIdx.x;
+    int x = blk;
     const int g = x % G;
     x /= G;
     const int tau = x % ntiles;
@@ -178,6 +176,21 @@ __global__ __launch_bounds__(256) void k_tile_cb(const TI *__restrict__ Bm, cons
         } else {
             buf_st128(__builtin_bit_cast(u32x4, acc[cb]), rg, off);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_prepare: both preparation jobs in one launch (the first work-groups form
+// C B^T tiles, the rest the log-decays); they are independent, so their
+// latencies overlap instead of adding up.
+// ---------------------------------------------------------------------------
+template <typename TI, int Q, int N>
+__global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
+    const int blk = blockIdx.x;
+    if (blk < a.cb_blocks) {
+        tile_cb<TI, N>(blk, (const TI *)a.B, (const TI *)a.C, (TI *)a.Gbuf, a.T, a.G, a.ntiles, a.g_bytes);
+    } else {
+        dt_cumsum<TI, Q>(blk - a.cb_blocks, (const TI *)a.dt, a.A, a.cs2, a.dtf, a.T, a.H, a.nC, a.Tpad);
     }
 }
 
@@ -658,16 +671,16 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
 // ---------------------------------------------------------------------------
 template <typename TI, int Q, int N>
 static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
-    const int nC = (int)f.nC;
-    const int hblocks = (int)((f.H + kCumsumHeads - 1) / kCumsumHeads);
-    if (launch(k_dt_cumsum<TI, Q>, dim3((unsigned)(f.batch * hblocks * nC)), dim3(256), s,
-               (const TI *)f.dt, f.A, f.cs2, f.dtf, (int)f.T, (int)f.H, nC, (int)f.Tpad) != hipSuccess)
-        return SSD_ERR_HIP;
-    const int ntiles = (int)(f.Tpad / 64);
-    if (launch(k_tile_cb<TI, N>, dim3((unsigned)(f.batch * ntiles * f.G)), dim3(256), s, (const TI *)f.B,
-               (const TI *)f.C, (TI *)f.Gbuf, (int)f.T, (int)f.G, ntiles, (uint32_t)f.g_bytes) != hipSuccess)
-        return SSD_ERR_HIP;
-    return SSD_OK;
+    PrepArgs a;
+    a.dt = f.dt; a.B = f.B; a.C = f.C; a.A = f.A; a.Gbuf = f.Gbuf; a.cs2 = f.cs2; a.dtf = f.dtf;
+    a.T = (int)f.T; a.H = (int)f.H; a.G = (int)f.G; a.nC = (int)f.nC; a.Tpad = (int)f.Tpad;
+    a.ntiles = (int)(f.Tpad / 64);
+    a.g_bytes = (uint32_t)f.g_bytes;
+    a.cb_blocks = (int)(f.batch * a.ntiles * f.G);
+    const int64_t hblocks = (f.H + kCumsumHeads - 1) / kCumsumHeads;
+    const int64_t blocks = a.cb_blocks + f.batch * hblocks * f.nC;
+    return launch(k_prepare<TI, Q, N>, dim3((unsigned)blocks), dim3(256), s, a) == hipSuccess ? SSD_OK
+                                                                                             : SSD_ERR_HIP;
 }
 
 template <typename TI, int Q, int PW, int N>

@@ -23,6 +23,15 @@ struct FwdArgs {
 };
 
 // Kernel arguments of the chunk walk (passed by value).
+struct PrepArgs {
+    const void *dt, *B, *C;
+    const float *A;
+    void *Gbuf;
+    float *cs2, *dtf;
+    int T, H, G, nC, Tpad, ntiles, cb_blocks;
+    uint32_t g_bytes;
+};
+
 struct WalkArgs {
     const void *X, *B, *C;
     void *Y;
