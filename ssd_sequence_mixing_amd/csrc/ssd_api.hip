@@ -29,7 +29,8 @@ bool in_set(int64_t v, std::initializer_list<int64_t> s) {
 int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
 struct FwdLayout {
-    int64_t nC, Tpad, cs_bytes, g_bytes, total;
+    int64_t nC, Tpad, cs_bytes, g_bytes, seg_bytes, total;
+    ssd::WalkPlan plan;
 };
 
 // Shape checks shared by the workspace query and the forward entry points.
@@ -43,26 +44,27 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     if (!in_set(chunk, {64, 128, 256})) return SSD_ERR_UNSUPPORTED;
     if (!in_set(headdim, {16, 32, 64, 128}) || !in_set(dstate, {16, 32, 64, 128, 256}))
         return SSD_ERR_UNSUPPORTED;
-    const int lds = ssd::fwd_lds_bytes((ssd_dtype)dtype, chunk, headdim, dstate);
-    if (lds < 0 || lds > ssd::kMaxLds) return SSD_ERR_UNSUPPORTED;
+    if (seqlen > kTwoGiB || nheads > 65536) return SSD_ERR_UNSUPPORTED;
+    if (ssd::fwd_plan((ssd_dtype)dtype, batch, nheads, headdim, dstate, chunk, (seqlen + chunk - 1) / chunk,
+                      &lay->plan) != 0)
+        return SSD_ERR_UNSUPPORTED;
     const int64_t es = esize((ssd_dtype)dtype);
     // 32-bit buffer offsets: every per-batch slab, padded to whole chunks, and
     // the C B^T buffer stay under 2 GiB, so an offset past the end of a slab
     // (a token past T) can never wrap back into range
-    if (seqlen > kTwoGiB || nheads > 65536) return SSD_ERR_UNSUPPORTED;
     const int64_t nC = (seqlen + chunk - 1) / chunk;
     const int64_t Tpad = nC * chunk;
     if (Tpad * nheads * headdim * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (Tpad * ngroups * dstate * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (Tpad * nheads * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    const int64_t ntiles = Tpad / 64;
     lay->nC = nC;
     lay->Tpad = Tpad;
     lay->cs_bytes = align256(batch * nheads * Tpad * 4);
-    lay->g_bytes = align256(batch * ngroups * ntiles * 4096 * es);
+    lay->g_bytes = align256(batch * ngroups * Tpad * lay->plan.tt * es);  // one tt x tt tile per tt tokens
     if (lay->g_bytes >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    if (batch * nheads > (int64_t)INT32_MAX / 2) return SSD_ERR_UNSUPPORTED;
-    lay->total = (batch == 0 || seqlen == 0) ? 0 : 2 * lay->cs_bytes + lay->g_bytes;
+    if (batch * nheads > (int64_t)INT32_MAX / 16) return SSD_ERR_UNSUPPORTED;  // grid: x ns x S <= 16
+    lay->seg_bytes = align256(batch * nheads * (lay->plan.S - 1) * headdim * dstate * 4);
+    lay->total = (batch == 0 || seqlen == 0) ? 0 : 2 * lay->cs_bytes + lay->g_bytes + lay->seg_bytes;
     return SSD_OK;
 }
 
@@ -85,6 +87,11 @@ FwdArgs make_args(const FwdLayout &lay, int64_t batch, int64_t seqlen, int64_t n
     f.dtf = reinterpret_cast<float *>(ws + lay.cs_bytes);
     f.Gbuf = ws + 2 * lay.cs_bytes;
     f.g_bytes = lay.g_bytes;
+    f.ns = lay.plan.ns;
+    f.tt = lay.plan.tt;
+    f.S = lay.plan.S;
+    f.cps = lay.plan.cps;
+    f.seg = reinterpret_cast<float *>(ws + 2 * lay.cs_bytes + lay.g_bytes);
     return f;
 }
 

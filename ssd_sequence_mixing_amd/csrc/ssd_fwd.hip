@@ -121,20 +121,24 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
 }
 
 // ---------------------------------------------------------------------------
-// tile_cb: G[b, g, tile] = C_tile B_tile^T (64 x 64, row = query token i,
-// column = key token j), one tile per work-group, wave w owning rows
-// 16w..16w+15. The product is formed transposed (B rows as the A operand) so
-// that each lane holds four consecutive columns of one row: one 4-element
-// store each. Every operand load is issued before the first product.
+// tile_cb: G[b, g, tile] = C_tile B_tile^T (TT x TT, row = query token i,
+// column = key token j) for one band of 64 rows of one tile per work-group,
+// wave w owning rows 16w..16w+15 of the band. Only the column blocks the walk
+// reads (up to the band's diagonal) are formed. The product is formed
+// transposed (B rows as the A operand) so that each lane holds four
+// consecutive columns of one row: one 4-element store each.
 // ---------------------------------------------------------------------------
-template <typename TI, int N>
+template <typename TI, int N, int TT>
 __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, const TI *__restrict__ Cm,
                                         TI *__restrict__ Gout, int T, int G, int ntiles, uint32_t g_bytes) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
     constexpr int ES = Tr::kBytes;
     constexpr int NK = (N + 31) / 32;
+    constexpr int BANDS = TT / 64;
     int x = blk;
+    const int band = x % BANDS;
+    x /= BANDS;
     const int g = x % G;
     x /= G;
     const int tau = x % ntiles;
@@ -145,36 +149,45 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
     const rsrc_t rb = make_rsrc(reinterpret_cast<const char *>(Bm) + b * slab, (uint32_t)slab);
     const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(Cm) + b * slab, (uint32_t)slab);
     const rsrc_t rg = make_rsrc(Gout, g_bytes);
-    const int t0 = tau * 64;
-    const int ti = t0 + 16 * w + r;  // this lane's query token (B operand column)
-    frag cq[NK], bk[4][NK];
+    const int t0 = tau * TT;
+    const int row = 64 * band + 16 * w + r;  // tile row of this lane's query token (B operand column)
+    const int ti = t0 + row;
+    frag cq[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
         const int n0 = kk * 32 + 8 * kg;
         cq[kk] = Tr::load_frag(rc, oob_if(ti >= T || n0 >= N, (uint32_t)(((ti * G + g) * N + n0) * ES)));
+    }
+    const size_t tile = (((size_t)b * G + g) * ntiles + tau) * (size_t)(TT * TT);
+    for (int cgp = 0; cgp <= band; ++cgp) {  // 64-column groups up to the band's diagonal
+        frag bk[4][NK];
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const int n0 = kk * 32 + 8 * kg;
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int tj = t0 + 64 * cgp + 16 * cb + r;
+                bk[cb][kk] =
+                    Tr::load_frag(rb, oob_if(tj >= T || n0 >= N, (uint32_t)(((tj * G + g) * N + n0) * ES)));
+            }
+        }
+        // acc[cb][i] = G[row][64 cgp + 16 cb + 4 kg + i]
+        f32x4 acc[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) acc[cb] = Tr::mma(bk[cb][kk], cq[kk], acc[cb]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            const int tj = t0 + 16 * cb + r;
-            bk[cb][kk] = Tr::load_frag(rb, oob_if(tj >= T || n0 >= N, (uint32_t)(((tj * G + g) * N + n0) * ES)));
-        }
-    }
-    // acc[cb][i] = G[16w + r][16cb + 4kg + i]
-    f32x4 acc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[cb] = Tr::mma(bk[cb][kk], cq[kk], acc[cb]);
-    const size_t tile = (((size_t)b * G + g) * ntiles + tau) * 4096;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-        const uint32_t off = (uint32_t)((tile + (16 * w + r) * 64 + 16 * cb + 4 * kg) * ES);
-        if constexpr (ES == 2) {
-            const bf16x4 v = {(bf16)acc[cb][0], (bf16)acc[cb][1], (bf16)acc[cb][2], (bf16)acc[cb][3]};
-            buf_st64(__builtin_bit_cast(u32x2, v), rg, off);
-        } else {
-            buf_st128(__builtin_bit_cast(u32x4, acc[cb]), rg, off);
+            const uint32_t off = (uint32_t)((tile + row * TT + 64 * cgp + 16 * cb + 4 * kg) * ES);
+            if constexpr (ES == 2) {
+                const bf16x4 v = {(bf16)acc[cb][0], (bf16)acc[cb][1], (bf16)acc[cb][2], (bf16)acc[cb][3]};
+                buf_st64(__builtin_bit_cast(u32x2, v), rg, off);
+            } else {
+                buf_st128(__builtin_bit_cast(u32x4, acc[cb]), rg, off);
+            }
         }
     }
 }
@@ -184,11 +197,11 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
 // C B^T tiles, the rest the log-decays); they are independent, so their
 // latencies overlap instead of adding up.
 // ---------------------------------------------------------------------------
-template <typename TI, int Q, int N>
+template <typename TI, int Q, int N, int TT>
 __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
     const int blk = blockIdx.x;
     if (blk < a.cb_blocks) {
-        tile_cb<TI, N>(blk, (const TI *)a.B, (const TI *)a.C, (TI *)a.Gbuf, a.T, a.G, a.ntiles, a.g_bytes);
+        tile_cb<TI, N, TT>(blk, (const TI *)a.B, (const TI *)a.C, (TI *)a.Gbuf, a.T, a.G, a.ntiles, a.g_bytes);
     } else {
         dt_cumsum<TI, Q>(blk - a.cb_blocks, (const TI *)a.dt, a.A, a.cs2, a.dtf, a.T, a.H, a.nC, a.Tpad);
     }
@@ -197,48 +210,54 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
 // ---------------------------------------------------------------------------
 // k_chunk_walk
 //
-// One work-group per (batch, head) walks the sequence in 64-token tiles, with
-// the P x N fp32 state in matrix-core accumulators. Its 8 wavefronts take two
-// roles that run side by side on every SIMD:
-//   output waves (0-3), 16 rows of the tile each: C rows and the tile's C B^T
-//     rows come from global memory one tile ahead; the state at the tile's
-//     start comes from an LDS copy; form the state term, the masked diagonal
-//     block and the skip term; store Y through a per-wave LDS staging area.
+// One work-group per (batch, head, column slice) walks the sequence in tiles
+// of TT tokens (64 or 128), with the PW x N fp32 state in matrix-core
+// accumulators. Its 8 wavefronts take two roles that run side by side on
+// every SIMD:
+//   output waves (0-3), TT/4 rows of the tile each (16-row blocks w and, for
+//     128-token tiles, 7 - w, which balances the triangular diagonal work):
+//     C rows and the tile's C B^T rows come from global memory one tile
+//     ahead; the state at the tile's start comes from an LDS copy; form the
+//     state term, the masked diagonal block and the skip term; store Y
+//     through a per-wave LDS staging area.
 //   state waves (4-7), a quarter of the state's rows n each: X, B and
 //     log-decays come from global memory two tiles ahead (one when a chunk
 //     has an odd tile count); update h with this tile, write h as the next
-//     tile's LDS copy, and stage the next tile's X (plain and scaled) and
-//     B^T into the other LDS slots.
+//     tile's LDS copy, and stage the next tile's X and B^T into the other
+//     LDS slots. The decay weights w_j of the state update are applied to
+//     B^T as it is staged, so one copy of X serves both roles.
 // One barrier per tile; a second one where LDS cannot hold two copies of
 // B^T or of the state.
 // The state is accumulated transposed (h^T[n][p]) so that each lane holds
 // four consecutive n of one row p: the LDS copy and the final state are
 // written four elements at a time.
 // ---------------------------------------------------------------------------
-template <typename TI, int Q, int PW, int N>
+template <typename TI, int Q, int PW, int N, int TT>
 struct WalkCfg {
     static constexpr int ES = Traits<TI>::kBytes;
-    static constexpr int NT = Q / 64;
+    static constexpr int NTT = TT / 64;              // 16-row blocks per output wave
+    static constexpr int NT = Q / TT;                // tiles per chunk
+    static constexpr int KB = TT / 32;               // 32-token k-steps per tile
     static constexpr int PB = PW / 16;
     static constexpr int NB = N / 16;
     static constexpr int NTH = 512;                  // 4 output + 4 state wavefronts
     static constexpr int NBW = (NB + 3) / 4;         // state n-blocks per state wave
     static constexpr int NK = (N + 31) / 32;         // 32-wide k-steps over N
     static constexpr int PAD = 16 / ES;
-    static constexpr int X_LD = 2 * 64 + PAD;        // X tiles (plain and scaled): two slots each
-    static constexpr int BT_LD = 64 + PAD;
+    static constexpr int X_LD = 2 * TT + PAD;        // X: two tile slots
+    static constexpr int BT_LD = TT + PAD;
     static constexpr int HS_LD = NK * 32 + PAD;
     static constexpr int YS_LD = PW + PAD;
-    static constexpr int UX = 16 * (PW / 8);         // staging units: 4 tokens x 8 columns
-    static constexpr int UB = 16 * (N / 8);
+    static constexpr int TQ = TT / 4;                // token quads per tile
+    static constexpr int UX = TQ * (PW / 8);         // staging units: 4 tokens x 8 columns
+    static constexpr int UB = TQ * (N / 8);
     static constexpr int RX = (UX + 255) / 256;      // units per state-wave thread
     static constexpr int RB = (UB + 255) / 256;
     static constexpr bool kHSReg = PB * NK * ES <= 32;  // state fragments held in registers
     static constexpr int XT_OFF = 0;
     static constexpr int X_BYTES = PW * X_LD * ES;
-    static constexpr int XH_OFF = XT_OFF + X_BYTES;
-    static constexpr int YS_OFF = XH_OFF + X_BYTES;
-    static constexpr int YS_BYTES = 64 * YS_LD * ES;
+    static constexpr int YS_OFF = XT_OFF + X_BYTES;
+    static constexpr int YS_BYTES = TT * YS_LD * ES;
     static constexpr int CS_OFF = YS_OFF + YS_BYTES;  // 2 x (cs2[Q], cs'[Q]) fp32
     static constexpr int CS_BYTES = 2 * 2 * Q * 4;
     static constexpr int HS_OFF = CS_OFF + CS_BYTES;
@@ -249,8 +268,11 @@ struct WalkCfg {
     static constexpr bool kHS2 = BASE + (kBT2 ? BT_BYTES : 0) + HS_BYTES <= 160 * 1024;
     static constexpr int BT_OFF = HS_OFF + (kHS2 ? 2 : 1) * HS_BYTES;
     static constexpr int LDS = BT_OFF + (kBT2 ? 2 : 1) * BT_BYTES;
-    static constexpr bool kFits = LDS <= 160 * 1024;
+    static constexpr bool kFits = LDS <= 160 * 1024 && Q % TT == 0;
     static constexpr bool kMidSync = !kBT2 || !kHS2;
+    // loads run two tiles ahead of the staging when a chunk has an even
+    // number of tiles (register set of tile t = t % 2, static), else one
+    static constexpr int kDepth = (NT % 2 == 0) ? 2 : 1;
 };
 
 template <int... Is, typename F>
@@ -288,23 +310,24 @@ __device__ __forceinline__ void lds_load4(TI *d, const TI *p) {
 // sees it once the compiler keeps them in that order.
 __device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
 
-template <typename TI, int Q, int PW, int N>
-__global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(WalkArgs a) {
+// kStateOnly: the state waves alone (256 threads), for the first pass of a
+// sequence split: each segment's end state from its own entering state.
+template <typename TI, int Q, int PW, int N, int TT, bool kStateOnly>
+__global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkArgs a) {
     using Tr = Traits<TI>;
-    using Cfg = WalkCfg<TI, Q, PW, N>;
+    using Cfg = WalkCfg<TI, Q, PW, N, TT>;
     using frag = typename Tr::frag;
-    constexpr int ES = Cfg::ES, NT = Cfg::NT, PB = Cfg::PB, NB = Cfg::NB;
-    constexpr int NBW = Cfg::NBW, NK = Cfg::NK;
+    constexpr int ES = Cfg::ES, NT = Cfg::NT, NTT = Cfg::NTT, KB = Cfg::KB, PB = Cfg::PB, NB = Cfg::NB;
+    constexpr int NBW = Cfg::NBW, NK = Cfg::NK, TQ = Cfg::TQ;
     constexpr int RX = Cfg::RX, RB = Cfg::RB, UX = Cfg::UX, UB = Cfg::UB;
     constexpr int X_LD = Cfg::X_LD, BT_LD = Cfg::BT_LD, HS_LD = Cfg::HS_LD, YS_LD = Cfg::YS_LD;
     constexpr bool kHSReg = Cfg::kHSReg, kBT2 = Cfg::kBT2, kHS2 = Cfg::kHS2, kMidSync = Cfg::kMidSync;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
-    TI *XT = reinterpret_cast<TI *>(smem + Cfg::XT_OFF);  // [p][slot*64 + token], plain X
-    TI *XH = reinterpret_cast<TI *>(smem + Cfg::XH_OFF);  // [p][slot*64 + token], scaled X
+    TI *XT = reinterpret_cast<TI *>(smem + Cfg::XT_OFF);  // [p][slot*TT + token]
     TI *YS = reinterpret_cast<TI *>(smem + Cfg::YS_OFF);
     float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);  // [buf][cs2 Q | cs' Q]
     TI *HSB = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);        // [copy][p][n]
-    TI *BTB = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);        // [copy][n][token]
+    TI *BTB = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);        // [copy][n][token], weighted
 
     const int H = a.H, G = a.G, T = a.T, nC = a.nC, P = a.P, NS = a.NS;
     const int ntiles = nC * NT;
@@ -312,17 +335,33 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
     // share an XCD (dispatch goes round-robin over the 8 XCDs), so the slices
     // of a head and the heads of one batch element, which read the same B, C
     // and C B^T, share one L2.
-    const int W = a.batch * H * NS;
+    // logical index = ((b H + h) SL + s) NS + ps, s the sequence segment
+    const int SL = a.SL, S = a.S;
+    const int W = a.batch * H * SL * NS;
     int L = blockIdx.x;
     if ((W & 7) == 0) L = (blockIdx.x & 7) * (W >> 3) + (blockIdx.x >> 3);
     const int ps = L % NS;
-    const int b = (L / NS) / H, h = (L / NS) - b * H;
+    const int seg = (L / NS) % SL;
+    const int bhi = (L / NS) / SL;
+    const int b = bhi / H, h = bhi - b * H;
     const int g = (h * G) / H;
     const int p0 = ps * PW;
+    // this work-group's chunks, and the state it starts from / ends in
+    const int cb = seg * a.cps, ce = min(cb + a.cps, nC);
+    const int last_tile = ce * NT - 1;
+    const size_t bhs = (size_t)bhi;
+    // pass 1 (state only) enters every segment but the first with zero; the
+    // full walk enters segment s with the scanned state in slot s - 1
+    const float *init_mat = (seg == 0) ? (a.init ? a.init + bhs * P * N : nullptr)
+                            : kStateOnly ? nullptr
+                                         : a.seg + (bhs * (S - 1) + seg - 1) * P * N;
+    float *out_mat = kStateOnly ? a.seg + (bhs * (S - 1) + seg) * P * N
+                                : ((seg == S - 1 && a.final_state) ? a.final_state + bhs * P * N : nullptr);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
-    const bool out_wave = wv < 4;
+    const bool out_wave = !kStateOnly && wv < 4;
+    constexpr int NTH = kStateOnly ? 256 : Cfg::NTH;
     const int w = wv & 3;              // index within the role
     const int st = tid & 255;          // thread index within the role
     const int r = lane & 15, kg = lane >> 4;
@@ -339,62 +378,75 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
     const float Dh = a.D[h];
     const uint32_t x_tok = (uint32_t)(H * P * ES), b_tok = (uint32_t)(G * N * ES);
     const uint32_t hp0 = (uint32_t)((h * P + p0) * ES);  // this slice's columns within a token row
-    const size_t bh = (size_t)b * H + h;
 
-    // ---- prologue: the log-decays of chunk 0, zero padding of the state copies ----
-    for (int k = tid; k < Q; k += Cfg::NTH) {
-        CSB[k] = cs_row[k];
-        CSB[Q + k] = cp_row[k];
+    // ---- prologue: the log-decays of the first chunk, zero padding of the state copies ----
+    for (int k = tid; k < Q; k += NTH) {
+        CSB[k] = cs_row[cb * Q + k];
+        CSB[Q + k] = cp_row[cb * Q + k];
     }
     if constexpr (N % 32 != 0) {
         constexpr int PADN = NK * 32 - N;
-        for (int k = tid; k < (kHS2 ? 2 : 1) * PW * PADN; k += Cfg::NTH) {
+        for (int k = tid; k < (kHS2 ? 2 : 1) * PW * PADN; k += NTH) {
             const int q = k / (PW * PADN), kr = k % (PW * PADN);
             HSB[q * PW * HS_LD + (kr / PADN) * HS_LD + N + kr % PADN] = Tr::from_f32(0.f);
         }
     }
 
-    if (out_wave) {
+    if (!kStateOnly && out_wave) {
         // ===================== output waves =====================
-        uint32_t vc[NK], vg[2];
+        // 16-row blocks of the tile: w, and 4 NTT - 1 - w for 128-token tiles
+        int rbk[NTT];
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            const int n0 = kk * 32 + 8 * kg;
-            vc[kk] = oob_if(n0 >= N, (uint32_t)(16 * w + r) * b_tok + (uint32_t)(n0 * ES));
+        for (int j = 0; j < NTT; ++j) rbk[j] = (j == 0) ? w : 4 * NTT - 1 - w;
+        uint32_t vc[NTT][NK], vg[NTT][KB];
+#pragma unroll
+        for (int j = 0; j < NTT; ++j) {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int n0 = kk * 32 + 8 * kg;
+                vc[j][kk] = oob_if(n0 >= N, (uint32_t)(16 * rbk[j] + r) * b_tok + (uint32_t)(n0 * ES));
+            }
+            // C B^T column blocks above the block's diagonal are not needed
+#pragma unroll
+            for (int k2 = 0; k2 < KB; ++k2)
+                vg[j][k2] = oob_if(32 * k2 > 16 * rbk[j] + 15,
+                                   (uint32_t)(((16 * rbk[j] + r) * TT + 32 * k2 + 8 * kg) * ES));
         }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) vg[k2] = (uint32_t)(((16 * w + r) * 64 + 32 * k2 + 8 * kg) * ES);
         const size_t gbase = ((size_t)b * G + g) * ntiles;
         // C rows and the C B^T rows of the next tile are loaded while this one
         // is computed (C right after its last use, C B^T after the diagonal).
-        frag cf[NK], gd[2];
+        frag cf[NTT][NK], gd[NTT][KB];
         auto load_c = [&](int tt) {  // C rows of the tile at token tt
             const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) cf[kk] = Tr::load_frag_s(rc, vc[kk], sb);
+            for (int j = 0; j < NTT; ++j)
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) cf[j][kk] = Tr::load_frag_s(rc, vc[j][kk], sb);
         };
         auto load_g = [&](int tau) {  // this wave's rows of the tile's C B^T
-            const uint32_t sg = (uint32_t)((gbase + tau) * 4096 * ES);
+            const uint32_t sg = (uint32_t)((gbase + tau) * (size_t)(TT * TT * ES));
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) gd[k2] = Tr::load_frag_s(rg, vg[k2], sg);
+            for (int j = 0; j < NTT; ++j)
+#pragma unroll
+                for (int k2 = 0; k2 < KB; ++k2) gd[j][k2] = Tr::load_frag_s(rg, vg[j][k2], sg);
         };
         // same issue order as inside the loop (C rows first), so that the
         // compiler's wait counts at the loop head fit both ways in
-        load_c(0);
+        load_c(cb * Q);
         __builtin_amdgcn_sched_barrier(0);
-        load_g(0);
+        load_g(cb * NT);
         frag hsf[kHSReg ? PB : 1][kHSReg ? NK : 1];
         __syncthreads();
-        for (int c = 0; c < nC; ++c) {
+        for (int c = cb; c < ce; ++c) {
             const int t0 = c * Q;
-            const float *CSL = CSB + (c & 1) * 2 * Q;  // cs2 of this chunk
-            const float *CPL = CSL + Q;                // cs' of this chunk
+            const float *CSL = CSB + ((c - cb) & 1) * 2 * Q;  // cs2 of this chunk
+            const float *CPL = CSL + Q;                       // cs' of this chunk
             static_for<NT>([&](auto Ic) {
                 constexpr int I = decltype(Ic)::value;
-                const int tile0 = I * 64;  // chunk-local
+                const int tile0 = I * TT;  // chunk-local
                 const int tau = c * NT + I;
                 const TI *HSr = HSB + (kHS2 ? (tau & 1) : 0) * PW * HS_LD;
-                const TI *XTc = XT + (tau & 1) * 64;
+                const TI *XTc = XT + (tau & 1) * TT;
                 if constexpr (kHSReg) {
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb)
@@ -402,15 +454,13 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
                         for (int kk = 0; kk < NK; ++kk)
                             hsf[pb][kk] = Tr::lds_frag(HSr + (16 * pb + r) * HS_LD + kk * 32 + 8 * kg);
                 }
-                const int irow = tile0 + 16 * w + r;  // chunk-local token of this lane's A row
                 const float cs_ref = (I > 0) ? CSL[tile0 - 1] : 0.f;
-                float cs_rows[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) cs_rows[i] = CSL[tile0 + 16 * w + 4 * kg + i];
                 // state -> output
-                f32x4 acc[PB];
+                f32x4 acc[NTT][PB];
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) acc[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < NTT; ++j)
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) acc[j][pb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
@@ -421,25 +471,29 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
                         } else {
                             hb = Tr::lds_frag(HSr + (16 * pb + r) * HS_LD + kk * 32 + 8 * kg);
                         }
-                        acc[pb] = Tr::mma(cf[kk], hb, acc[pb]);
+#pragma unroll
+                        for (int j = 0; j < NTT; ++j) acc[j][pb] = Tr::mma(cf[j][kk], hb, acc[j][pb]);
                     }
                 }
                 // the state copy (and a single B^T copy) may be overwritten
                 // from here on
                 if constexpr (kMidSync) __syncthreads();
-                load_c(min(tau + 1, ntiles - 1) * 64);  // past the end: a harmless reload
+                load_c(min(tau + 1, last_tile) * TT);  // past the end: a harmless reload
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float f = fast_exp2(cs_rows[i] - cs_ref);
+                for (int j = 0; j < NTT; ++j) {
+                    const int rows0 = tile0 + 16 * rbk[j];
 #pragma unroll
-                    for (int pb = 0; pb < PB; ++pb) acc[pb][i] *= f;
-                }
-                // diagonal block: weight exp2(cs_i - cs'_j) per element, j > i selected to zero
-                {
+                    for (int i = 0; i < 4; ++i) {
+                        const float f = fast_exp2(CSL[rows0 + 4 * kg + i] - cs_ref);
+#pragma unroll
+                        for (int pb = 0; pb < PB; ++pb) acc[j][pb][i] *= f;
+                    }
+                    // diagonal block: weight exp2(cs_i - cs'_j) per element, j > i selected to zero
+                    const int irow = rows0 + r;  // chunk-local token of this lane's A row
                     const float cs_i = CSL[irow];
 #pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        if (32 * k2 > 16 * w + 15) continue;  // wave-uniform: above the diagonal
+                    for (int k2 = 0; k2 < KB; ++k2) {
+                        if (32 * k2 > 16 * rbk[j] + 15) continue;  // wave-uniform: above the diagonal
                         const int j0 = tile0 + 32 * k2 + 8 * kg;
                         const f32x4 cpa = *reinterpret_cast<const f32x4 *>(CPL + j0);
                         const f32x4 cpb = *reinterpret_cast<const f32x4 *>(CPL + j0 + 4);
@@ -447,38 +501,43 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float cpj = e < 4 ? cpa[e] : cpb[e - 4];
-                            const float v = Tr::frag_get(gd[k2], e) * fast_exp2(cs_i - cpj);
+                            const float v = Tr::frag_get(gd[j][k2], e) * fast_exp2(cs_i - cpj);
                             Tr::frag_set(ma, e, (j0 + e <= irow) ? v : 0.f);
                         }
 #pragma unroll
                         for (int pb = 0; pb < PB; ++pb) {
                             const frag xb = Tr::lds_frag(XTc + (16 * pb + r) * X_LD + 32 * k2 + 8 * kg);
-                            acc[pb] = Tr::mma(ma, xb, acc[pb]);
+                            acc[j][pb] = Tr::mma(ma, xb, acc[j][pb]);
                         }
                     }
                 }
-                load_g(min(tau + 1, ntiles - 1));
+                load_g(min(tau + 1, last_tile));
                 // skip term, staging through this wave's own rows, store
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    TI xs4[4];
-                    lds_load4<TI>(xs4, XTc + (16 * pb + r) * X_LD + 16 * w + 4 * kg);
+                for (int j = 0; j < NTT; ++j) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int rl = 16 * w + 4 * kg + i;  // tile-local token
-                        YS[rl * YS_LD + 16 * pb + r] = Tr::from_f32(acc[pb][i] + Dh * Tr::to_f32(xs4[i]));
+                    for (int pb = 0; pb < PB; ++pb) {
+                        TI xs4[4];
+                        lds_load4<TI>(xs4, XTc + (16 * pb + r) * X_LD + 16 * rbk[j] + 4 * kg);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int rl = 16 * rbk[j] + 4 * kg + i;  // tile-local token
+                            YS[rl * YS_LD + 16 * pb + r] =
+                                Tr::from_f32(acc[j][pb][i] + Dh * Tr::to_f32(xs4[i]));
+                        }
                     }
                 }
                 wave_lds_order();
-                {
+#pragma unroll
+                for (int j = 0; j < NTT; ++j) {
                     constexpr int VPR = PW * ES / 16;  // 16-byte vectors per row
-                    const uint32_t sy = (uint32_t)(t0 + tile0 + 16 * w) * x_tok + hp0;
+                    const uint32_t sy = (uint32_t)(t0 + tile0 + 16 * rbk[j]) * x_tok + hp0;
 #pragma unroll
                     for (int v = lane; v < 16 * VPR; v += 64) {
                         const int rl = v / VPR, cv = v % VPR;
                         const u32x4 d =
                             *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
-                                                             (16 * w + rl) * YS_LD * ES + cv * 16);
+                                                             (16 * rbk[j] + rl) * YS_LD * ES + cv * 16);
                         buf_st128s(d, ry, (uint32_t)rl * x_tok + (uint32_t)(cv * 16), sy);
                     }
                 }
@@ -499,19 +558,16 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
 #pragma unroll
         for (int k = 0; k < RX; ++k) {
             const int u = st + 256 * k;
-            vx[k] = oob_if(!x_unit(k), (uint32_t)(4 * (u % 16)) * x_tok + (uint32_t)(8 * ((u / 16) % (PW / 8)) * ES));
+            vx[k] = oob_if(!x_unit(k), (uint32_t)(4 * (u % TQ)) * x_tok + (uint32_t)(8 * ((u / TQ) % (PW / 8)) * ES));
         }
 #pragma unroll
         for (int k = 0; k < RB; ++k) {
             const int u = st + 256 * k;
-            vb[k] = oob_if(!b_unit(k), (uint32_t)(4 * (u % 16)) * b_tok + (uint32_t)(8 * ((u / 16) % (N / 8)) * ES));
+            vb[k] = oob_if(!b_unit(k), (uint32_t)(4 * (u % TQ)) * b_tok + (uint32_t)(8 * ((u / TQ) % (N / 8)) * ES));
         }
-        // Loads run kDepth tiles ahead of the staging; with two register sets
-        // the set of tile t is t % 2, static when a chunk has an even number
-        // of tiles.
-        constexpr int kDepth = (NT % 2 == 0) ? 2 : 1;
+        constexpr int kDepth = Cfg::kDepth;
         frag xr[kDepth][RX][4], br[kDepth][RB][4];
-        f32x4 xcp[kDepth][RX];   // cs' of the unit's 4 tokens
+        f32x4 bcp[kDepth][RB];   // cs' of the B unit's 4 tokens
         float xce[kDepth] = {};  // cs2 of the tile's last token
         const rsrc_t rcs = make_rsrc(cs_row, (uint32_t)a.Tpad * 4u);
         auto issue_stage = [&](int tt, auto Sc) {  // X, B and log-decays of the tile at token tt
@@ -522,15 +578,15 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
             for (int k = 0; k < RX; ++k) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xr[S][k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
-                xcp[S][k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % 16));
             }
             // a vector load: a scalar one would hold up every LDS wait (both
             // count in lgkmcnt) until it returns
-            xce[S] = __builtin_bit_cast(float, buf_ld32(rcs, (uint32_t)(tt + 63) * 4u));
+            xce[S] = __builtin_bit_cast(float, buf_ld32(rcs, (uint32_t)(tt + TT - 1) * 4u));
 #pragma unroll
             for (int k = 0; k < RB; ++k) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) br[S][k][i] = Tr::load_frag_s(rbm, vb[k] + i * b_tok, sb);
+                bcp[S][k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % TQ));
             }
         };
         auto stage = [&](auto Sc, int slot) {  // into X slot `slot` and the matching B^T copy
@@ -540,31 +596,28 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
             for (int k = 0; k < RX; ++k)
                 if (x_unit(k)) {
                     const int u = st + 256 * k;
-                    const int tq = u % 16, po = (u / 16) % (PW / 8);
-                    float sc[4];
+                    const int tq = u % TQ, po = (u / TQ) % (PW / 8);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce[S] - xcp[S][k][i]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int row = 8 * po + e;
-                        lds_store4<TI>(XT + row * X_LD + slot * 64 + 4 * tq, xr[S][k][0][e], xr[S][k][1][e],
-                                       xr[S][k][2][e], xr[S][k][3][e]);
-                        lds_store4<TI>(XH + row * X_LD + slot * 64 + 4 * tq,
-                                       Tr::from_f32(Tr::frag_get(xr[S][k][0], e) * sc[0]),
-                                       Tr::from_f32(Tr::frag_get(xr[S][k][1], e) * sc[1]),
-                                       Tr::from_f32(Tr::frag_get(xr[S][k][2], e) * sc[2]),
-                                       Tr::from_f32(Tr::frag_get(xr[S][k][3], e) * sc[3]));
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        lds_store4<TI>(XT + (8 * po + e) * X_LD + slot * TT + 4 * tq, xr[S][k][0][e],
+                                       xr[S][k][1][e], xr[S][k][2][e], xr[S][k][3][e]);
                 }
 #pragma unroll
             for (int k = 0; k < RB; ++k)
                 if (b_unit(k)) {
                     const int u = st + 256 * k;
-                    const int tq = u % 16, no = (u / 16) % (N / 8);
+                    const int tq = u % TQ, no = (u / TQ) % (N / 8);
+                    // the state update's weights w_j = exp2(cs_e - cs'_j) <= dt_j
+                    float sc[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce[S] - bcp[S][k][i]);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq, br[S][k][0][e], br[S][k][1][e],
-                                       br[S][k][2][e], br[S][k][3][e]);
+                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq,
+                                       Tr::from_f32(Tr::frag_get(br[S][k][0], e) * sc[0]),
+                                       Tr::from_f32(Tr::frag_get(br[S][k][1], e) * sc[1]),
+                                       Tr::from_f32(Tr::frag_get(br[S][k][2], e) * sc[2]),
+                                       Tr::from_f32(Tr::frag_get(br[S][k][3], e) * sc[3]));
                 }
         };
         // transposed state: hacc[pb][j][i] = h[p = 16pb + r][n = 16(w + 4j) + 4kg + i]
@@ -587,46 +640,47 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
             for (int j = 0; j < NBW; ++j) {
                 const int nb = w + 4 * j;
                 f32x4 v = {0.f, 0.f, 0.f, 0.f};
-                if (a.init && nb < NB)
-                    v = *reinterpret_cast<const f32x4 *>(a.init + (bh * P + p0 + 16 * pb + r) * N + 16 * nb + 4 * kg);
+                if (init_mat && nb < NB)
+                    v = *reinterpret_cast<const f32x4 *>(init_mat + (p0 + 16 * pb + r) * N + 16 * nb + 4 * kg);
                 hacc[pb][j] = v;
             }
-        write_hs(HSB);
-        issue_stage(0, std::integral_constant<int, 0>{});
-        stage(std::integral_constant<int, 0>{}, 0);
-        if constexpr (kDepth == 2) issue_stage(ntiles > 1 ? 64 : 0, std::integral_constant<int, 1>{});
+        const int tile_b = cb * NT;  // first tile
+        if constexpr (!kStateOnly) write_hs(HSB + (kHS2 ? (tile_b & 1) : 0) * PW * HS_LD);
+        issue_stage(tile_b * TT, std::integral_constant<int, 0>{});
+        stage(std::integral_constant<int, 0>{}, tile_b & 1);
+        if constexpr (kDepth == 2) issue_stage(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
         __syncthreads();
         float csn = 0.f, cpn = 0.f;
-        for (int c = 0; c < nC; ++c) {
+        for (int c = cb; c < ce; ++c) {
             const int t0 = c * Q;
-            const float *CSL = CSB + (c & 1) * 2 * Q;  // cs2 of this chunk
+            const float *CSL = CSB + ((c - cb) & 1) * 2 * Q;  // cs2 of this chunk
             static_for<NT>([&](auto Ic) {
                 constexpr int I = decltype(Ic)::value;
-                const int tile0 = I * 64;
+                const int tile0 = I * TT;
                 const int tau = c * NT + I;
                 const int slot = tau & 1;
                 if constexpr (I == 0) {
                     // the next chunk's log-decays (Q <= 256: one per thread),
                     // issued first and written at the chunk's last tile
-                    const int kn = (c + 1 < nC ? t0 + Q : t0) + min(st, Q - 1);
+                    const int kn = (c + 1 < ce ? t0 + Q : t0) + min(st, Q - 1);
                     csn = cs_row[kn];
                     cpn = cp_row[kn];
                 }
-                issue_stage(min(tau + kDepth, ntiles - 1) * 64,
+                issue_stage(min(tau + kDepth, last_tile) * TT,
                             std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
                 const TI *BT = BTB + (kBT2 ? slot : 0) * N * BT_LD;
                 const float cs_ref = (I > 0) ? CSL[tile0 - 1] : 0.f;
-                const float dec = fast_exp2(CSL[tile0 + 63] - cs_ref);
+                const float dec = fast_exp2(CSL[tile0 + TT - 1] - cs_ref);
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) hacc[pb][j] *= dec;
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
+                for (int k2 = 0; k2 < KB; ++k2) {
                     frag xa[PB];
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb)
-                        xa[pb] = Tr::lds_frag(XH + (16 * pb + r) * X_LD + slot * 64 + 32 * k2 + 8 * kg);
+                        xa[pb] = Tr::lds_frag(XT + (16 * pb + r) * X_LD + slot * TT + 32 * k2 + 8 * kg);
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) {
                         const int nb = w + 4 * j;
@@ -640,26 +694,26 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
                 // a single B^T copy, or a single state copy, is read up to here
                 if constexpr (kMidSync) __syncthreads();
                 if constexpr (I == NT - 1) {
-                    if (c + 1 < nC && st < Q) {
-                        float *CSN = CSB + ((c + 1) & 1) * 2 * Q;
+                    if (c + 1 < ce && st < Q) {
+                        float *CSN = CSB + ((c + 1 - cb) & 1) * 2 * Q;
                         CSN[st] = csn;
                         CSN[Q + st] = cpn;
                     }
                 }
-                write_hs(HSB + (kHS2 ? ((tau + 1) & 1) : 0) * PW * HS_LD);
+                if constexpr (!kStateOnly) write_hs(HSB + (kHS2 ? ((tau + 1) & 1) : 0) * PW * HS_LD);
                 // (after the last tile this stages a reload into slots nobody reads)
                 stage(std::integral_constant<int, kDepth == 2 ? ((I + 1) & 1) : 0>{}, (tau + 1) & 1);
                 __syncthreads();
             });
         }
-        if (a.final_state) {
+        if (out_mat) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
                 for (int j = 0; j < NBW; ++j) {
                     const int nb = w + 4 * j;
                     if (nb < NB)
-                        *reinterpret_cast<f32x4 *>(a.final_state + (bh * P + p0 + 16 * pb + r) * N + 16 * nb + 4 * kg) =
+                        *reinterpret_cast<f32x4 *>(out_mat + (p0 + 16 * pb + r) * N + 16 * nb + 4 * kg) =
                             hacc[pb][j];
                 }
         }
@@ -667,49 +721,87 @@ __global__ __launch_bounds__((WalkCfg<TI, Q, PW, N>::NTH), 1) void k_chunk_walk(
 }
 
 // ---------------------------------------------------------------------------
-// host-side launches for one instantiation
+// k_seg_scan: between the two passes of a sequence split. Pass 1 left, for
+// each segment s < S - 1, the state at its end when entered with zero (with
+// the caller's initial state for s = 0). The state entering segment s + 1 is
+//   E_0 = end_0,   E_s = 2^{D_s} E_{s-1} + end_s,
+// D_s the segment's total log-decay (the sum of its chunks' last cs2), i.e.
+// the state passing of the chunked method at segment granularity. Rewritten in
+// place: slot s ends up holding the state entering segment s + 1. One thread
+// per 4 state elements.
 // ---------------------------------------------------------------------------
-template <typename TI, int Q, int N>
-static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
-    PrepArgs a;
-    a.dt = f.dt; a.B = f.B; a.C = f.C; a.A = f.A; a.Gbuf = f.Gbuf; a.cs2 = f.cs2; a.dtf = f.dtf;
-    a.T = (int)f.T; a.H = (int)f.H; a.G = (int)f.G; a.nC = (int)f.nC; a.Tpad = (int)f.Tpad;
-    a.ntiles = (int)(f.Tpad / 64);
-    a.g_bytes = (uint32_t)f.g_bytes;
-    a.cb_blocks = (int)(f.batch * a.ntiles * f.G);
-    const int64_t hblocks = (f.H + kCumsumHeads - 1) / kCumsumHeads;
-    const int64_t blocks = a.cb_blocks + f.batch * hblocks * f.nC;
-    return launch(k_prepare<TI, Q, N>, dim3((unsigned)blocks), dim3(256), s, a) == hipSuccess ? SSD_OK
-                                                                                             : SSD_ERR_HIP;
-}
-
-template <typename TI, int Q, int PW, int N>
-static ssd_status run_walk(const FwdArgs &f, int ns, hipStream_t s) {
-    using Cfg = WalkCfg<TI, Q, PW, N>;
-    if constexpr (!Cfg::kFits) {
-        return SSD_ERR_UNSUPPORTED;
-    } else {
-        WalkArgs wa;
-        wa.X = f.X; wa.B = f.B; wa.C = f.C; wa.Y = f.Y; wa.Gbuf = f.Gbuf;
-        wa.cs2 = f.cs2; wa.dtf = f.dtf; wa.D = f.D; wa.init = f.init; wa.final_state = f.final_state;
-        wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
-        wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = ns; wa.g_bytes = (uint32_t)f.g_bytes;
-        return launch(k_chunk_walk<TI, Q, PW, N>, dim3((unsigned)(f.batch * f.H * ns)), dim3(Cfg::NTH), s,
-                      wa) == hipSuccess
-                   ? SSD_OK
-                   : SSD_ERR_HIP;
+__global__ __launch_bounds__(256) void k_seg_scan(float *__restrict__ seg, const float *__restrict__ cs2,
+                                                  int64_t bh_count, int PN, int S, int cps, int nC, int Q,
+                                                  int Tpad) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // f32x4 index
+    const int per = PN / 4;
+    if (v >= bh_count * per) return;
+    const int64_t bhi = v / per;
+    const int e = (int)(v - bhi * per);
+    const float *cs = cs2 + bhi * Tpad;
+    f32x4 *base = reinterpret_cast<f32x4 *>(seg + bhi * (int64_t)(S - 1) * PN) + e;
+    f32x4 E = base[0];
+    for (int s = 1; s < S - 1; ++s) {
+        float D = 0.f;
+        for (int c = s * cps; c < min((s + 1) * cps, nC); ++c) D += cs[c * Q + Q - 1];
+        const float a = fast_exp2(D);
+        f32x4 *slot = base + (int64_t)s * (PN / 4);
+        E = a * E + *slot;
+        *slot = E;
     }
 }
 
+// ---------------------------------------------------------------------------
+// host side: the plan (column slices, tile size) and the launches
+// ---------------------------------------------------------------------------
+template <typename TI, int Q, int PW, int N, int TT>
+static constexpr bool fits() {
+    if constexpr (Q % TT != 0) {
+        return false;
+    } else {
+        return WalkCfg<TI, Q, PW, N, TT>::kFits;
+    }
+}
+
+// The tile: 64 tokens. (128-token tiles, which halve the per-tile barriers,
+// were measured slower on every benchmark shape: the cost per tile grows with
+// the work, not with the number of tiles.)
+template <typename TI, int Q, int PW, int N>
+static int tile_of() {
+    if (fits<TI, Q, PW, N, 64>()) return 64;
+    return 0;
+}
+
 template <typename TI, int Q, int PW>
-static ssd_status walk_n(const FwdArgs &f, int ns, hipStream_t s) {
-    switch (f.N) {
-        case 16: return run_walk<TI, Q, PW, 16>(f, ns, s);
-        case 32: return run_walk<TI, Q, PW, 32>(f, ns, s);
-        case 64: return run_walk<TI, Q, PW, 64>(f, ns, s);
-        case 128: return run_walk<TI, Q, PW, 128>(f, ns, s);
-        case 256: return run_walk<TI, Q, PW, 256>(f, ns, s);
-        default: return SSD_ERR_UNSUPPORTED;
+static int tile_n(int64_t N) {
+    switch (N) {
+        case 16: return tile_of<TI, Q, PW, 16>();
+        case 32: return tile_of<TI, Q, PW, 32>();
+        case 64: return tile_of<TI, Q, PW, 64>();
+        case 128: return tile_of<TI, Q, PW, 128>();
+        case 256: return tile_of<TI, Q, PW, 256>();
+        default: return 0;
+    }
+}
+
+template <typename TI, int Q>
+static int tile_p(int64_t PW, int64_t N) {
+    switch (PW) {
+        case 16: return tile_n<TI, Q, 16>(N);
+        case 32: return tile_n<TI, Q, 32>(N);
+        case 64: return tile_n<TI, Q, 64>(N);
+        case 128: return tile_n<TI, Q, 128>(N);
+        default: return 0;
+    }
+}
+
+template <typename TI>
+static int tile_q(int64_t Q, int64_t PW, int64_t N) {
+    switch (Q) {
+        case 64: return tile_p<TI, 64>(PW, N);
+        case 128: return tile_p<TI, 128>(PW, N);
+        case 256: return tile_p<TI, 256>(PW, N);
+        default: return 0;
     }
 }
 
@@ -720,21 +812,113 @@ static ssd_status walk_n(const FwdArgs &f, int ns, hipStream_t s) {
 // stage the whole B tile and build the whole masked C B^T block.
 constexpr int kCUs = 256;
 
-static int walk_split(const FwdArgs &f) {
-    const int64_t walks = f.batch * f.H;
+int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64_t Q, int64_t nC,
+             WalkPlan *plan) {
+    const int64_t walks = batch * H;
+    // Long sequences with few heads: split the sequence into S segments (at
+    // least two chunks each) so that more, shorter walks fill the CUs; then
+    // split heads' columns while walks are still fewer than CUs.
+    int S = 1;
+    while (walks * 2 * S <= kCUs && nC / (2 * S) >= 2) S *= 2;
+    while (S > 1 && (S - 1) * ((nC + S - 1) / S) >= nC) S /= 2;  // no empty segment
     int ns = 1;
-    while (ns < 4 && walks * ns < kCUs && f.P % (2 * ns) == 0 && f.P / (2 * ns) >= 16) ns *= 2;
-    return ns;
+    while (ns < 4 && walks * S * 2 * ns <= kCUs && P % (2 * ns) == 0 && P / (2 * ns) >= 16) ns *= 2;
+    int tt = dt == SSD_BF16 ? tile_q<bf16>(Q, P / ns, N) : tile_q<float>(Q, P / ns, N);
+    // the plan must not depend on the batch for a shape to be supported: the
+    // unsplit head has to fit too
+    const int tt1 = dt == SSD_BF16 ? tile_q<bf16>(Q, P, N) : tile_q<float>(Q, P, N);
+    if (!tt || !tt1) return -1;
+    plan->ns = ns;
+    plan->tt = tt;
+    plan->S = S;
+    plan->cps = (int)((nC + S - 1) / S);
+    return 0;
+}
+
+template <typename TI, int Q, int N, int TT>
+static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
+    PrepArgs a;
+    a.dt = f.dt; a.B = f.B; a.C = f.C; a.A = f.A; a.Gbuf = f.Gbuf; a.cs2 = f.cs2; a.dtf = f.dtf;
+    a.T = (int)f.T; a.H = (int)f.H; a.G = (int)f.G; a.nC = (int)f.nC; a.Tpad = (int)f.Tpad;
+    a.ntiles = (int)(f.Tpad / TT);
+    a.g_bytes = (uint32_t)f.g_bytes;
+    a.cb_blocks = (int)(f.batch * a.ntiles * f.G * (TT / 64));
+    const int64_t hblocks = (f.H + kCumsumHeads - 1) / kCumsumHeads;
+    const int64_t blocks = a.cb_blocks + f.batch * hblocks * f.nC;
+    return launch(k_prepare<TI, Q, N, TT>, dim3((unsigned)blocks), dim3(256), s, a) == hipSuccess
+               ? SSD_OK
+               : SSD_ERR_HIP;
+}
+
+// A split sequence (S > 1) takes three launches: the state-only walk of
+// segments 0..S-2, the scan of their end states, the full walk of all S
+// segments each from its entering state.
+template <typename TI, int Q, int PW, int N, int TT>
+static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
+    if constexpr (!fits<TI, Q, PW, N, TT>()) {
+        return SSD_ERR_UNSUPPORTED;
+    } else {
+        WalkArgs wa;
+        wa.X = f.X; wa.B = f.B; wa.C = f.C; wa.Y = f.Y; wa.Gbuf = f.Gbuf;
+        wa.cs2 = f.cs2; wa.dtf = f.dtf; wa.D = f.D; wa.init = f.init; wa.final_state = f.final_state;
+        wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
+        wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
+        wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg;
+        const int64_t heads = f.batch * f.H * f.ns;
+        if (f.S > 1) {
+            wa.SL = f.S - 1;
+            if (launch(k_chunk_walk<TI, Q, PW, N, TT, true>, dim3((unsigned)(heads * wa.SL)), dim3(256), s, wa) !=
+                hipSuccess)
+                return SSD_ERR_HIP;
+            const int64_t n4 = f.batch * f.H * f.P * f.N / 4;
+            if (f.S > 2 && launch(k_seg_scan, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, f.seg,
+                                  (const float *)f.cs2, f.batch * f.H, (int)(f.P * f.N), f.S, f.cps,
+                                  (int)f.nC, (int)f.Q, (int)f.Tpad) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
+        wa.SL = f.S;
+        return launch(k_chunk_walk<TI, Q, PW, N, TT, false>, dim3((unsigned)(heads * f.S)), dim3(512), s, wa) ==
+                       hipSuccess
+                   ? SSD_OK
+                   : SSD_ERR_HIP;
+    }
+}
+
+template <typename TI, int Q, int PW, int N>
+static ssd_status walk_t(const FwdArgs &f, hipStream_t s) {
+    switch (f.tt) {
+        case 64: return run_walk<TI, Q, PW, N, 64>(f, s);
+        default: return SSD_ERR_UNSUPPORTED;
+    }
+}
+
+template <typename TI, int Q, int PW>
+static ssd_status walk_n(const FwdArgs &f, hipStream_t s) {
+    switch (f.N) {
+        case 16: return walk_t<TI, Q, PW, 16>(f, s);
+        case 32: return walk_t<TI, Q, PW, 32>(f, s);
+        case 64: return walk_t<TI, Q, PW, 64>(f, s);
+        case 128: return walk_t<TI, Q, PW, 128>(f, s);
+        case 256: return walk_t<TI, Q, PW, 256>(f, s);
+        default: return SSD_ERR_UNSUPPORTED;
+    }
 }
 
 template <typename TI, int Q>
 static ssd_status walk_p(const FwdArgs &f, hipStream_t s) {
-    const int ns = walk_split(f);
-    switch (f.P / ns) {
-        case 16: return walk_n<TI, Q, 16>(f, ns, s);
-        case 32: return walk_n<TI, Q, 32>(f, ns, s);
-        case 64: return walk_n<TI, Q, 64>(f, ns, s);
-        case 128: return walk_n<TI, Q, 128>(f, ns, s);
+    switch (f.P / f.ns) {
+        case 16: return walk_n<TI, Q, 16>(f, s);
+        case 32: return walk_n<TI, Q, 32>(f, s);
+        case 64: return walk_n<TI, Q, 64>(f, s);
+        case 128: return walk_n<TI, Q, 128>(f, s);
+        default: return SSD_ERR_UNSUPPORTED;
+    }
+}
+
+template <typename TI, int Q, int N>
+static ssd_status prepare_t(const FwdArgs &f, hipStream_t s) {
+    switch (f.tt) {
+        case 64: return run_prepare<TI, Q, N, 64>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
@@ -742,11 +926,11 @@ static ssd_status walk_p(const FwdArgs &f, hipStream_t s) {
 template <typename TI, int Q>
 static ssd_status prepare_n(const FwdArgs &f, hipStream_t s) {
     switch (f.N) {
-        case 16: return run_prepare<TI, Q, 16>(f, s);
-        case 32: return run_prepare<TI, Q, 32>(f, s);
-        case 64: return run_prepare<TI, Q, 64>(f, s);
-        case 128: return run_prepare<TI, Q, 128>(f, s);
-        case 256: return run_prepare<TI, Q, 256>(f, s);
+        case 16: return prepare_t<TI, Q, 16>(f, s);
+        case 32: return prepare_t<TI, Q, 32>(f, s);
+        case 64: return prepare_t<TI, Q, 64>(f, s);
+        case 128: return prepare_t<TI, Q, 128>(f, s);
+        case 256: return prepare_t<TI, Q, 256>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
@@ -767,42 +951,6 @@ ssd_status launch_prepare(const FwdArgs &f, hipStream_t s) {
 
 ssd_status launch_walk(const FwdArgs &f, hipStream_t s) {
     return f.dtype == SSD_BF16 ? dispatch_q<bf16, true>(f, s) : dispatch_q<float, true>(f, s);
-}
-
-template <typename TI, int Q, int P, int N>
-static constexpr int lds_of() { return WalkCfg<TI, Q, P, N>::LDS; }
-
-template <typename TI>
-static int lds_table(int64_t Q, int64_t P, int64_t N) {
-#define SSD_LDS_N(Qv, Pv)                                   \
-    switch (N) {                                            \
-        case 16: return lds_of<TI, Qv, Pv, 16>();           \
-        case 32: return lds_of<TI, Qv, Pv, 32>();           \
-        case 64: return lds_of<TI, Qv, Pv, 64>();           \
-        case 128: return lds_of<TI, Qv, Pv, 128>();         \
-        case 256: return lds_of<TI, Qv, Pv, 256>();         \
-        default: return -1;                                 \
-    }
-#define SSD_LDS_P(Qv)                                       \
-    switch (P) {                                            \
-        case 16: SSD_LDS_N(Qv, 16)                          \
-        case 32: SSD_LDS_N(Qv, 32)                          \
-        case 64: SSD_LDS_N(Qv, 64)                          \
-        case 128: SSD_LDS_N(Qv, 128)                        \
-        default: return -1;                                 \
-    }
-    switch (Q) {
-        case 64: SSD_LDS_P(64)
-        case 128: SSD_LDS_P(128)
-        case 256: SSD_LDS_P(256)
-        default: return -1;
-    }
-#undef SSD_LDS_P
-#undef SSD_LDS_N
-}
-
-int fwd_lds_bytes(ssd_dtype dt, int64_t Q, int64_t P, int64_t N) {
-    return dt == SSD_BF16 ? lds_table<bf16>(Q, P, N) : lds_table<float>(Q, P, N);
 }
 
 }  // namespace ssd

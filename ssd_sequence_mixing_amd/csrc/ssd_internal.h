@@ -18,9 +18,22 @@ struct FwdArgs {
     int64_t batch, T, H, P, N, G, Q, nC, Tpad;
     ssd_dtype dtype;
     float *cs2, *dtf;          // workspace: (batch, H, Tpad) each
-    void *Gbuf;                // workspace: (batch, G, tiles, 64, 64) in the storage type
+    void *Gbuf;                // workspace: (batch, G, Tpad / tt, tt, tt) in the storage type
     int64_t g_bytes;
+    int ns, tt;                // walk plan: work-groups per head, tile tokens
+    int S, cps;                // walk plan: sequence segments, chunks per segment
+    float *seg;                // workspace: (batch, H, S - 1, P, N) fp32 segment states
 };
+
+// How the walk covers a shape: ns work-groups per head (P / ns columns each)
+// and tiles of tt tokens.
+struct WalkPlan {
+    int ns, tt;   // work-groups per head (P / ns columns each), tile tokens
+    int S, cps;   // sequence segments walked in parallel, chunks per segment
+};
+// Fills the plan; -1 if no kernel covers the shape.
+int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64_t Q, int64_t nC,
+             WalkPlan *plan);
 
 // Kernel arguments of the chunk walk (passed by value).
 struct PrepArgs {
@@ -41,6 +54,8 @@ struct WalkArgs {
     float *final_state;        // may be null
     int batch, T, H, G, nC, Tpad;
     int P, NS;                 // head dimension, and the work-groups sharing each head's P columns
+    int S, SL, cps;            // sequence segments, segments in this launch, chunks per segment
+    float *seg;                // (batch, H, S - 1, P, N) segment states (S > 1)
     uint32_t g_bytes;
 };
 
@@ -57,11 +72,8 @@ struct StepArgs {
 ssd_status launch_prepare(const FwdArgs &f, hipStream_t s);
 // Phase 2: the chunk walk (reads the prepared workspace).
 ssd_status launch_walk(const FwdArgs &f, hipStream_t s);
-// LDS bytes one chunk-walk work-group needs, or -1 if there is no kernel.
-int fwd_lds_bytes(ssd_dtype dt, int64_t Q, int64_t P, int64_t N);
+// One recurrent decode step.
 ssd_status launch_step(const StepArgs &a, hipStream_t s);
-
-constexpr int kMaxLds = 160 * 1024;
 
 // Launches a kernel and returns the status of that launch itself (not an
 // error some earlier, unrelated runtime call may have left pending).
