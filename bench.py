@@ -121,6 +121,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk length")
+    ap.add_argument("--workload", default="l1p3b_bf16",
+                    choices=["l1p3b_bf16", "l125m_bf16", "long16k_bf16"],
+                    help="forward workload (default: the 1.3B-layer shape the metric is quoted on; "
+                         "the others are the 125M-layer shape and the 16K-token shape)")
     ap.add_argument("--sets", type=int, default=3, help="rotating input/output/workspace sets")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
@@ -154,7 +158,7 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    cfg = si.CONFIGS["l1p3b_bf16"]
+    cfg = si.CONFIGS[args.workload]
     chunk = args.chunk or cfg.chunk
     code = ssd.SSD_BF16 if cfg.dtype == "bf16" else ssd.SSD_F32
     Bz, T, H, P, N, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
@@ -237,7 +241,7 @@ def main():
     hbm_frac = hbm_gbs / HBM_PEAK_GBS
     roof_time = max(acc["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12), acc["bytes"] / (HBM_PEAK_GBS * 1e9))
     walk_gbs = acc["walk_bytes"] / (walk_ms / 1e3) / 1e9
-    traffic = read_traffic()
+    traffic = read_traffic() if args.workload == "l1p3b_bf16" else None
 
     out = {
         "metric": METRIC,
@@ -252,7 +256,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "ssd_fwd 1.3B-layer shape", "batch": Bz, "seqlen": T, "nheads": H,
+        "config": {"workload": {"l1p3b_bf16": "ssd_fwd 1.3B-layer shape", "l125m_bf16": "ssd_fwd 125M-layer shape",
+                                "long16k_bf16": "ssd_fwd 16K-token shape"}[args.workload],
+                   "batch": Bz, "seqlen": T, "nheads": H,
                    "headdim": P, "dstate": N, "ngroups": G, "chunk": chunk, "storage": cfg.dtype,
                    "rotating_sets": len(sets)},
         "roofline": {"bound": "hbm", "kernel": "k_chunk_walk", "achieved": walk_gbs,
