@@ -139,6 +139,48 @@ ssd_status ssd_chunk_scan_walk(const void *X, const void *B, const void *C, cons
                                void *stream);
 
 /*
+ * Packed variable-length batch: num_seqs sequences of different lengths laid
+ * end to end along the token axis, each walked from its own starting state
+ * (the state is reset at every sequence start; the reading report's section
+ * on systems names such batches as a Mamba-2 feature, and the SSD theory
+ * page's chunking section allows a partial last chunk per sequence).
+ *
+ *   X, Y (total_tokens, nheads, headdim)      dtype
+ *   dt   (total_tokens, nheads)               dtype
+ *   B, C (total_tokens, ngroups, dstate)      dtype
+ *   A, D (nheads)                             float32
+ *   cu_seqlens (num_seqs + 1)                 int32, DEVICE memory:
+ *        sequence i is tokens [cu_seqlens[i], cu_seqlens[i+1]); cu_seqlens[0]
+ *        = 0, non-decreasing, every length <= max_seqlen, last entry <=
+ *        total_tokens. Entries are clamped on the device to [0, total_tokens]
+ *        and lengths to max_seqlen, so a malformed table never causes an
+ *        access out of range (the affected sequences' results are then
+ *        unspecified); tokens outside every sequence are not written.
+ *   initial_state (num_seqs, nheads, headdim, dstate) float32, or NULL: the
+ *        state before each sequence's first token (zero when NULL)
+ *   final_state (num_seqs, nheads, headdim, dstate) float32, or NULL: the
+ *        state after each sequence's last token (the initial state, or zero,
+ *        for an empty sequence)
+ *
+ * Chunks start at each sequence's first token, so each sequence is computed
+ * exactly as a batch of one would be. The workspace query takes num_seqs and
+ * max_seqlen in place of batch and seqlen; workspace grows with num_seqs x
+ * max_seqlen. Shape support, alignment and error behaviour are those of
+ * ssd_chunk_scan_fwd; X, B and C must each be under 2 GiB in total.
+ */
+size_t ssd_chunk_scan_varlen_workspace_bytes(int64_t num_seqs, int64_t max_seqlen, int64_t nheads,
+                                             int64_t headdim, int64_t dstate, int64_t ngroups,
+                                             int64_t chunk, ssd_dtype dtype);
+
+ssd_status ssd_chunk_scan_fwd_varlen(const void *X, const void *dt, const float *A, const void *B,
+                                     const void *C, const float *D, int64_t chunk,
+                                     const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                                     int64_t total_tokens, const float *initial_state, void *Y,
+                                     float *final_state, int64_t nheads, int64_t headdim,
+                                     int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * One recurrent decode step, updating `state` in place:
  *
  *   state (batch, nheads, headdim, dstate)    float32   in/out

@@ -15,7 +15,8 @@ from typing import Optional, Tuple
 __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "load", "lib_path", "ssd_status_string",
     "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_chunk_scan_prepare",
-    "ssd_chunk_scan_walk", "ssd_step", "EXPORTS",
+    "ssd_chunk_scan_walk", "ssd_step", "ssd_chunk_scan_varlen_workspace_bytes",
+    "ssd_chunk_scan_fwd_varlen", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -26,7 +27,8 @@ _lib = None
 
 # Entry points include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd",
-           "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step")
+           "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step",
+           "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen")
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -91,6 +93,11 @@ def load():
                                                                            ctypes.c_size_t, _V]
     lib.ssd_step.restype = ctypes.c_int
     lib.ssd_step.argtypes = [_V] * 8 + [_I] * 5 + [ctypes.c_int, _V]
+    lib.ssd_chunk_scan_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_varlen_workspace_bytes.argtypes = [_I] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_fwd_varlen.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_varlen.argtypes = ([_V] * 6 + [_I, _V] + [_I] * 3 + [_V, _V, _V] + [_I] * 4 +
+                                              [ctypes.c_int, _V, ctypes.c_size_t, _V])
     _lib = lib
     return lib
 
@@ -220,6 +227,46 @@ def ssd_step(state, x, dt, A, B, C, D, y=None, *, stream=None):
     if st != 0:
         raise SSDError(st, "ssd_step")
     return y
+
+
+def ssd_chunk_scan_varlen_workspace_bytes(num_seqs, max_seqlen, nheads, headdim, dstate, ngroups,
+                                          chunk, dtype: int) -> int:
+    n = load().ssd_chunk_scan_varlen_workspace_bytes(num_seqs, max_seqlen, nheads, headdim, dstate,
+                                                     ngroups, chunk, dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise SSDError(3, "ssd_chunk_scan_varlen_workspace_bytes")
+    return int(n)
+
+
+def ssd_chunk_scan_fwd_varlen(X, dt, A, B, C, D, chunk: int, cu_seqlens, max_seqlen: int,
+                              initial_state=None, Y=None, final_state=None, *,
+                              want_final: bool = True, workspace=None, stream=None):
+    """Forward over a packed variable-length batch. X (total, H, P), dt (total, H),
+    B/C (total, G, N); cu_seqlens int32 on the GPU, (num_seqs + 1) cumulative
+    lengths; max_seqlen the longest sequence (a host int, so that no device value
+    has to be read here). Returns (Y, final_state) with final_state
+    (num_seqs, H, P, N) fp32."""
+    import torch
+    lib = load()
+    total, H, P = X.shape
+    G, N = B.shape[1], B.shape[2]
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    nseq = cu_seqlens.numel() - 1
+    code = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        final_state = torch.empty((nseq, H, P, N), dtype=torch.float32, device=X.device)
+    need = ssd_chunk_scan_varlen_workspace_bytes(nseq, max_seqlen, H, P, N, G, chunk, code)
+    workspace, nbytes = _workspace(workspace, need, X.device)
+    st = lib.ssd_chunk_scan_fwd_varlen(_ptr(X), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), chunk,
+                                       _ptr(cu_seqlens), nseq, max_seqlen, total, _ptr(initial_state),
+                                       _ptr(Y), _ptr(final_state), H, P, N, G, code, _ptr(workspace),
+                                       nbytes, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_varlen")
+    return Y, final_state
 
 
 def raw_call(name: str, *args) -> int:

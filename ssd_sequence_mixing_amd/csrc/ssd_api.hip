@@ -34,9 +34,11 @@ struct FwdLayout {
 };
 
 // Shape checks shared by the workspace query and the forward entry points.
+// For a packed variable-length batch, batch is the number of sequences,
+// seqlen the longest one, and total the tokens in the packed tensors.
 ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                            int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
-                           FwdLayout *lay) {
+                           FwdLayout *lay, bool varlen = false, int64_t total = 0) {
     if (!valid_dtype(dtype)) return SSD_ERR_UNSUPPORTED;
     if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
         return SSD_ERR_SHAPE;
@@ -45,8 +47,9 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     if (!in_set(headdim, {16, 32, 64, 128}) || !in_set(dstate, {16, 32, 64, 128, 256}))
         return SSD_ERR_UNSUPPORTED;
     if (seqlen > kTwoGiB || nheads > 65536) return SSD_ERR_UNSUPPORTED;
+    if (total < 0 || total > kTwoGiB) return SSD_ERR_SHAPE;
     if (ssd::fwd_plan((ssd_dtype)dtype, batch, nheads, headdim, dstate, chunk, (seqlen + chunk - 1) / chunk,
-                      &lay->plan) != 0)
+                      !varlen, &lay->plan) != 0)
         return SSD_ERR_UNSUPPORTED;
     const int64_t es = esize((ssd_dtype)dtype);
     // 32-bit buffer offsets: every per-batch slab, padded to whole chunks, and
@@ -57,6 +60,8 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     if (Tpad * nheads * headdim * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (Tpad * ngroups * dstate * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
     if (Tpad * nheads * es >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
+    if (total * nheads * headdim * es >= kTwoGiB || total * ngroups * dstate * es >= kTwoGiB)
+        return SSD_ERR_UNSUPPORTED;
     lay->nC = nC;
     lay->Tpad = Tpad;
     lay->cs_bytes = align256(batch * nheads * Tpad * 4);
@@ -203,6 +208,47 @@ ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, con
     FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
                           workspace);
     f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y; f.final_state = final_state;
+    if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
+    return ssd::launch_walk(f, s);
+}
+
+size_t ssd_chunk_scan_varlen_workspace_bytes(int64_t num_seqs, int64_t max_seqlen, int64_t nheads,
+                                             int64_t headdim, int64_t dstate, int64_t ngroups,
+                                             int64_t chunk, ssd_dtype dtype) {
+    FwdLayout lay;
+    if (check_fwd_shape(num_seqs, max_seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay,
+                        true) != SSD_OK)
+        return (size_t)-1;
+    return (size_t)lay.total;
+}
+
+ssd_status ssd_chunk_scan_fwd_varlen(const void *X, const void *dt, const float *A, const void *B,
+                                     const void *C, const float *D, int64_t chunk,
+                                     const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                                     int64_t total_tokens, const float *initial_state, void *Y,
+                                     float *final_state, int64_t nheads, int64_t headdim,
+                                     int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    const bool empty = (num_seqs == 0 || max_seqlen == 0 || total_tokens == 0);
+    if (num_seqs > 0 && !cu_seqlens) return SSD_ERR_NULL;
+    if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
+    FwdLayout lay;
+    ssd_status st = check_fwd_shape(num_seqs, max_seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype,
+                                    &lay, true, total_tokens);
+    if (st != SSD_OK) return st;
+    if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(D) || !aligned16(Y) || !aligned16(initial_state) || !aligned16(final_state))
+        return SSD_ERR_ALIGN;
+    if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (num_seqs == 0) return SSD_OK;
+    if (empty)
+        return empty_final_state(final_state, initial_state, num_seqs * nheads * headdim * dstate, s);
+    FwdArgs f = make_args(lay, num_seqs, max_seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          workspace);
+    f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y;
+    f.init = initial_state; f.final_state = final_state;
+    f.cu = cu_seqlens; f.total = total_tokens;
     if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
     return ssd::launch_walk(f, s);
 }

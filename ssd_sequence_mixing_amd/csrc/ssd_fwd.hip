@@ -48,14 +48,30 @@
 namespace ssd {
 
 // ---------------------------------------------------------------------------
+// The tokens of batch element b: [start, start + len). In a packed
+// variable-length batch (cu = cumulative sequence lengths, on the device)
+// element b is sequence b, clamped to [0, total) and to at most T tokens;
+// otherwise every element has T tokens.
+// ---------------------------------------------------------------------------
+struct SeqRange {
+    int start, len;
+};
+__device__ __forceinline__ SeqRange seq_range(const int *cu, int total, int b, int T) {
+    if (!cu) return {b * T, T};
+    const int s0 = min(max(cu[b], 0), total);
+    const int s1 = min(max(cu[b + 1], s0), total);
+    return {s0, min(s1 - s0, T)};
+}
+
+// ---------------------------------------------------------------------------
 // dt_cumsum: one work-group per (batch, chunk, block of 16 heads)
 // ---------------------------------------------------------------------------
 constexpr int kCumsumHeads = 16;
 
 template <typename TI, int Q>
 __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, const float *__restrict__ A,
-                                          float *__restrict__ cs2, float *__restrict__ dtf, int T, int H,
-                                          int nC, int Tpad) {
+                                          float *__restrict__ cs2, float *__restrict__ dtf, int Tmax, int H,
+                                          int nC, int Tpad, const int *cu, int total) {
     constexpr int ES = Traits<TI>::kBytes;
     constexpr int LD = Q + 1;
     __shared__ float tile[kCumsumHeads * LD];
@@ -68,7 +84,9 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
     const int h0 = hb * kCumsumHeads;
     const int Hb = min(kCumsumHeads, H - h0);
     const int t0 = c * Q;
-    const rsrc_t r = make_rsrc(reinterpret_cast<const char *>(dt) + (size_t)b * T * H * ES,
+    const SeqRange sq = seq_range(cu, total, b, Tmax);
+    const int T = sq.len;
+    const rsrc_t r = make_rsrc(reinterpret_cast<const char *>(dt) + (size_t)sq.start * H * ES,
                                (uint32_t)((size_t)T * H * ES));
     // one token row per thread: all of its loads are issued before any is used
     for (int t = threadIdx.x; t < Q; t += 256) {
@@ -130,7 +148,8 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
 // ---------------------------------------------------------------------------
 template <typename TI, int N, int TT>
 __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, const TI *__restrict__ Cm,
-                                        TI *__restrict__ Gout, int T, int G, int ntiles, uint32_t g_bytes) {
+                                        TI *__restrict__ Gout, int Tmax, int G, int ntiles, uint32_t g_bytes,
+                                        const int *cu, int total) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
     constexpr int ES = Tr::kBytes;
@@ -145,9 +164,12 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
     const int b = x / ntiles;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int r = lane & 15, kg = lane >> 4;
+    const SeqRange sq = seq_range(cu, total, b, Tmax);
+    const int T = sq.len;
     const size_t slab = (size_t)T * G * N * ES;
-    const rsrc_t rb = make_rsrc(reinterpret_cast<const char *>(Bm) + b * slab, (uint32_t)slab);
-    const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(Cm) + b * slab, (uint32_t)slab);
+    const size_t sb0 = (size_t)sq.start * G * N * ES;
+    const rsrc_t rb = make_rsrc(reinterpret_cast<const char *>(Bm) + sb0, (uint32_t)slab);
+    const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(Cm) + sb0, (uint32_t)slab);
     const rsrc_t rg = make_rsrc(Gout, g_bytes);
     const int t0 = tau * TT;
     const int row = 64 * band + 16 * w + r;  // tile row of this lane's query token (B operand column)
@@ -201,9 +223,11 @@ template <typename TI, int Q, int N, int TT>
 __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
     const int blk = blockIdx.x;
     if (blk < a.cb_blocks) {
-        tile_cb<TI, N, TT>(blk, (const TI *)a.B, (const TI *)a.C, (TI *)a.Gbuf, a.T, a.G, a.ntiles, a.g_bytes);
+        tile_cb<TI, N, TT>(blk, (const TI *)a.B, (const TI *)a.C, (TI *)a.Gbuf, a.T, a.G, a.ntiles, a.g_bytes,
+                           a.cu, a.total);
     } else {
-        dt_cumsum<TI, Q>(blk - a.cb_blocks, (const TI *)a.dt, a.A, a.cs2, a.dtf, a.T, a.H, a.nC, a.Tpad);
+        dt_cumsum<TI, Q>(blk - a.cb_blocks, (const TI *)a.dt, a.A, a.cs2, a.dtf, a.T, a.H, a.nC, a.Tpad, a.cu,
+                         a.total);
     }
 }
 
@@ -347,8 +371,10 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     const int g = (h * G) / H;
     const int p0 = ps * PW;
     // this work-group's chunks, and the state it starts from / ends in
-    const int cb = seg * a.cps, ce = min(cb + a.cps, nC);
-    const int last_tile = ce * NT - 1;
+    const SeqRange sq = seq_range(a.cu, a.total, b, T);
+    const int nCb = (sq.len + Q - 1) / Q;  // chunks of this element (all nC unless packed)
+    const int cb = seg * a.cps, ce = min(cb + a.cps, nCb);
+    const int last_tile = max(ce * NT - 1, cb * NT);  // loads past the end reload it
     const size_t bhs = (size_t)bhi;
     // pass 1 (state only) enters every segment but the first with zero; the
     // full walk enters segment s with the scanned state in slot s - 1
@@ -366,12 +392,12 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     const int st = tid & 255;          // thread index within the role
     const int r = lane & 15, kg = lane >> 4;
 
-    const size_t xslab = (size_t)T * H * P * ES;
-    const size_t bslab = (size_t)T * G * N * ES;
-    const rsrc_t rx = make_rsrc(reinterpret_cast<const char *>(a.X) + b * xslab, (uint32_t)xslab);
-    const rsrc_t ry = make_rsrc(reinterpret_cast<char *>(a.Y) + b * xslab, (uint32_t)xslab);
-    const rsrc_t rbm = make_rsrc(reinterpret_cast<const char *>(a.B) + b * bslab, (uint32_t)bslab);
-    const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(a.C) + b * bslab, (uint32_t)bslab);
+    const size_t xslab = (size_t)sq.len * H * P * ES, x0 = (size_t)sq.start * H * P * ES;
+    const size_t bslab = (size_t)sq.len * G * N * ES, b0 = (size_t)sq.start * G * N * ES;
+    const rsrc_t rx = make_rsrc(reinterpret_cast<const char *>(a.X) + x0, (uint32_t)xslab);
+    const rsrc_t ry = make_rsrc(reinterpret_cast<char *>(a.Y) + x0, (uint32_t)xslab);
+    const rsrc_t rbm = make_rsrc(reinterpret_cast<const char *>(a.B) + b0, (uint32_t)bslab);
+    const rsrc_t rc = make_rsrc(reinterpret_cast<const char *>(a.C) + b0, (uint32_t)bslab);
     const rsrc_t rg = make_rsrc(a.Gbuf, a.g_bytes);
     const float *cs_row = a.cs2 + ((size_t)b * H + h) * a.Tpad;
     const float *cp_row = a.dtf + ((size_t)b * H + h) * a.Tpad;  // cs' = cs2 - log2(dt)
@@ -813,13 +839,13 @@ static int tile_q(int64_t Q, int64_t PW, int64_t N) {
 constexpr int kCUs = 256;
 
 int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64_t Q, int64_t nC,
-             WalkPlan *plan) {
+             bool segments, WalkPlan *plan) {
     const int64_t walks = batch * H;
     // Long sequences with few heads: split the sequence into S segments (at
     // least two chunks each) so that more, shorter walks fill the CUs; then
     // split heads' columns while walks are still fewer than CUs.
     int S = 1;
-    while (walks * 2 * S <= kCUs && nC / (2 * S) >= 2) S *= 2;
+    while (segments && walks * 2 * S <= kCUs && nC / (2 * S) >= 2) S *= 2;
     while (S > 1 && (S - 1) * ((nC + S - 1) / S) >= nC) S /= 2;  // no empty segment
     int ns = 1;
     while (ns < 4 && walks * S * 2 * ns <= kCUs && P % (2 * ns) == 0 && P / (2 * ns) >= 16) ns *= 2;
@@ -840,6 +866,7 @@ static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
     PrepArgs a;
     a.dt = f.dt; a.B = f.B; a.C = f.C; a.A = f.A; a.Gbuf = f.Gbuf; a.cs2 = f.cs2; a.dtf = f.dtf;
     a.T = (int)f.T; a.H = (int)f.H; a.G = (int)f.G; a.nC = (int)f.nC; a.Tpad = (int)f.Tpad;
+    a.cu = f.cu; a.total = (int)f.total;
     a.ntiles = (int)(f.Tpad / TT);
     a.g_bytes = (uint32_t)f.g_bytes;
     a.cb_blocks = (int)(f.batch * a.ntiles * f.G * (TT / 64));
@@ -864,6 +891,7 @@ static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
         wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
         wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
         wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg;
+        wa.cu = f.cu; wa.total = (int)f.total;
         const int64_t heads = f.batch * f.H * f.ns;
         if (f.S > 1) {
             wa.SL = f.S - 1;

@@ -16,6 +16,8 @@ struct FwdArgs {
     float *final_state;        // may be null
     const float *init;         // (batch, H, P, N) initial state, or null for zero
     int64_t batch, T, H, P, N, G, Q, nC, Tpad;
+    const int *cu;             // packed variable-length batch: (batch + 1) cumulative lengths, or null
+    int64_t total;             // tokens in the packed batch (cu != null)
     ssd_dtype dtype;
     float *cs2, *dtf;          // workspace: (batch, H, Tpad) each
     void *Gbuf;                // workspace: (batch, G, Tpad / tt, tt, tt) in the storage type
@@ -32,8 +34,9 @@ struct WalkPlan {
     int S, cps;   // sequence segments walked in parallel, chunks per segment
 };
 // Fills the plan; -1 if no kernel covers the shape.
+// segments: whether the sequence may be split (not for packed batches).
 int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64_t Q, int64_t nC,
-             WalkPlan *plan);
+             bool segments, WalkPlan *plan);
 
 // Kernel arguments of the chunk walk (passed by value).
 struct PrepArgs {
@@ -42,6 +45,8 @@ struct PrepArgs {
     void *Gbuf;
     float *cs2, *dtf;
     int T, H, G, nC, Tpad, ntiles, cb_blocks;
+    const int *cu;             // see FwdArgs
+    int total;
     uint32_t g_bytes;
 };
 
@@ -56,6 +61,8 @@ struct WalkArgs {
     int P, NS;                 // head dimension, and the work-groups sharing each head's P columns
     int S, SL, cps;            // sequence segments, segments in this launch, chunks per segment
     float *seg;                // (batch, H, S - 1, P, N) segment states (S > 1)
+    const int *cu;             // see FwdArgs
+    int total;
     uint32_t g_bytes;
 };
 
