@@ -190,3 +190,41 @@ def test_prepare_and_walk_shape_checks(kw, code):
 def test_prepare_and_walk_empty():
     assert prep(batch=0, wsp=None, wsb=0) == OK
     assert walk(batch=0, wsp=None, wsb=0) == OK
+
+
+def varlen(X=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, chunk=256, cu=P16, nseq=8, maxlen=2048,
+           total=8192, init=None, Y=P16, fin=P16, H=64, P=64, N=128, G=1, dtype=BF16, wsp=P16 * 16,
+           wsb=1 << 40, stream=None):
+    return ssd.raw_call("ssd_chunk_scan_fwd_varlen", X, dt, A, B, C, D, chunk, cu, nseq, maxlen, total,
+                        init, Y, fin, H, P, N, G, dtype, wsp, wsb, stream)
+
+
+def test_varlen_workspace_query():
+    q = ssd.load().ssd_chunk_scan_varlen_workspace_bytes
+    # packed batches are never split into segments: no segment states
+    assert q(1, 16384, 64, 64, 256, 8, 256, BF16) == 2 * 64 * 16384 * 4 + 8 * 16384 * 64 * 2
+    assert q(8, 2048, 64, 64, 128, 1, 256, BF16) == ws(8, 2048, 64, 64, 128, 1, 256, BF16)
+    assert q(8, 2048, 64, 64, 96, 1, 256, BF16) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("field", ["X", "dt", "A", "B", "C", "D", "Y", "cu"])
+def test_varlen_null(field):
+    assert varlen(**{field: None}) == ENULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nseq=-1), ESHAPE), (dict(maxlen=-1), ESHAPE), (dict(total=-3), ESHAPE),
+    (dict(H=64, G=3), ESHAPE), (dict(chunk=32), EUNSUP), (dict(total=1 << 40), ESHAPE),
+])
+def test_varlen_shape_checks(kw, code):
+    assert varlen(**kw) == code
+
+
+@pytest.mark.parametrize("field", ["X", "dt", "B", "Y", "init", "fin"])
+def test_varlen_alignment(field):
+    assert varlen(**{field: P16 + 4}) == EALIGN
+
+
+def test_varlen_workspace_and_empty():
+    assert varlen(wsp=None) == EWS
+    assert varlen(nseq=0, cu=None, wsp=None, wsb=0) == OK
