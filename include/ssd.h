@@ -198,6 +198,44 @@ ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A,
                     int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
                     void *stream);
 
+/*
+ * The same forward and decode step with a Mamba-2 layer's step-size prologue
+ * and output gate fused in (the SSD theory page's selective-SSM layer, section
+ * 4.1, gates the scan's output with SiLU(z); the Mamba explainer page makes
+ * the step size with a softplus, and in its training-stability notes, section
+ * 5.2, adds a learned bias to it):
+ *
+ *   dt_bias (nheads) float32, or NULL (zero)
+ *   dt_softplus   0: dt <- dt + dt_bias[h]
+ *                 1: dt <- softplus(dt + dt_bias[h])
+ *                 2: dt <- softplus(dt) + dt_bias[h]     (the explainer's order)
+ *                 softplus(v) = log(1 + e^v), all in fp32; other values return
+ *                 SSD_ERR_UNSUPPORTED
+ *   z  shaped like X (step: like x), dtype, or NULL: Y <- Y * z * sigmoid(z),
+ *                 computed in fp32 on the output (bf16 storage: on the
+ *                 bf16-rounded output, rounded again)
+ *
+ * The step sizes this makes must be positive, as ssd_chunk_scan_fwd requires
+ * (mode 1 always gives that; under modes 0 and 2 the bias must keep them so).
+ * With dt_bias = NULL, dt_softplus = 0 and z = NULL they are exactly
+ * ssd_chunk_scan_fwd and ssd_step. The prologue applies to real tokens only
+ * (padding past seqlen stays dt = 0). Other arguments, shapes, alignment
+ * (dt_bias and z 16-byte aligned too), workspace and errors as above.
+ */
+ssd_status ssd_chunk_scan_fwd_gated(const void *X, const void *dt, const float *dt_bias,
+                                    int dt_softplus, const float *A, const void *B, const void *C,
+                                    const float *D, const void *z, int64_t chunk, void *Y,
+                                    float *final_state, int64_t batch, int64_t seqlen,
+                                    int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                                    ssd_dtype dtype, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const float *dt_bias,
+                          int dt_softplus, const float *A, const void *B, const void *C,
+                          const float *D, const void *z, void *y, int64_t batch, int64_t nheads,
+                          int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

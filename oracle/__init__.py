@@ -17,6 +17,7 @@ import os
 import numpy as np
 
 from .dual import dual_form, decay_mask  # noqa: F401
+from .fused import dt_prologue, gate, silu, softplus  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")

@@ -16,7 +16,7 @@ __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "load", "lib_path", "ssd_status_string",
     "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_chunk_scan_prepare",
     "ssd_chunk_scan_walk", "ssd_step", "ssd_chunk_scan_varlen_workspace_bytes",
-    "ssd_chunk_scan_fwd_varlen", "EXPORTS",
+    "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_gated", "ssd_step_gated", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -28,7 +28,8 @@ _lib = None
 # Entry points include/ssd.h declares.
 EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd",
            "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step",
-           "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen")
+           "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen",
+           "ssd_chunk_scan_fwd_gated", "ssd_step_gated")
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -95,6 +96,12 @@ def load():
     lib.ssd_step.argtypes = [_V] * 8 + [_I] * 5 + [ctypes.c_int, _V]
     lib.ssd_chunk_scan_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_varlen_workspace_bytes.argtypes = [_I] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_fwd_gated.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_gated.argtypes = ([_V, _V, _V, ctypes.c_int] + [_V] * 5 + [_I, _V, _V] + [_I] * 6 +
+                                             [ctypes.c_int, _V, ctypes.c_size_t, _V])
+    lib.ssd_step_gated.restype = ctypes.c_int
+    lib.ssd_step_gated.argtypes = ([_V, _V, _V, _V, ctypes.c_int] + [_V] * 6 + [_I] * 5 +
+                                   [ctypes.c_int, _V])
     lib.ssd_chunk_scan_fwd_varlen.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_varlen.argtypes = ([_V] * 6 + [_I, _V] + [_I] * 3 + [_V, _V, _V] + [_I] * 4 +
                                               [ctypes.c_int, _V, ctypes.c_size_t, _V])
@@ -267,6 +274,47 @@ def ssd_chunk_scan_fwd_varlen(X, dt, A, B, C, D, chunk: int, cu_seqlens, max_seq
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_varlen")
     return Y, final_state
+
+
+def ssd_chunk_scan_fwd_gated(X, dt, A, B, C, D, chunk: int, *, dt_bias=None, dt_softplus: int = 0, z=None,
+                             Y=None, final_state=None, want_final: bool = True, workspace=None, stream=None):
+    """ssd_chunk_scan_fwd with the fused prologue (dt_bias, dt_softplus: 0 none,
+    1 softplus(dt + bias), 2 softplus(dt) + bias) and output gate Y * silu(z)."""
+    import torch
+    lib = load()
+    bsz, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=X.device)
+    need = ssd_chunk_scan_fwd_workspace_bytes(bsz, T, H, P, N, G, chunk, code)
+    workspace, nbytes = _workspace(workspace, need, X.device)
+    st = lib.ssd_chunk_scan_fwd_gated(_ptr(X), _ptr(dt), _ptr(dt_bias), int(dt_softplus), _ptr(A), _ptr(B),
+                                      _ptr(C), _ptr(D), _ptr(z), chunk, _ptr(Y), _ptr(final_state), bsz, T,
+                                      H, P, N, G, code, _ptr(workspace), nbytes, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_gated")
+    return Y, final_state
+
+
+def ssd_step_gated(state, x, dt, A, B, C, D, *, dt_bias=None, dt_softplus: int = 0, z=None, y=None,
+                   stream=None):
+    """ssd_step with the fused prologue and output gate (see ssd_chunk_scan_fwd_gated)."""
+    import torch
+    lib = load()
+    bsz, H, P, N = state.shape
+    G = B.shape[1]
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.ssd_step_gated(_ptr(state), _ptr(x), _ptr(dt), _ptr(dt_bias), int(dt_softplus), _ptr(A),
+                            _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(y), bsz, H, P, N, G, code,
+                            _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_step_gated")
+    return y
 
 
 def raw_call(name: str, *args) -> int:

@@ -190,6 +190,18 @@ ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, con
                               float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
                               int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
                               void *workspace, size_t workspace_bytes, void *stream) {
+    return ssd_chunk_scan_fwd_gated(X, dt, nullptr, 0, A, B, C, D, nullptr, chunk, Y, final_state, batch,
+                                    seqlen, nheads, headdim, dstate, ngroups, dtype, workspace,
+                                    workspace_bytes, stream);
+}
+
+ssd_status ssd_chunk_scan_fwd_gated(const void *X, const void *dt, const float *dt_bias, int dt_softplus,
+                                    const float *A, const void *B, const void *C, const float *D,
+                                    const void *z, int64_t chunk, void *Y, float *final_state,
+                                    int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                    int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+    if (dt_softplus < 0 || dt_softplus > 2) return SSD_ERR_UNSUPPORTED;
     const bool empty = (batch == 0 || seqlen == 0);
     // an empty problem reads no input, so its input pointers may be NULL
     if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
@@ -198,7 +210,7 @@ ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, con
         check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
     if (st != SSD_OK) return st;
     if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
-        !aligned16(D) || !aligned16(Y) || !aligned16(final_state))
+        !aligned16(D) || !aligned16(Y) || !aligned16(final_state) || !aligned16(dt_bias) || !aligned16(z))
         return SSD_ERR_ALIGN;
     if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -208,6 +220,7 @@ ssd_status ssd_chunk_scan_fwd(const void *X, const void *dt, const float *A, con
     FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
                           workspace);
     f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y; f.final_state = final_state;
+    f.dt_bias = dt_bias; f.softplus = dt_softplus; f.z = z;
     if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
     return ssd::launch_walk(f, s);
 }
@@ -257,13 +270,22 @@ ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A,
                     const void *C, const float *D, void *y, int64_t batch, int64_t nheads,
                     int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
                     void *stream) {
+    return ssd_step_gated(state, x, dt, nullptr, 0, A, B, C, D, nullptr, y, batch, nheads, headdim, dstate,
+                          ngroups, dtype, stream);
+}
+
+ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const float *dt_bias, int dt_softplus,
+                          const float *A, const void *B, const void *C, const float *D, const void *z,
+                          void *y, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                          int64_t ngroups, ssd_dtype dtype, void *stream) {
+    if (dt_softplus < 0 || dt_softplus > 2) return SSD_ERR_UNSUPPORTED;
     if (batch != 0 && (!state || !x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
     if (!valid_dtype((int)dtype)) return SSD_ERR_UNSUPPORTED;
     if (batch < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0) return SSD_ERR_SHAPE;
     if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
     if (!in_set(dstate, {4, 8, 16, 32, 64, 128, 256})) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(state) || !aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
-        !aligned16(C) || !aligned16(D) || !aligned16(y))
+        !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(dt_bias) || !aligned16(z))
         return SSD_ERR_ALIGN;
     if (batch == 0) return SSD_OK;
     const int64_t rows = batch * nheads * headdim;
@@ -271,6 +293,7 @@ ssd_status ssd_step(float *state, const void *x, const void *dt, const float *A,
     ssd::StepArgs a;
     a.state = state; a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
     a.batch = batch; a.H = nheads; a.P = headdim; a.N = dstate; a.G = ngroups; a.dtype = dtype;
+    a.dt_bias = dt_bias; a.softplus = dt_softplus; a.z = z;
     return ssd::launch_step(a, reinterpret_cast<hipStream_t>(stream));
 }
 

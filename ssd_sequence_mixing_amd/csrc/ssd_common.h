@@ -83,6 +83,22 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// The step-size prologue of a Mamba-2 layer, optionally fused into the core.
+// mode 0: dt = raw + bias; 1: dt = softplus(raw + bias); 2: dt = softplus(raw)
+// + bias (the bias after the softplus, as the Mamba explainer page's
+// training-stability notes write it). softplus(x) = log(1 + e^x), with log1p
+// for accuracy at large negative x and x itself above 20, where e^{-x} is
+// below fp32 resolution.
+__device__ __forceinline__ float softplus_f32(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+__device__ __forceinline__ float dt_prologue(float raw, float bias, int mode) {
+    if (mode == 1) return softplus_f32(raw + bias);
+    if (mode == 2) return softplus_f32(raw) + bias;
+    return raw + bias;
+}
+
+// The output gate: y * silu(z) = y * z / (1 + e^{-z}).
+__device__ __forceinline__ float silu_gate(float y, float z) { return y * (z / (1.f + expf(-z))); }
+
 // ---------------------------------------------------------------------------
 // Storage-type traits. A "fragment" is the 8 consecutive K-elements one lane
 // contributes to a 16x16x32 matrix-core product.

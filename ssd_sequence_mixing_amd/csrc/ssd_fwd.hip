@@ -71,7 +71,8 @@ constexpr int kCumsumHeads = 16;
 template <typename TI, int Q>
 __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, const float *__restrict__ A,
                                           float *__restrict__ cs2, float *__restrict__ dtf, int Tmax, int H,
-                                          int nC, int Tpad, const int *cu, int total) {
+                                          int nC, int Tpad, const int *cu, int total,
+                                          const float *__restrict__ dt_bias, int softplus) {
     constexpr int ES = Traits<TI>::kBytes;
     constexpr int LD = Q + 1;
     __shared__ float tile[kCumsumHeads * LD];
@@ -100,6 +101,13 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
             } else {
                 v[hl] = __builtin_bit_cast(float, buf_ld32(r, off));
             }
+        }
+        // the optional prologue (bias, softplus) applies to real tokens only:
+        // padding keeps dt = 0
+        if (dt_bias || softplus) {
+#pragma unroll
+            for (int hl = 0; hl < kCumsumHeads; ++hl)
+                if (hl < Hb && t0 + t < T) v[hl] = dt_prologue(v[hl], dt_bias ? dt_bias[h0 + hl] : 0.f, softplus);
         }
 #pragma unroll
         for (int hl = 0; hl < kCumsumHeads; ++hl) tile[hl * LD + t] = v[hl];
@@ -227,7 +235,7 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
                            a.cu, a.total);
     } else {
         dt_cumsum<TI, Q>(blk - a.cb_blocks, (const TI *)a.dt, a.A, a.cs2, a.dtf, a.T, a.H, a.nC, a.Tpad, a.cu,
-                         a.total);
+                         a.total, a.dt_bias, a.softplus);
     }
 }
 
@@ -458,9 +466,33 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         };
         // same issue order as inside the loop (C rows first), so that the
         // compiler's wait counts at the loop head fit both ways in
+        // the gate's z pieces (the 16-byte row pieces this lane stores), loaded
+        // a tile ahead like C; without z the resource is empty and they read 0
+        constexpr int VPR = PW * ES / 16;           // 16-byte vectors per row
+        constexpr int NZ = (16 * VPR + 63) / 64;    // per lane and row block
+        const bool gate = a.z != nullptr;
+        const rsrc_t rz = make_rsrc(reinterpret_cast<const char *>(a.z) + (gate ? x0 : 0),
+                                    gate ? (uint32_t)xslab : 0u);
+        u32x4 zq[NTT][NZ];
+        uint32_t vz[NZ];
+#pragma unroll
+        for (int k = 0; k < NZ; ++k) {
+            const int v = lane + 64 * k;
+            vz[k] = oob_if(v >= 16 * VPR, (uint32_t)(v / VPR) * x_tok + (uint32_t)((v % VPR) * 16));
+        }
+        auto load_z = [&](int tt) {  // z pieces of the tile at token tt
+#pragma unroll
+            for (int j = 0; j < NTT; ++j) {
+                const uint32_t sz = (uint32_t)(tt + 16 * rbk[j]) * x_tok + hp0;
+#pragma unroll
+                for (int k = 0; k < NZ; ++k) zq[j][k] = buf_ld128s(rz, vz[k], sz);
+            }
+        };
         load_c(cb * Q);
         __builtin_amdgcn_sched_barrier(0);
         load_g(cb * NT);
+        __builtin_amdgcn_sched_barrier(0);
+        load_z(cb * Q);
         frag hsf[kHSReg ? PB : 1][kHSReg ? NK : 1];
         __syncthreads();
         for (int c = cb; c < ce; ++c) {
@@ -556,17 +588,33 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                 wave_lds_order();
 #pragma unroll
                 for (int j = 0; j < NTT; ++j) {
-                    constexpr int VPR = PW * ES / 16;  // 16-byte vectors per row
                     const uint32_t sy = (uint32_t)(t0 + tile0 + 16 * rbk[j]) * x_tok + hp0;
 #pragma unroll
-                    for (int v = lane; v < 16 * VPR; v += 64) {
+                    for (int k = 0; k < NZ; ++k) {
+                        const int v = lane + 64 * k;
+                        if (NZ * 64 > 16 * VPR && v >= 16 * VPR) break;
                         const int rl = v / VPR, cv = v % VPR;
-                        const u32x4 d =
-                            *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
-                                                             (16 * rbk[j] + rl) * YS_LD * ES + cv * 16);
+                        u32x4 d = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
+                                                                   (16 * rbk[j] + rl) * YS_LD * ES + cv * 16);
+                        if (gate) {  // fused output gate y * silu(z), in fp32
+                            if constexpr (ES == 2) {
+                                bf16x8 yv = __builtin_bit_cast(bf16x8, d);
+                                const bf16x8 zv = __builtin_bit_cast(bf16x8, zq[j][k]);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) yv[e] = (bf16)silu_gate((float)yv[e], (float)zv[e]);
+                                d = __builtin_bit_cast(u32x4, yv);
+                            } else {
+                                f32x4 yv = __builtin_bit_cast(f32x4, d);
+                                const f32x4 zv = __builtin_bit_cast(f32x4, zq[j][k]);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) yv[e] = silu_gate(yv[e], zv[e]);
+                                d = __builtin_bit_cast(u32x4, yv);
+                            }
+                        }
                         buf_st128s(d, ry, (uint32_t)rl * x_tok + (uint32_t)(cv * 16), sy);
                     }
                 }
+                load_z(min(tau + 1, last_tile) * TT);
                 __syncthreads();
             });
         }
@@ -867,6 +915,7 @@ static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
     a.dt = f.dt; a.B = f.B; a.C = f.C; a.A = f.A; a.Gbuf = f.Gbuf; a.cs2 = f.cs2; a.dtf = f.dtf;
     a.T = (int)f.T; a.H = (int)f.H; a.G = (int)f.G; a.nC = (int)f.nC; a.Tpad = (int)f.Tpad;
     a.cu = f.cu; a.total = (int)f.total;
+    a.dt_bias = f.dt_bias; a.softplus = f.softplus;
     a.ntiles = (int)(f.Tpad / TT);
     a.g_bytes = (uint32_t)f.g_bytes;
     a.cb_blocks = (int)(f.batch * a.ntiles * f.G * (TT / 64));
@@ -891,7 +940,7 @@ static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
         wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
         wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
         wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg;
-        wa.cu = f.cu; wa.total = (int)f.total;
+        wa.cu = f.cu; wa.total = (int)f.total; wa.z = f.z;
         const int64_t heads = f.batch * f.H * f.ns;
         if (f.S > 1) {
             wa.SL = f.S - 1;

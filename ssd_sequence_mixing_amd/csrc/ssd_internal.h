@@ -18,6 +18,9 @@ struct FwdArgs {
     int64_t batch, T, H, P, N, G, Q, nC, Tpad;
     const int *cu;             // packed variable-length batch: (batch + 1) cumulative lengths, or null
     int64_t total;             // tokens in the packed batch (cu != null)
+    const float *dt_bias;      // fused prologue: dt = [softplus](dt + dt_bias[h]); null = no bias
+    int softplus;
+    const void *z;             // fused epilogue: Y *= silu(z), z shaped like X; null = no gate
     ssd_dtype dtype;
     float *cs2, *dtf;          // workspace: (batch, H, Tpad) each
     void *Gbuf;                // workspace: (batch, G, Tpad / tt, tt, tt) in the storage type
@@ -47,6 +50,8 @@ struct PrepArgs {
     int T, H, G, nC, Tpad, ntiles, cb_blocks;
     const int *cu;             // see FwdArgs
     int total;
+    const float *dt_bias;      // see FwdArgs
+    int softplus;
     uint32_t g_bytes;
 };
 
@@ -63,6 +68,7 @@ struct WalkArgs {
     float *seg;                // (batch, H, S - 1, P, N) segment states (S > 1)
     const int *cu;             // see FwdArgs
     int total;
+    const void *z;             // see FwdArgs
     uint32_t g_bytes;
 };
 
@@ -71,6 +77,9 @@ struct StepArgs {
     const void *x, *dt, *B, *C;
     const float *A, *D;
     void *y;
+    const float *dt_bias;      // see FwdArgs
+    int softplus;
+    const void *z;             // (batch, H, P) like x, or null
     int64_t batch, H, P, N, G;
     ssd_dtype dtype;
 };

@@ -5,6 +5,9 @@
 //   a = exp(dt[b,h] A[h]);  s[p,n] <- a s[p,n] + dt x[p] B[g,n];
 //   y[p] = sum_n s[p,n] C[g,n] + D[h] x[p]
 //
+// optionally with the layer's prologue and epilogue fused in: dt =
+// softplus(dt + dt_bias[h]) and y <- y * silu(z[p]).
+//
 // The state is the only large operand: the kernel streams it once in and
 // once out with 16-byte non-temporal accesses (it is not reused by this
 // step, so it should not displace anything in the caches). A row of N fp32
@@ -41,7 +44,8 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a, int pblocks) 
     const int64_t bb = bh / H;
     const int h = (int)(bh - bb * H);
     const int g = (h * G) / H;
-    const float dtv = Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[bh]);
+    float dtv = Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[bh]);
+    if (a.dt_bias || a.softplus) dtv = dt_prologue(dtv, a.dt_bias ? a.dt_bias[h] : 0.f, a.softplus);
     const float dec = fast_exp2(dtv * a.A[h] * kLog2e);
     const float Dh = a.D[h];
     float *srow = a.state + bh * P * N;
@@ -78,7 +82,11 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a, int pblocks) 
         if (ok) __builtin_nontemporal_store(sn, reinterpret_cast<f32x4 *>(srow + (int64_t)p[u] * N) + c4);
 #pragma unroll
         for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
-        if (ok && c4 == 0) reinterpret_cast<TI *>(a.y)[bh * P + p[u]] = Tr::from_f32(part + Dh * xv);
+        if (ok && c4 == 0) {
+            float yv = part + Dh * xv;
+            if (a.z) yv = silu_gate(yv, Tr::to_f32(reinterpret_cast<const TI *>(a.z)[bh * P + p[u]]));
+            reinterpret_cast<TI *>(a.y)[bh * P + p[u]] = Tr::from_f32(yv);
+        }
     }
 }
 

@@ -153,3 +153,48 @@ def test_planted_mistake_is_caught(kind):
         except (AssertionError, FloatingPointError, OverflowError, ValueError):
             failed.append(pin.__name__)
     assert failed, f"mutant {kind!r} passed every pin"
+
+
+# ---- the fused prologue / epilogue (oracle.fused) ----
+
+def test_softplus_pins():
+    import oracle
+    assert oracle.softplus(0.0) == np.log(2.0)
+    x = np.linspace(-30, 30, 601)
+    sp = oracle.softplus(x)
+    # softplus(x) - softplus(-x) = x (log(1+e^x) - log(1+e^-x) = log e^x), and it stays above max(x, 0)
+    assert np.max(np.abs(sp - oracle.softplus(-x) - x)) < 1e-12
+    assert np.all(sp > np.maximum(x, 0.0))
+    # far out it is e^x (left) and x + e^-x (right) to first order
+    assert abs(oracle.softplus(-30.0) / np.exp(-30.0) - 1) < 1e-12
+    assert abs(oracle.softplus(30.0) - 30.0 - np.exp(-30.0)) < 1e-14
+    assert oracle.softplus(800.0) == 800.0  # no overflow
+
+
+def test_dt_prologue_modes():
+    import oracle
+    dt = np.array([[-1.0, 0.5, 2.0]])
+    bias = np.array([0.25, -0.5, 1.0])
+    assert np.array_equal(oracle.dt_prologue(dt, None, 0), dt)
+    assert np.allclose(oracle.dt_prologue(dt, bias, 0), dt + bias)
+    assert np.allclose(oracle.dt_prologue(dt, bias, 1), np.log1p(np.exp(dt + bias)))
+    assert np.allclose(oracle.dt_prologue(dt, bias, 2), np.log1p(np.exp(dt)) + bias)
+    # the two orders differ unless the bias is zero
+    assert not np.allclose(oracle.dt_prologue(dt, bias, 1), oracle.dt_prologue(dt, bias, 2))
+    assert np.allclose(oracle.dt_prologue(dt, None, 1), oracle.dt_prologue(dt, None, 2))
+
+
+def test_silu_gate_pins():
+    import oracle
+    z = np.linspace(-40, 40, 801)
+    s = oracle.silu(z)
+    assert oracle.silu(0.0) == 0.0
+    # sigmoid(z) + sigmoid(-z) = 1, so silu(z) - silu(-z) = z
+    assert np.max(np.abs(s - oracle.silu(-z) - z)) < 1e-12
+    assert abs(oracle.silu(40.0) - 40.0) < 1e-15 * 40 + 40 * np.exp(-40.0) * 2
+    assert abs(oracle.silu(-40.0)) < 40 * np.exp(-40.0) * 1.01
+    y = np.array([1.5, -2.0, 3.0])
+    assert np.allclose(oracle.gate(y, np.zeros(3)), 0.0)
+    # for large z the gate passes y * z (sigmoid -> 1), for very negative z it closes
+    assert np.allclose(oracle.gate(y, np.full(3, 50.0)), 50.0 * y)
+    assert np.max(np.abs(oracle.gate(y, np.full(3, -50.0)))) < 1e-19
