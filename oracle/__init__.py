@@ -8,6 +8,8 @@ Pins (tests/test_oracle.py): the dense dual form, closed forms for a constant
 decay, the A = 0 linear-attention special case, the memoryless limit, the
 group mapping, causality, linearity, split invariance with an initial state,
 step/forward consistency and a hand-derived example under tests/golden/.
+The backward oracle (backward.py) is pinned in tests/test_oracle_bwd.py by
+finite differences of the forward, homogeneity identities and closed forms.
 """
 from __future__ import annotations
 
@@ -16,6 +18,7 @@ import os
 
 import numpy as np
 
+from .backward import bwd  # noqa: F401
 from .dual import dual_form, decay_mask  # noqa: F401
 from .fused import dt_prologue, gate, silu, softplus  # noqa: F401
 
