@@ -10,7 +10,8 @@ storage), with inputs resident in HBM. Three independent input / output /
 workspace sets rotate (444 MB together, more than the 256 MB Infinity Cache),
 so no step reads the previous step's data from the cache. The decode step is
 timed after the forward: 1000 ssd_step calls on the 256 x 64 x 64 x 128 fp32
-state. Prints one JSON line.
+state, then 20 backward passes (ssd_chunk_scan_bwd) of the forward workload,
+reported beside the forward. Prints one JSON line.
 
 The oracle is timed beside the GPU on a bounded sample of the same workload
 (whole batch elements, about ten seconds of host work) for the cpu_baseline
@@ -129,6 +130,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for counter runs: 5 walk launches, then 5 element-wise negations of a "
                          "512 MiB bf16 buffer (a copy of known size, to calibrate the counters); "
@@ -300,6 +303,43 @@ def main():
                          "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": dacc["bytes"],
                          "kernel": "k_step"}
         del state, dsets
+
+    bwd_ok = not args.no_backward and cfg.dtype == "bf16"
+    if bwd_ok:
+        try:
+            ssd.ssd_chunk_scan_bwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
+        except ssd.SSDError:
+            bwd_ok = False  # no backward kernel for this shape (e.g. N 256)
+            out["backward"] = None
+    if bwd_ok:
+        # one backward (ssd_chunk_scan_bwd) of the same workload; its states per
+        # 64-token tile (2 x 134 MB at the 1.3B shape) already exceed the cache
+        t = sets[0]
+        rng = np.random.default_rng(7)
+        dY = up(si.bf16_round_bits(rng.standard_normal((Bz, T, H, P)).astype(np.float32)))
+        nb = ssd.ssd_chunk_scan_bwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
+        bws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        def bwd():
+            return ssd.ssd_chunk_scan_bwd(t["X"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk, dY,
+                                          workspace=bws, stream=stream)
+        for _ in range(3):
+            bwd()
+        torch.cuda.synchronize()
+        bs, be = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bs.record(stream)
+        for _ in range(args.backward_steps):
+            bwd()
+        be.record(stream)
+        torch.cuda.synchronize()
+        ms_b = bs.elapsed_time(be) / args.backward_steps
+        es = 2
+        bbytes = 2 * (2 * Bz * T * H * P * es + Bz * T * H * es + 2 * Bz * T * G * N * es)
+        out["backward"] = {"workload": out["config"]["workload"], "ms_per_call": ms_b,
+                           "tokens_per_s": Bz * T / (ms_b / 1e3),
+                           "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
+                           "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
+                           "kernels": "k_state_pass x2, k_bwd_tile, k_bwd_fin, k_bwd_sum_bc (+ k_prepare)"}
+        del bws, dY
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(first_inp, cfg)

@@ -236,6 +236,51 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
                           int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
                           void *stream);
 
+/*
+ * Backward pass: the gradients of the scalar  <dY, Y> + <dF, final_state>
+ * for one ssd_chunk_scan_fwd (from initial_state, or zero), with respect to
+ * every input. Training needs them; the pages' speed comparisons are of
+ * training throughput (the SSD theory page, section 6.1). With
+ * a_t = exp(dt_t A), states s_t and the adjoint ds_t = dy_t C_t^T + a_{t+1}
+ * ds_{t+1} (plus dF at the last token), per head:
+ *   dX_t = dt_t ds_t B_t + D dY_t           dD = sum_t <dY_t, X_t>
+ *   dB_t = sum over the group's heads of dt_t ds_t^T X_t
+ *   dC_t = sum over the group's heads of s_t^T dY_t
+ *   ddt_t = X_t^T ds_t B_t + A a_t <ds_t, s_{t-1}>
+ *   dA = sum over batch and tokens of dt_t a_t <ds_t, s_{t-1}>
+ *   d_initial_state = a_0 ds_0
+ *
+ *   X, dt, A, B, C, D, chunk, initial_state: as for the forward
+ *   dY (batch, seqlen, nheads, headdim)       dtype     gradient of Y
+ *   d_final_state (batch, nheads, headdim, dstate) float32, or NULL (zero)
+ *   dX like X, ddt like dt, dB and dC like B   dtype     outputs (overwritten)
+ *   dA, dD (nheads)                           float32   outputs (overwritten)
+ *   d_initial_state (batch, nheads, headdim, dstate) float32, or NULL (not written)
+ *
+ * Arithmetic in fp32 from the stored inputs; the per-tile states handed
+ * between the passes are kept in the storage type. Supported: bf16 with
+ * headdim in {32, 64} and dstate in {32, 64, 128}; float32 with (headdim,
+ * dstate) in {(32, 32), (32, 64), (64, 32)}; other shapes return
+ * SSD_ERR_UNSUPPORTED. Workspace
+ * from ssd_chunk_scan_bwd_workspace_bytes ((size_t)-1 for an unsupported
+ * shape), 256-byte aligned; at the 1.3B-layer shape it holds two bf16 copies
+ * of the state per 64 tokens (134 MB each). Alignment, stream semantics and
+ * error behaviour as for the forward. With seqlen == 0, dA = dD = 0 and
+ * d_initial_state = d_final_state (or zero).
+ */
+size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads,
+                                          int64_t headdim, int64_t dstate, int64_t ngroups,
+                                          int64_t chunk, ssd_dtype dtype);
+
+ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, const void *B,
+                              const void *C, const float *D, int64_t chunk,
+                              const float *initial_state, const void *dY,
+                              const float *d_final_state, void *dX, void *ddt, float *dA,
+                              void *dB, void *dC, float *dD, float *d_initial_state,
+                              int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

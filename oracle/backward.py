@@ -42,7 +42,8 @@ def bwd(X, dt, A, B, C, D, ngroups: int, dY, init_state=None, d_final=None):
 
     Shapes as the forward oracle: X, dY (Bz,T,H,P); dt (Bz,T,H); A, D (H,);
     B, C (Bz,T,G,N); init_state, d_final (Bz,H,P,N) or None (zero).
-    Returns a dict with dX, ddt, dA, dB, dC, dD, dinit (all fp64).
+    Returns a dict with dX, ddt, dA, dB, dC, dD, dinit (all fp64), and lam
+    (Bz,T,H): Lambda_t = a_t <ds_t, s_{t-1}>, whose dt-weighted sum is dA.
     """
     X, dt, A, B, C, D, dY = map(_f64, (X, dt, A, B, C, D, dY))
     Bz, T, H, P = X.shape
@@ -66,6 +67,7 @@ def bwd(X, dt, A, B, C, D, ngroups: int, dY, init_state=None, d_final=None):
     dBh = np.empty((Bz, T, H, N))
     dCh = np.empty((Bz, T, H, N))
     dA = np.zeros(H)
+    lams = np.empty((Bz, T, H))
     ds = np.zeros((Bz, H, P, N)) if d_final is None else _f64(d_final).copy()
     for t in range(T - 1, -1, -1):
         ds += dY[:, t, :, :, None] * Ch[:, t, :, None, :]           # ds_t
@@ -74,6 +76,7 @@ def bwd(X, dt, A, B, C, D, ngroups: int, dY, init_state=None, d_final=None):
         dX[:, t] = dt[:, t, :, None] * v + D[None, :, None] * dY[:, t]
         dBh[:, t] = dt[:, t, :, None] * np.einsum('bhpn,bhp->bhn', ds, X[:, t])
         lam = np.einsum('bhpn,bhpn->bh', ds, a[:, t, :, None, None] * S[t])
+        lams[:, t] = lam
         ddt[:, t] = np.einsum('bhp,bhp->bh', X[:, t], v) + A[None, :] * lam
         dA += (dt[:, t] * lam).sum(axis=0)
         ds = a[:, t, :, None, None] * ds                            # adjoint entering s_{t-1}
@@ -83,4 +86,4 @@ def bwd(X, dt, A, B, C, D, ngroups: int, dY, init_state=None, d_final=None):
         dB[:, :, grp[h]] += dBh[:, :, h]
         dC[:, :, grp[h]] += dCh[:, :, h]
     dD = np.einsum('bthp,bthp->h', dY, X)
-    return {"dX": dX, "ddt": ddt, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dinit": ds}
+    return {"dX": dX, "ddt": ddt, "dA": dA, "dB": dB, "dC": dC, "dD": dD, "dinit": ds, "lam": lams}

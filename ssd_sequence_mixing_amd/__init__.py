@@ -16,7 +16,8 @@ __all__ = [
     "SSD_F32", "SSD_BF16", "SSDError", "load", "lib_path", "ssd_status_string",
     "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_chunk_scan_prepare",
     "ssd_chunk_scan_walk", "ssd_step", "ssd_chunk_scan_varlen_workspace_bytes",
-    "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_gated", "ssd_step_gated", "EXPORTS",
+    "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_gated", "ssd_step_gated",
+    "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -29,7 +30,8 @@ _lib = None
 EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd",
            "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step",
            "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen",
-           "ssd_chunk_scan_fwd_gated", "ssd_step_gated")
+           "ssd_chunk_scan_fwd_gated", "ssd_step_gated", "ssd_chunk_scan_bwd_workspace_bytes",
+           "ssd_chunk_scan_bwd")
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -105,6 +107,11 @@ def load():
     lib.ssd_chunk_scan_fwd_varlen.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_varlen.argtypes = ([_V] * 6 + [_I, _V] + [_I] * 3 + [_V, _V, _V] + [_I] * 4 +
                                               [ctypes.c_int, _V, ctypes.c_size_t, _V])
+    lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [_I] * 7 + [ctypes.c_int]
+    lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
+    lib.ssd_chunk_scan_bwd.argtypes = ([_V] * 6 + [_I] + [_V] * 10 + [_I] * 6 +
+                                       [ctypes.c_int, _V, ctypes.c_size_t, _V])
     _lib = lib
     return lib
 
@@ -315,6 +322,44 @@ def ssd_step_gated(state, x, dt, A, B, C, D, *, dt_bias=None, dt_softplus: int =
     if st != 0:
         raise SSDError(st, "ssd_step_gated")
     return y
+
+
+def ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                       dtype=SSD_BF16) -> int:
+    n = load().ssd_chunk_scan_bwd_workspace_bytes(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                                  int(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise SSDError(3, "ssd_chunk_scan_bwd_workspace_bytes")
+    return int(n)
+
+
+def ssd_chunk_scan_bwd(X, dt, A, B, C, D, chunk: int, dY, *, initial_state=None, d_final_state=None,
+                       want_initial_grad: bool = False, workspace=None, stream=None):
+    """Gradients of <dY, Y> + <dF, final_state> for ssd_chunk_scan_fwd(X, dt, A, B, C, D, chunk)
+    from initial_state (zero when None). Returns (dX, ddt, dA, dB, dC, dD, d_initial_state);
+    the last is None unless want_initial_grad."""
+    import torch
+    lib = load()
+    bsz, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(X)
+    dX, ddt = torch.empty_like(X), torch.empty_like(dt)
+    dB, dC = torch.empty_like(B), torch.empty_like(C)
+    dA = torch.empty((H,), dtype=torch.float32, device=X.device)
+    dD = torch.empty((H,), dtype=torch.float32, device=X.device)
+    dinit = (torch.empty((bsz, H, P, N), dtype=torch.float32, device=X.device)
+             if want_initial_grad else None)
+    nbytes = ssd_chunk_scan_bwd_workspace_bytes(bsz, T, H, P, N, G, chunk, code)
+    if workspace is None:
+        workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=X.device)
+    st = lib.ssd_chunk_scan_bwd(_ptr(X), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), int(chunk),
+                                _ptr(initial_state), _ptr(dY), _ptr(d_final_state), _ptr(dX), _ptr(ddt),
+                                _ptr(dA), _ptr(dB), _ptr(dC), _ptr(dD), _ptr(dinit), bsz, T, H, P, N, G,
+                                code, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_bwd")
+    return dX, ddt, dA, dB, dC, dD, dinit
 
 
 def raw_call(name: str, *args) -> int:

@@ -114,6 +114,49 @@ ssd_status empty_final_state(float *final_state, const float *init, int64_t n, h
                : SSD_ERR_HIP;
 }
 
+// Backward workspace: the forward's (log-decays, C B^T tiles) followed by the
+// per-tile states and adjoints, Lambda at every tile end, three per-token
+// scalars and the head blocks' partial dB / dC.
+struct BwdLayout {
+    FwdLayout fl;
+    int nblk;
+    int64_t ntiles, st_bytes, lamb_bytes, tok_bytes, part_bytes, total;
+};
+
+// Head blocks per group: the fewest (a divisor of the group's head count)
+// that give at least two work-groups per CU.
+int bwd_blocks(int64_t batch, int64_t ntiles, int64_t G, int64_t HG) {
+    for (int64_t k = 1; k <= HG; ++k)
+        if (HG % k == 0 && batch * ntiles * G * k >= 512) return (int)k;
+    return (int)HG;
+}
+
+ssd_status check_bwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                           int64_t ngroups, int64_t chunk, int dtype, BwdLayout *lay) {
+    ssd_status st = check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, &lay->fl);
+    if (st != SSD_OK) return st;
+    if (!ssd::bwd_supported((ssd_dtype)dtype, headdim, dstate)) return SSD_ERR_UNSUPPORTED;
+    const int64_t es = esize((ssd_dtype)dtype);
+    const int64_t Tpad = lay->fl.Tpad;
+    lay->ntiles = Tpad / 64;
+    if (batch * lay->ntiles * nheads > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    lay->nblk = bwd_blocks(batch, lay->ntiles, ngroups, nheads / ngroups);
+    lay->st_bytes = align256(batch * nheads * lay->ntiles * headdim * dstate * es);
+    lay->lamb_bytes = align256(batch * nheads * lay->ntiles * 4);
+    lay->tok_bytes = align256(batch * nheads * Tpad * 4);
+    lay->part_bytes = align256(batch * Tpad * lay->nblk * ngroups * dstate * 4);
+    const int64_t fwd = 2 * lay->fl.cs_bytes + lay->fl.g_bytes + lay->fl.seg_bytes;
+    lay->total = (batch == 0 || seqlen == 0)
+                     ? 0
+                     : fwd + 2 * lay->st_bytes + lay->lamb_bytes + 3 * lay->tok_bytes + 2 * lay->part_bytes;
+    return SSD_OK;
+}
+
+__global__ void k_zero(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0.f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +338,67 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
     a.batch = batch; a.H = nheads; a.P = headdim; a.N = dstate; a.G = ngroups; a.dtype = dtype;
     a.dt_bias = dt_bias; a.softplus = dt_softplus; a.z = z;
     return ssd::launch_step(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t ssd_chunk_scan_bwd_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                          int64_t dstate, int64_t ngroups, int64_t chunk, ssd_dtype dtype) {
+    BwdLayout lay;
+    if (check_bwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay) != SSD_OK)
+        return (size_t)-1;
+    return (size_t)lay.total;
+}
+
+ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, const void *B, const void *C,
+                              const float *D, int64_t chunk, const float *initial_state, const void *dY,
+                              const float *d_final_state, void *dX, void *ddt, float *dA, void *dB, void *dC,
+                              float *dD, float *d_initial_state, int64_t batch, int64_t seqlen, int64_t nheads,
+                              int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    if (batch > 0 && (!A || !D || !dA || !dD)) return SSD_ERR_NULL;
+    const bool empty = (batch == 0 || seqlen == 0);
+    if (!empty && (!X || !dt || !B || !C || !dY || !dX || !ddt || !dB || !dC)) return SSD_ERR_NULL;
+    BwdLayout lay;
+    ssd_status st = check_bwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
+    if (st != SSD_OK) return st;
+    if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D) ||
+        !aligned16(initial_state) || !aligned16(dY) || !aligned16(d_final_state) || !aligned16(dX) ||
+        !aligned16(ddt) || !aligned16(dA) || !aligned16(dB) || !aligned16(dC) || !aligned16(dD) ||
+        !aligned16(d_initial_state))
+        return SSD_ERR_ALIGN;
+    if (lay.total > 0) {
+        if (!workspace || workspace_bytes < (size_t)lay.total) return SSD_ERR_WORKSPACE;
+        if (((uintptr_t)workspace & 255u) != 0) return SSD_ERR_ALIGN;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (batch == 0) return SSD_OK;
+    if (seqlen == 0) {
+        // nothing flows through: dA = dD = 0, and the initial state's gradient is dF
+        if (ssd::launch(k_zero, dim3((unsigned)((nheads + 255) / 256)), dim3(256), s, dA, nheads) != hipSuccess ||
+            ssd::launch(k_zero, dim3((unsigned)((nheads + 255) / 256)), dim3(256), s, dD, nheads) != hipSuccess)
+            return SSD_ERR_HIP;
+        return empty_final_state(d_initial_state, d_final_state, batch * nheads * headdim * dstate, s);
+    }
+    ssd::BwdArgs w = {};
+    w.f = make_args(lay.fl, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, workspace);
+    w.f.X = X; w.f.dt = dt; w.f.A = A; w.f.B = B; w.f.C = C; w.f.D = D; w.f.init = initial_state;
+    char *ws = static_cast<char *>(workspace) + 2 * lay.fl.cs_bytes + lay.fl.g_bytes + lay.fl.seg_bytes;
+    w.Hst = ws; ws += lay.st_bytes;
+    w.Est = ws; ws += lay.st_bytes;
+    w.lamb = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
+    w.rbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
+    w.qbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
+    w.xybuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
+    w.dBp = reinterpret_cast<float *>(ws); ws += lay.part_bytes;
+    w.dCp = reinterpret_cast<float *>(ws);
+    w.nblk = lay.nblk;
+    w.dY = dY; w.dF = d_final_state; w.dX = dX; w.ddt = ddt; w.dB = dB; w.dC = dC;
+    w.dA = dA; w.dD = dD; w.dinit = d_initial_state;
+    if ((st = ssd::launch_prepare(w.f, s)) != SSD_OK) return st;
+    return ssd::launch_bwd(w, s);
 }
 
 }  // extern "C"

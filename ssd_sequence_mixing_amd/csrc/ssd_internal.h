@@ -84,6 +84,54 @@ struct StepArgs {
     ssd_dtype dtype;
 };
 
+// Backward pass (ssd_bwd.hip).
+struct StatePassArgs {          // k_state_pass
+    const void *U, *V;          // X / dY (batch, T, H, P) and B / C (batch, T, G, N)
+    const float *cs2, *dtf;     // log-decay workspace (batch, H, Tpad)
+    const float *init;          // state before the first tile walked (fp32), or null
+    void *Sst;                  // (batch, H, ntiles, P, N) storage type: the state entering each tile
+    float *out;                 // state after the last tile walked (fp32), or null
+    const void *Est;            // forward pass: the adjoints arriving at each tile (storage type)
+    float *lamb;                // forward pass: (batch, H, ntiles) <E_tile, state after the tile>
+    int H, G, T, Tpad, ntiles, tpc;  // tpc: 64-token tiles per chunk
+};
+
+struct BwdTileArgs {            // k_bwd_tile
+    const void *X, *dY, *B, *C, *dt;
+    const float *D;
+    const void *Hst, *Est;      // entering states / arriving adjoints per tile
+    const float *cs2, *dtf;
+    void *dX;
+    float *rbuf, *qbuf, *xybuf; // per (batch, head, token): x.v, dy.y' - dt x.v, dy.x
+    float *dBp, *dCp;           // (batch, Tpad, nblk, G, N) partial sums over head blocks
+    int H, G, T, Tpad, ntiles, tpc, nblk;
+};
+
+struct BwdFinArgs {             // k_bwd_fin
+    const float *qbuf, *rbuf, *xybuf, *lamb;
+    const void *dt;
+    const float *A;
+    void *ddt;
+    float *dA, *dD;
+    int batch, T, Tpad, H, ntiles;
+};
+
+struct BwdArgs {
+    FwdArgs f;                  // forward inputs and the prepared log-decays
+    const void *dY;
+    const float *dF;            // gradient of the final state, or null
+    void *dX, *ddt, *dB, *dC;
+    float *dA, *dD, *dinit;     // dinit may be null
+    void *Hst, *Est;            // workspace, storage type
+    float *lamb, *rbuf, *qbuf, *xybuf, *dBp, *dCp;  // workspace, fp32
+    int nblk;                   // head blocks per group
+};
+
+// Whether a backward kernel covers (dtype, P, N).
+bool bwd_supported(ssd_dtype dt, int64_t P, int64_t N);
+// The backward launches (after launch_prepare on the same FwdArgs).
+ssd_status launch_bwd(const BwdArgs &w, hipStream_t s);
+
 // Phase 1: chunk-local log-decay prefix sums and C B^T tiles into the workspace.
 ssd_status launch_prepare(const FwdArgs &f, hipStream_t s);
 // Phase 2: the chunk walk (reads the prepared workspace).

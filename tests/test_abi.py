@@ -228,3 +228,53 @@ def test_varlen_alignment(field):
 def test_varlen_workspace_and_empty():
     assert varlen(wsp=None) == EWS
     assert varlen(nseq=0, cu=None, wsp=None, wsb=0) == OK
+
+
+def bwd(X=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, chunk=256, init=None, dY=P16, dF=None, dX=P16, ddt=P16,
+        dA=P16, dB=P16, dC=P16, dD=P16, dinit=None, batch=4, T=2048, H=64, P=64, N=128, G=1, dtype=BF16,
+        wsp=P16 * 16, wsb=1 << 40, stream=None):
+    return ssd.raw_call("ssd_chunk_scan_bwd", X, dt, A, B, C, D, chunk, init, dY, dF, dX, ddt, dA, dB, dC, dD,
+                        dinit, batch, T, H, P, N, G, dtype, wsp, wsb, stream)
+
+
+def test_bwd_workspace_query():
+    q = ssd.load().ssd_chunk_scan_bwd_workspace_bytes
+    fwd = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
+    st = 4 * 64 * 32 * 64 * 128 * 2            # states per 64-token tile, bf16
+    lamb = 4 * 64 * 32 * 4
+    tok = 4 * 64 * 2048 * 4
+    nblk = 1                                    # 4 x 32 tiles x 1 group x 4 blocks = 512 work-groups
+    while 4 * 32 * nblk < 512:
+        nblk *= 2
+    part = 4 * 2048 * nblk * 128 * 4
+    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == fwd + 2 * st + lamb + 3 * tok + 2 * part
+    assert q(4, 2048, 64, 64, 256, 1, 256, BF16) == ctypes.c_size_t(-1).value   # N 256: not covered
+    assert q(4, 2048, 64, 128, 64, 1, 256, BF16) == ctypes.c_size_t(-1).value   # P 128: not covered
+    assert q(4, 2048, 64, 64, 128, 1, 256, F32) == ctypes.c_size_t(-1).value
+    assert q(2, 100, 4, 32, 64, 1, 64, F32) > 0
+    assert q(0, 2048, 64, 64, 128, 1, 256, BF16) == 0
+
+
+@pytest.mark.parametrize("field", ["X", "dt", "A", "B", "C", "D", "dY", "dX", "ddt", "dA", "dB", "dC", "dD"])
+def test_bwd_null(field):
+    assert bwd(**{field: None}) == ENULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ESHAPE), (dict(H=64, G=3), ESHAPE), (dict(chunk=32), EUNSUP),
+    (dict(N=256), EUNSUP), (dict(P=128), EUNSUP), (dict(dtype=F32), EUNSUP), (dict(dtype=7), EUNSUP),
+])
+def test_bwd_shape_checks(kw, code):
+    assert bwd(**kw) == code
+
+
+@pytest.mark.parametrize("field", ["X", "dY", "dX", "ddt", "dA", "dB", "dinit", "dF", "init"])
+def test_bwd_alignment(field):
+    assert bwd(**{field: P16 + 4}) == EALIGN
+
+
+def test_bwd_workspace_and_empty():
+    assert bwd(wsp=None) == EWS
+    assert bwd(wsb=1000) == EWS
+    assert bwd(wsp=P16 + 16) == EALIGN
+    assert bwd(batch=0, wsp=None, wsb=0) == OK
