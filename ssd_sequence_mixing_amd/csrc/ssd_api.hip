@@ -115,8 +115,9 @@ ssd_status empty_final_state(float *final_state, const float *init, int64_t n, h
 }
 
 // Backward workspace: the forward's (log-decays, C B^T tiles) followed by the
-// per-tile states and adjoints, Lambda at every tile end, three per-token
-// scalars and the head blocks' partial dB / dC.
+// per-tile states and adjoints, Lambda at every tile end and each tile's
+// shares of dA and dD, three per-token scalars and the head blocks' partial
+// dB / dC.
 struct BwdLayout {
     FwdLayout fl;
     int nblk;
@@ -148,7 +149,7 @@ ssd_status check_bwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     const int64_t fwd = 2 * lay->fl.cs_bytes + lay->fl.g_bytes + lay->fl.seg_bytes;
     lay->total = (batch == 0 || seqlen == 0)
                      ? 0
-                     : fwd + 2 * lay->st_bytes + lay->lamb_bytes + 3 * lay->tok_bytes + 2 * lay->part_bytes;
+                     : fwd + 2 * lay->st_bytes + 3 * lay->lamb_bytes + 3 * lay->tok_bytes + 2 * lay->part_bytes;
     return SSD_OK;
 }
 
@@ -389,6 +390,8 @@ ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, con
     w.Hst = ws; ws += lay.st_bytes;
     w.Est = ws; ws += lay.st_bytes;
     w.lamb = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
+    w.dApart = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
+    w.dDpart = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
     w.rbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
     w.qbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
     w.xybuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;

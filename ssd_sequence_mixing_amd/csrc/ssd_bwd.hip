@@ -32,7 +32,8 @@
 //                      inside the tile from h (entering state) and E (arriving
 //                      adjoint): y', v, dx, the per-token scalars of Lambda,
 //                      and dB, dC summed over the block's heads;
-//   k_bwd_fin          per head: Lambda inside each tile, ddt, dA, dD;
+//   k_bwd_fin          per (batch, head, tile): Lambda down the tile, ddt, and
+//                      the tile's shares of dA, dD (k_bwd_heads adds them up);
 //   k_bwd_sum_bc       dB and dC summed over head blocks, in the storage type.
 // Within a tile (t the row token, j <= t and u >= t other tokens of the
 // tile, cs the chunk-local base-2 log-decays, cs' = cs - log2 dt, r / e the
@@ -154,6 +155,70 @@ __device__ __forceinline__ void stage_N(rsrc_t rs, uint32_t off0, uint32_t rstri
     }
 }
 
+// Two-phase staging, so that a tile's global loads can be issued while the
+// previous one is computed: load() fills registers with an R x Cc tile in
+// units of 4 rows x 8 columns; store_T() / store_N() write them to LDS
+// transposed (dst[c * LD + q], rows optionally weighted) or as they are
+// (dst[q * LD + c]).
+template <typename TI, int R, int Cc, int NTH>
+struct TileRegs {
+    using Tr = Traits<TI>;
+    static constexpr int ES = Tr::kBytes, UR = R / 4, U = UR * (Cc / 8), K = (U + NTH - 1) / NTH;
+    typename Tr::frag v[K][4];
+    __device__ __forceinline__ void load(rsrc_t rs, uint32_t off0, uint32_t rstride, int tid) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int u = tid + k * NTH;
+            const int rq = u % UR, co = (u / UR) % (Cc / 8);
+            const uint32_t o = off0 + (uint32_t)(4 * rq) * rstride + (uint32_t)(8 * co * ES);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[k][i] = Tr::load_frag(rs, oob_if(u >= U, o + (uint32_t)i * rstride));
+        }
+    }
+    template <bool kW, typename WF>
+    __device__ __forceinline__ void store_T(TI *dst, int LD, int tid, WF wt) const {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int u = tid + k * NTH;
+            if (u >= U) continue;
+            const int rq = u % UR, co = u / UR;
+            if constexpr (kW) {
+                float w[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) w[i] = wt(4 * rq + i);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    lds_st4<TI>(dst + (8 * co + e) * LD + 4 * rq, Tr::frag_get(v[k][0], e) * w[0],
+                                Tr::frag_get(v[k][1], e) * w[1], Tr::frag_get(v[k][2], e) * w[2],
+                                Tr::frag_get(v[k][3], e) * w[3]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    TI *d = dst + (8 * co + e) * LD + 4 * rq;
+                    if constexpr (ES == 2) {
+                        const bf16x4 q = {v[k][0][e], v[k][1][e], v[k][2][e], v[k][3][e]};
+                        *reinterpret_cast<bf16x4 *>(d) = q;
+                    } else {
+                        const f32x4 q = {v[k][0][e], v[k][1][e], v[k][2][e], v[k][3][e]};
+                        *reinterpret_cast<f32x4 *>(d) = q;
+                    }
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store_N(TI *dst, int LD, int tid) const {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int u = tid + k * NTH;
+            if (u >= U) continue;
+            const int rq = u % UR, co = u / UR;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<typename Tr::frag *>(dst + (4 * rq + i) * LD + 8 * co) = v[k][i];
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // k_state_pass: one work-group (4 wavefronts) per (batch, head) walks the
 // tiles (backwards when kRev) with the P x N state in matrix-core
@@ -196,9 +261,38 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
             acc[pb][j] = v;
         }
     const int ntiles = a.ntiles;
-    for (int it = 0; it < ntiles; ++it) {
-        const int tau = kRev ? ntiles - 1 - it : it;
+    // a tile's U, V, per-token exponent terms (and, forward, the adjoint
+    // arriving at it), loaded two tiles ahead into one of two register sets
+    TileRegs<TI, kBT, P, 256> ur[2];
+    TileRegs<TI, kBT, N, 256> vr[2];
+    float wcs[2] = {0.f, 0.f};                   // this thread's token term (tid < 64)
+    float pcs_r[2] = {0.f, 0.f}, pcs_e[2] = {0.f, 0.f};
+    TI e4[2][PB][NBW][4];
+    auto issue = [&](int tau, auto Sc) {
+        constexpr int S = decltype(Sc)::value;
         const int t0 = tau * kBT;
+        ur[S].load(ru, (uint32_t)(((size_t)t0 * H + h) * P * ES), (uint32_t)(H * P * ES), tid);
+        vr[S].load(rv, (uint32_t)(((size_t)t0 * G + g) * N * ES), (uint32_t)(G * N * ES), tid);
+        pcs_r[S] = (tau % a.tpc == 0) ? 0.f : cs[t0 - 1];
+        pcs_e[S] = cs[t0 + kBT - 1];
+        wcs[S] = kRev ? cs[t0 + (tid & 63)] : cp[t0 + (tid & 63)];
+        if constexpr (!kRev) {
+            const TI *E = reinterpret_cast<const TI *>(a.Est) + ((size_t)bh * ntiles + tau) * P * N;
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int j = 0; j < NBW; ++j) {
+                    const int nb = w + 4 * j;
+                    if (nb < NB) lds_ld4<TI>(e4[S][pb][j], E + (16 * pb + r) * N + 16 * nb + 4 * kg);
+                }
+        }
+    };
+    auto tile_of = [&](int it) { return kRev ? max(ntiles - 1 - it, 0) : min(it, ntiles - 1); };
+    issue(tile_of(0), std::integral_constant<int, 0>{});
+    issue(tile_of(1), std::integral_constant<int, 1>{});
+    auto step = [&](int it, auto Sc) {
+        constexpr int S = decltype(Sc)::value;
+        const int tau = tile_of(it);
         TI *dst = reinterpret_cast<TI *>(a.Sst) + ((size_t)bh * ntiles + tau) * P * N;
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
@@ -207,15 +301,23 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
                 const int nb = w + 4 * j;
                 if (nb < NB) store4<TI>(dst + (16 * pb + r) * N + 16 * nb + 4 * kg, acc[pb][j]);
             }
-        const float cs_r = (tau % a.tpc == 0) ? 0.f : cs[t0 - 1];
-        const float cs_e = cs[t0 + kBT - 1];
-        if (tid < kBT) WT[tid] = kRev ? fast_exp2(cs[t0 + tid] - cs_r) : fast_exp2(cs_e - cp[t0 + tid]);
+        const float cs_r = pcs_r[S], cs_e = pcs_e[S];
+        if (tid < kBT) WT[tid] = kRev ? fast_exp2(wcs[S] - cs_r) : fast_exp2(cs_e - wcs[S]);
         __syncthreads();  // WT visible; the previous tile's reads of UT / VT are done
-        stage_T<TI, kBT, P, 256, false>(ru, (uint32_t)(((size_t)t0 * H + h) * P * ES), (uint32_t)(H * P * ES), UT,
-                                        T_LD, tid, [](int) { return 1.f; });
-        stage_T<TI, kBT, N, 256, true>(rv, (uint32_t)(((size_t)t0 * G + g) * N * ES), (uint32_t)(G * N * ES), VT,
-                                       T_LD, tid, [&](int q) { return WT[q]; });
+        ur[S].template store_T<false>(UT, T_LD, tid, [](int) { return 1.f; });
+        vr[S].template store_T<true>(VT, T_LD, tid, [&](int q) { return WT[q]; });
         __syncthreads();
+        TI ee[PB][NBW][4];
+        if constexpr (!kRev) {
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ee[pb][j][i] = e4[S][pb][j][i];
+        }
+        // the tile after next is loaded while this one is computed (past the end: a reload)
+        issue(tile_of(it + 2), Sc);
         const float dec = fast_exp2(cs_e - cs_r);
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
@@ -238,7 +340,6 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
         }
         if constexpr (!kRev) {
             // Lambda at the tile's end: <E of this tile, state after it>
-            const TI *E = reinterpret_cast<const TI *>(a.Est) + ((size_t)bh * ntiles + tau) * P * N;
             float part = 0.f;
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
@@ -246,10 +347,8 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
                 for (int j = 0; j < NBW; ++j) {
                     const int nb = w + 4 * j;
                     if (nb < NB) {
-                        TI e4[4];
-                        lds_ld4<TI>(e4, E + (16 * pb + r) * N + 16 * nb + 4 * kg);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) part += Tr::to_f32(e4[i]) * acc[pb][j][i];
+                        for (int i = 0; i < 4; ++i) part += Tr::to_f32(ee[pb][j][i]) * acc[pb][j][i];
                     }
                 }
 #pragma unroll
@@ -259,6 +358,10 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
             if (tid == 0) a.lamb[(size_t)bh * ntiles + tau] = (WT[0] + WT[1]) + (WT[2] + WT[3]);
         }
         __syncthreads();
+    };
+    for (int it = 0; it < ntiles; it += 2) {
+        step(it, std::integral_constant<int, 0>{});
+        if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
     }
     if (a.out) {
 #pragma unroll
@@ -299,8 +402,12 @@ struct BwdCfg {
     static constexpr bool kFits = LDS <= 160 * 1024 && P % 32 == 0 && N % 32 == 0;
 };
 
+// 8 wavefronts in two roles over the same staged tile and head: waves 0-3
+// (16 token rows each) form y', v, dX and the per-token scalars; waves 4-7
+// (same rows) form x.dy products, dC and dB. The roles share no results, so
+// the two waves on each SIMD overlap.
 template <typename TI, int P, int N>
-__global__ __launch_bounds__(256, 1) void k_bwd_tile(BwdTileArgs a) {
+__global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
     using Cfg = BwdCfg<TI, P, N>;
@@ -322,7 +429,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_tile(BwdTileArgs a) {
     const int tau = x % a.ntiles;
     const int b = x / a.ntiles;
     const int t0 = tau * kBT;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
+    constexpr int NTH = 512;
+    const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool roleA = wv < 4;  // wave-uniform
+    const int w = wv & 3;
     TI *OS = L + Cfg::OS_OFF + w * 16 * P_LD;
 
     const size_t xslab = (size_t)T * H * P * ES, bslab = (size_t)T * G * N * ES;
@@ -334,334 +445,399 @@ __global__ __launch_bounds__(256, 1) void k_bwd_tile(BwdTileArgs a) {
     const uint32_t b_tok = (uint32_t)(G * N * ES), x_tok = (uint32_t)(H * P * ES);
 
     // ---- per tile, shared by the block's heads ----
-    stage_T<TI, kBT, N, 256, false>(rb, (uint32_t)(((size_t)t0 * G + g) * N * ES), b_tok, BT, T_LD, tid,
+    stage_T<TI, kBT, N, NTH, false>(rb, (uint32_t)(((size_t)t0 * G + g) * N * ES), b_tok, BT, T_LD, tid,
                                     [](int) { return 1.f; });
-    stage_T<TI, kBT, N, 256, false>(rc, (uint32_t)(((size_t)t0 * G + g) * N * ES), b_tok, CT, T_LD, tid,
+    stage_T<TI, kBT, N, NTH, false>(rc, (uint32_t)(((size_t)t0 * G + g) * N * ES), b_tok, CT, T_LD, tid,
                                     [](int) { return 1.f; });
-    // this wave's rows t = 16 w + r of C and B (A operands), and C B^T both ways:
-    //   g1[jb][i] = C_t . B_j with j = 16 jb + 4 kg + i   (jb <= w)
-    //   g2[ub][i] = C_u . B_t with u = 16 ub + 4 kg + i   (ub >= w)
-    frag cw[NK], bw[NK];
-    const uint32_t grow = (uint32_t)((t0 * G + g) * N * ES);
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-        const uint32_t o = grow + (uint32_t)(16 * w + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
-        cw[kk] = Tr::load_frag(rc, o);
-        bw[kk] = Tr::load_frag(rb, o);
-    }
-    f32x4 g1[4], g2[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        g1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        g2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (q <= w) {
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const uint32_t o = grow + (uint32_t)(16 * q + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
-                g1[q] = Tr::mma(Tr::load_frag(rb, o), cw[kk], g1[q]);
-            }
-        }
-        if (q >= w) {
-#pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                const uint32_t o = grow + (uint32_t)(16 * q + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
-                g2[q] = Tr::mma(Tr::load_frag(rc, o), bw[kk], g2[q]);
-            }
-        }
-    }
-
-    f32x4 accb[NB], accc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        accb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     const int trow = 16 * w + r;  // this lane's row token for A operands (tile-local)
+    const int kc = w / 2;         // the k step holding the diagonal
+    const int rt = tid & 255;     // thread index within the role
+    constexpr bool kSplit = ES == 2;  // bf16: y' and v (which feed Lambda) take hi + lo
 
-    for (int k = 0; k < hpb; ++k) {
-        const int h = g * HG + blk * hpb + k;
-        const size_t bh = (size_t)b * H + h;
-        const float *cs = a.cs2 + bh * a.Tpad + t0;
-        const float *cp = a.dtf + bh * a.Tpad + t0;
-        const float cs_r = (tau % a.tpc == 0) ? 0.f : cs[-1];
-        const float cs_e = cs[kBT - 1];
-        const float Dh = a.D[h];
-        __syncthreads();  // the previous head's reads are done
-        if (tid < kBT) {
-            CS[tid] = cs[tid];
-            CP[tid] = cp[tid];
-            const int t = t0 + tid;
-            DT[tid] = t < T ? Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[((size_t)b * T + t) * H + h]) : 0.f;
-        }
-        const uint32_t xo = (uint32_t)(((size_t)t0 * H + h) * P * ES);
-        stage_T<TI, kBT, P, 256, false>(rx, xo, x_tok, XT, T_LD, tid, [](int) { return 1.f; });
-        stage_T<TI, kBT, P, 256, false>(rdy, xo, x_tok, DYT, T_LD, tid, [](int) { return 1.f; });
-        stage_N<TI, kBT, P, 256>(rx, xo, x_tok, XN, P_LD, tid);
-        stage_N<TI, kBT, P, 256>(rdy, xo, x_tok, DYN, P_LD, tid);
-        const size_t so = (bh * a.ntiles + tau) * (size_t)(P * N);
-        const rsrc_t rh = make_rsrc(reinterpret_cast<const TI *>(a.Hst) + so, (uint32_t)(P * N * ES));
-        const rsrc_t re = make_rsrc(reinterpret_cast<const TI *>(a.Est) + so, (uint32_t)(P * N * ES));
-        stage_N<TI, P, N, 256>(rh, 0u, (uint32_t)(N * ES), HN, N_LD, tid);
-        stage_N<TI, P, N, 256>(re, 0u, (uint32_t)(N * ES), EN, N_LD, tid);
-        stage_T<TI, P, N, 256, false>(rh, 0u, (uint32_t)(N * ES), HT, P_LD, tid, [](int) { return 1.f; });
-        stage_T<TI, P, N, 256, false>(re, 0u, (uint32_t)(N * ES), ET, P_LD, tid, [](int) { return 1.f; });
-        __syncthreads();
-
-        const float cs_t = CS[trow];  // A-operand row token
-        float cs_o[4], dt_o[4];       // output rows t = 16 w + 4 kg + i
+    // A operand (rows t = 16 w + r) over k slots of step k2 from two
+    // 16-column accumulator blocks: slot e < 4 is column 32 k2 + 4 kg + e of
+    // src[2 k2], slot e >= 4 column 32 k2 + 16 + 4 kg + e - 4 of src[2 k2 + 1];
+    // `causal`: keep columns j <= t weighted 2^{cs_t - cs'_j}, else columns
+    // u >= t weighted 2^{cs_u - cs_t}. With `lo`, also the rounding residual
+    // of each element in a second fragment (bf16), so hi + lo carries fp32.
+    auto make_a = [&](const f32x4 *src, int k2, bool causal, float cs_t, frag *lo) {
+        frag f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            cs_o[i] = CS[16 * w + 4 * kg + i];
-            dt_o[i] = DT[16 * w + 4 * kg + i];
-        }
-        // A operand (rows t = 16 w + r) over k slots of step k2 from two
-        // 16-column accumulator blocks: slot e < 4 is column 32 k2 + 4 kg + e of
-        // src[2 k2], slot e >= 4 column 32 k2 + 16 + 4 kg + e - 4 of src[2 k2 + 1];
-        // `causal`: keep columns j <= t weighted 2^{cs_t - cs'_j}, else columns
-        // u >= t weighted 2^{cs_u - cs_t}.
-        // With `lo`, also the rounding residual of each element in a second
-        // fragment (bf16 storage), so that hi + lo carries the fp32 value.
-        auto make_a = [&](const f32x4 *src, int k2, bool causal, frag *lo = nullptr) {
-            frag f;
+        for (int half = 0; half < 2; ++half) {
+            const int c0 = 32 * k2 + 16 * half + 4 * kg;
+            const f32x4 ref = *reinterpret_cast<const f32x4 *>((causal ? CP : CS) + c0);
+            const f32x4 sv = src[2 * k2 + half];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int c0 = 32 * k2 + 16 * half + 4 * kg;
-                const f32x4 ref = *reinterpret_cast<const f32x4 *>((causal ? CP : CS) + c0);
-                const f32x4 s = src[2 * k2 + half];
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + i;
+                float v;
+                if (causal) v = (c <= trow) ? sv[i] * fast_exp2(cs_t - ref[i]) : 0.f;
+                else v = (c >= trow) ? sv[i] * fast_exp2(ref[i] - cs_t) : 0.f;
+                Tr::frag_set(f, 4 * half + i, v);
+                if (lo) Tr::frag_set(*lo, 4 * half + i, v - Tr::frag_get(f, 4 * half + i));
+            }
+        }
+        return f;
+    };
+    // The two roles run separate loops with the same barriers, so that
+    // neither role's registers stay live in the other's code.
+    if (roleA) {
+        // ================= role A: y', v, dX, per-token scalars =================
+        // this wave's rows t = 16 w + r of C and B (A operands), and C B^T both ways:
+        //   g1[jb][i] = C_t . B_j with j = 16 jb + 4 kg + i   (jb <= w)
+        //   g2[ub][i] = C_u . B_t with u = 16 ub + 4 kg + i   (ub >= w)
+        frag cw[NK], bw[NK];
+        f32x4 g1[4], g2[4];
+        const uint32_t grow = (uint32_t)((t0 * G + g) * N * ES);
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const uint32_t o = grow + (uint32_t)(16 * w + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
+            cw[kk] = Tr::load_frag(rc, o);
+            bw[kk] = Tr::load_frag(rb, o);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            g1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            g2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (q <= w) {
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const uint32_t o = grow + (uint32_t)(16 * q + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
+                    g1[q] = Tr::mma(Tr::load_frag(rb, o), cw[kk], g1[q]);
+                }
+            }
+            if (q >= w) {
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    const uint32_t o = grow + (uint32_t)(16 * q + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
+                    g2[q] = Tr::mma(Tr::load_frag(rc, o), bw[kk], g2[q]);
+                }
+            }
+        }
+        // the next head's X, dY and per-token terms load while this head is computed
+        TileRegs<TI, kBT, P, 256> xr, dyr;
+        float pcs = 0.f, pcp = 0.f, pdt = 0.f;  // token t0 + (tid & 63) of the prefetched head
+        auto issue = [&](int k) {
+            const int h = g * HG + blk * hpb + k;
+            const size_t bh = (size_t)b * H + h;
+            const uint32_t xo = (uint32_t)(((size_t)t0 * H + h) * P * ES);
+            xr.load(rx, xo, x_tok, rt);
+            dyr.load(rdy, xo, x_tok, rt);
+            const int t = t0 + (tid & 63);
+            pcs = a.cs2[bh * a.Tpad + t];
+            pcp = a.dtf[bh * a.Tpad + t];
+            pdt = t < T ? Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[((size_t)b * T + t) * H + h]) : 0.f;
+        };
+        issue(0);
+        for (int k = 0; k < hpb; ++k) {
+            const int h = g * HG + blk * hpb + k;
+            const size_t bh = (size_t)b * H + h;
+            const float *cs = a.cs2 + bh * a.Tpad + t0;
+            const float cs_r = (tau % a.tpc == 0) ? 0.f : cs[-1];
+            const float cs_e = cs[kBT - 1];
+            const float Dh = a.D[h];
+            const uint32_t xo = (uint32_t)(((size_t)t0 * H + h) * P * ES);
+            __syncthreads();  // the previous head's reads are done
+            if (tid < kBT) {
+                CS[tid] = pcs;
+                CP[tid] = pcp;
+                DT[tid] = pdt;
+            }
+            xr.template store_T<false>(XT, T_LD, rt, [](int) { return 1.f; });
+            xr.store_N(XN, P_LD, rt);
+            dyr.template store_T<false>(DYT, T_LD, rt, [](int) { return 1.f; });
+            dyr.store_N(DYN, P_LD, rt);
+            __syncthreads();
+            issue(min(k + 1, hpb - 1));  // past the last head: a harmless reload
+            const float cs_t = CS[trow];
+            float cs_o[4], dt_o[4];  // output rows t = 16 w + 4 kg + i
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                cs_o[i] = CS[16 * w + 4 * kg + i];
+                dt_o[i] = DT[16 * w + 4 * kg + i];
+            }
+            // ---- y' (scan output) and v = ds B, both [t][p] ----
+            f32x4 ay[PB], av[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                ay[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                av[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk) {
+                    ay[pb] = Tr::mma(cw[kk], Tr::lds_frag(HN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), ay[pb]);
+                    av[pb] = Tr::mma(bw[kk], Tr::lds_frag(EN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), av[pb]);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int c = c0 + i;
-                    float v;
-                    if (causal) v = (c <= trow) ? s[i] * fast_exp2(cs_t - ref[i]) : 0.f;
-                    else v = (c >= trow) ? s[i] * fast_exp2(ref[i] - cs_t) : 0.f;
-                    Tr::frag_set(f, 4 * half + i, v);
-                    if (lo) Tr::frag_set(*lo, 4 * half + i, v - Tr::frag_get(f, 4 * half + i));
+                    ay[pb][i] *= fast_exp2(cs_o[i] - cs_r);
+                    av[pb][i] *= fast_exp2(cs_e - cs_o[i]);
                 }
             }
-            return f;
-        };
-        constexpr bool kSplit = ES == 2;  // bf16: y' and v (which feed Lambda) take hi + lo
-        const int kc = w / 2;  // the k step holding the diagonal
-
-        // ---- y' (scan output) and v = ds B, both [t][p] ----
-        f32x4 ay[PB], av[PB];
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
-            ay[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            av[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int k2 = 0; k2 < kBT / 32; ++k2) {
+                if (k2 <= kc) {
+                    frag lo;
+                    const frag m = make_a(g1, k2, true, cs_t, kSplit ? &lo : nullptr);
 #pragma unroll
-            for (int kk = 0; kk < NK; ++kk) {
-                ay[pb] = Tr::mma(cw[kk], Tr::lds_frag(HN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), ay[pb]);
-                av[pb] = Tr::mma(bw[kk], Tr::lds_frag(EN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), av[pb]);
-            }
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const TI *p = XT + (16 * pb + r) * T_LD + 32 * k2 + 4 * kg;
+                        const frag xb = lds_frag_split<TI>(p, p + 16);
+                        ay[pb] = Tr::mma(m, xb, ay[pb]);
+                        if constexpr (kSplit) ay[pb] = Tr::mma(lo, xb, ay[pb]);
+                    }
+                }
+                if (k2 >= kc) {
+                    frag lo;
+                    const frag m = make_a(g2, k2, false, cs_t, kSplit ? &lo : nullptr);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ay[pb][i] *= fast_exp2(cs_o[i] - cs_r);
-                av[pb][i] *= fast_exp2(cs_e - cs_o[i]);
-            }
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < kBT / 32; ++k2) {
-            if (k2 <= kc) {
-                frag lo;
-                const frag m = make_a(g1, k2, true, kSplit ? &lo : nullptr);
-#pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const TI *p = XT + (16 * pb + r) * T_LD + 32 * k2 + 4 * kg;
-                    const frag xb = lds_frag_split<TI>(p, p + 16);
-                    ay[pb] = Tr::mma(m, xb, ay[pb]);
-                    if constexpr (kSplit) ay[pb] = Tr::mma(lo, xb, ay[pb]);
+                    for (int pb = 0; pb < PB; ++pb) {
+                        const TI *p = DYT + (16 * pb + r) * T_LD + 32 * k2 + 4 * kg;
+                        const frag db = lds_frag_split<TI>(p, p + 16);
+                        av[pb] = Tr::mma(m, db, av[pb]);
+                        if constexpr (kSplit) av[pb] = Tr::mma(lo, db, av[pb]);
+                    }
                 }
             }
-            if (k2 >= kc) {
-                frag lo;
-                const frag m = make_a(g2, k2, false, kSplit ? &lo : nullptr);
+            // ---- dx, and the per-token scalars x.v, dy.y', dy.x ----
+            float sxv[4] = {0.f, 0.f, 0.f, 0.f}, sdy[4] = {0.f, 0.f, 0.f, 0.f}, sxy[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int pb = 0; pb < PB; ++pb) {
-                    const TI *p = DYT + (16 * pb + r) * T_LD + 32 * k2 + 4 * kg;
-                    const frag db = lds_frag_split<TI>(p, p + 16);
-                    av[pb] = Tr::mma(m, db, av[pb]);
-                    if constexpr (kSplit) av[pb] = Tr::mma(lo, db, av[pb]);
+            for (int pb = 0; pb < PB; ++pb) {
+                TI xs[4], ds[4];
+                lds_ld4<TI>(xs, XT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
+                lds_ld4<TI>(ds, DYT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float xv = Tr::to_f32(xs[i]), dv = Tr::to_f32(ds[i]);
+                    sxv[i] += xv * av[pb][i];
+                    sdy[i] += dv * ay[pb][i];
+                    sxy[i] += dv * xv;
+                    OS[(4 * kg + i) * P_LD + 16 * pb + r] = Tr::from_f32(dt_o[i] * av[pb][i] + Dh * dv);
                 }
             }
-        }
-        // ---- dx, and the per-token scalars x.v, dy.y', dy.x ----
-        float sxv[4] = {0.f, 0.f, 0.f, 0.f}, sdy[4] = {0.f, 0.f, 0.f, 0.f}, sxy[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
-            TI xs[4], ds[4];
-            lds_ld4<TI>(xs, XT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
-            lds_ld4<TI>(ds, DYT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
+            for (int m = 1; m < 16; m <<= 1)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float xv = Tr::to_f32(xs[i]), dv = Tr::to_f32(ds[i]);
-                sxv[i] += xv * av[pb][i];
-                sdy[i] += dv * ay[pb][i];
-                sxy[i] += dv * xv;
-                OS[(4 * kg + i) * P_LD + 16 * pb + r] = Tr::from_f32(dt_o[i] * av[pb][i] + Dh * dv);
+                for (int i = 0; i < 4; ++i) {
+                    sxv[i] += __shfl_xor(sxv[i], m);
+                    sdy[i] += __shfl_xor(sdy[i], m);
+                    sxy[i] += __shfl_xor(sxy[i], m);
+                }
+            if (r == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t o = bh * a.Tpad + t0 + 16 * w + 4 * kg + i;
+                    a.rbuf[o] = sxv[i];
+                    a.qbuf[o] = sdy[i] - dt_o[i] * sxv[i];
+                    a.xybuf[o] = sxy[i];
+                }
             }
-        }
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sxv[i] += __shfl_xor(sxv[i], m);
-                sdy[i] += __shfl_xor(sdy[i], m);
-                sxy[i] += __shfl_xor(sxy[i], m);
-            }
-        if (r == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const size_t o = bh * a.Tpad + t0 + 16 * w + 4 * kg + i;
-                a.rbuf[o] = sxv[i];
-                a.qbuf[o] = sdy[i] - dt_o[i] * sxv[i];
-                a.xybuf[o] = sxy[i];
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             constexpr int VPR = P * ES / 16;
             for (int v = lane; v < 16 * VPR; v += 64) {
                 const int rl = v / VPR, cv = v % VPR;
-                const u32x4 d = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(OS + rl * P_LD) +
-                                                                  cv * 16);
+                const u32x4 d =
+                    *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(OS + rl * P_LD) + cv * 16);
                 buf_st128(d, rdx, xo + (uint32_t)(16 * w + rl) * x_tok + (uint32_t)(cv * 16));
             }
         }
-
-        // ---- dC: 2^{cs_t - cs_r} dY h + (P1 o W1) B, P1[t][j] = x_j . dy_t ----
-        {
-            f32x4 p1[4];
+    } else {
+        // ================= role B: dC and dB, summed over the heads =================
+        f32x4 accb[NB], accc[NB];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                p1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (q <= w) {
+        for (int nb = 0; nb < NB; ++nb) {
+            accb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        TileRegs<TI, P, N, 256> hr, er;
+        auto issue = [&](int k) {
+            const int h = g * HG + blk * hpb + k;
+            const size_t so = (((size_t)b * H + h) * a.ntiles + tau) * (size_t)(P * N);
+            hr.load(make_rsrc(reinterpret_cast<const TI *>(a.Hst) + so, (uint32_t)(P * N * ES)), 0u,
+                    (uint32_t)(N * ES), rt);
+            er.load(make_rsrc(reinterpret_cast<const TI *>(a.Est) + so, (uint32_t)(P * N * ES)), 0u,
+                    (uint32_t)(N * ES), rt);
+        };
+        issue(0);
+        for (int k = 0; k < hpb; ++k) {
+            const int h = g * HG + blk * hpb + k;
+            const size_t bh = (size_t)b * H + h;
+            const float *cs = a.cs2 + bh * a.Tpad + t0;
+            const float cs_r = (tau % a.tpc == 0) ? 0.f : cs[-1];
+            const float cs_e = cs[kBT - 1];
+            __syncthreads();  // the previous head's reads are done
+            hr.store_N(HN, N_LD, rt);
+            hr.template store_T<false>(HT, P_LD, rt, [](int) { return 1.f; });
+            er.store_N(EN, N_LD, rt);
+            er.template store_T<false>(ET, P_LD, rt, [](int) { return 1.f; });
+            __syncthreads();
+            issue(min(k + 1, hpb - 1));
+            const float cs_t = CS[trow];
+            float cs_o[4], dt_o[4];
 #pragma unroll
-                    for (int kp = 0; kp < KP; ++kp)
-                        p1[q] = Tr::mma(Tr::lds_frag(XN + (16 * q + r) * P_LD + 32 * kp + 8 * kg),
-                                        Tr::lds_frag(DYN + trow * P_LD + 32 * kp + 8 * kg), p1[q]);
+            for (int i = 0; i < 4; ++i) {
+                cs_o[i] = CS[16 * w + 4 * kg + i];
+                dt_o[i] = DT[16 * w + 4 * kg + i];
+            }
+            // ---- dC: 2^{cs_t - cs_r} dY h + (P1 o W1) B, P1[t][j] = x_j . dy_t ----
+            {
+                f32x4 p1[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    p1[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (q <= w) {
+#pragma unroll
+                        for (int kp = 0; kp < KP; ++kp)
+                            p1[q] = Tr::mma(Tr::lds_frag(XN + (16 * q + r) * P_LD + 32 * kp + 8 * kg),
+                                            Tr::lds_frag(DYN + trow * P_LD + 32 * kp + 8 * kg), p1[q]);
+                    }
                 }
-            }
-            f32x4 tmp[NB];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                tmp[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kp = 0; kp < KP; ++kp)
-                    tmp[nb] = Tr::mma(Tr::lds_frag(DYN + trow * P_LD + 32 * kp + 8 * kg),
-                                      Tr::lds_frag(HT + (16 * nb + r) * P_LD + 32 * kp + 8 * kg), tmp[nb]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tmp[nb][i] *= fast_exp2(cs_o[i] - cs_r);
-            }
-#pragma unroll
-            for (int k2 = 0; k2 < kBT / 32; ++k2) {
-                if (k2 > kc) continue;
-                const frag m = make_a(p1, k2, true);
+                f32x4 tmp[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const TI *p = BT + (16 * nb + r) * T_LD + 32 * k2 + 4 * kg;
-                    tmp[nb] = Tr::mma(m, lds_frag_split<TI>(p, p + 16), tmp[nb]);
-                }
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) accc[nb] += tmp[nb];
-        }
-        // ---- dB: dt_t [2^{cs_e - cs_t} X E + (P2 o W2) C], P2[t][u] = dy_u . x_t ----
-        {
-            f32x4 p2[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                p2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (q >= w) {
+                    tmp[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
-                        p2[q] = Tr::mma(Tr::lds_frag(DYN + (16 * q + r) * P_LD + 32 * kp + 8 * kg),
-                                        Tr::lds_frag(XN + trow * P_LD + 32 * kp + 8 * kg), p2[q]);
+                        tmp[nb] = Tr::mma(Tr::lds_frag(DYN + trow * P_LD + 32 * kp + 8 * kg),
+                                          Tr::lds_frag(HT + (16 * nb + r) * P_LD + 32 * kp + 8 * kg), tmp[nb]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tmp[nb][i] *= fast_exp2(cs_o[i] - cs_r);
                 }
+#pragma unroll
+                for (int k2 = 0; k2 < kBT / 32; ++k2) {
+                    if (k2 > kc) continue;
+                    const frag m = make_a(p1, k2, true, cs_t, nullptr);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const TI *p = BT + (16 * nb + r) * T_LD + 32 * k2 + 4 * kg;
+                        tmp[nb] = Tr::mma(m, lds_frag_split<TI>(p, p + 16), tmp[nb]);
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) accc[nb] += tmp[nb];
             }
-            f32x4 tmp[NB];
+            // ---- dB: dt_t [2^{cs_e - cs_t} X E + (P2 o W2) C], P2[t][u] = dy_u . x_t ----
+            {
+                f32x4 p2[4];
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                tmp[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int q = 0; q < 4; ++q) {
+                    p2[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (q >= w) {
 #pragma unroll
-                for (int kp = 0; kp < KP; ++kp)
-                    tmp[nb] = Tr::mma(Tr::lds_frag(XN + trow * P_LD + 32 * kp + 8 * kg),
-                                      Tr::lds_frag(ET + (16 * nb + r) * P_LD + 32 * kp + 8 * kg), tmp[nb]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) tmp[nb][i] *= fast_exp2(cs_e - cs_o[i]);
-            }
-#pragma unroll
-            for (int k2 = 0; k2 < kBT / 32; ++k2) {
-                if (k2 < kc) continue;
-                const frag m = make_a(p2, k2, false);
+                        for (int kp = 0; kp < KP; ++kp)
+                            p2[q] = Tr::mma(Tr::lds_frag(DYN + (16 * q + r) * P_LD + 32 * kp + 8 * kg),
+                                            Tr::lds_frag(XN + trow * P_LD + 32 * kp + 8 * kg), p2[q]);
+                    }
+                }
+                f32x4 tmp[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
-                    const TI *p = CT + (16 * nb + r) * T_LD + 32 * k2 + 4 * kg;
-                    tmp[nb] = Tr::mma(m, lds_frag_split<TI>(p, p + 16), tmp[nb]);
+                    tmp[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kp = 0; kp < KP; ++kp)
+                        tmp[nb] = Tr::mma(Tr::lds_frag(XN + trow * P_LD + 32 * kp + 8 * kg),
+                                          Tr::lds_frag(ET + (16 * nb + r) * P_LD + 32 * kp + 8 * kg), tmp[nb]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) tmp[nb][i] *= fast_exp2(cs_e - cs_o[i]);
                 }
+#pragma unroll
+                for (int k2 = 0; k2 < kBT / 32; ++k2) {
+                    if (k2 < kc) continue;
+                    const frag m = make_a(p2, k2, false, cs_t, nullptr);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const TI *p = CT + (16 * nb + r) * T_LD + 32 * k2 + 4 * kg;
+                        tmp[nb] = Tr::mma(m, lds_frag_split<TI>(p, p + 16), tmp[nb]);
+                    }
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) accb[nb][i] += dt_o[i] * tmp[nb][i];
             }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) accb[nb][i] += dt_o[i] * tmp[nb][i];
         }
+        // dB, dC of this head block: part[b][t][blk][g][n] (fp32)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const size_t o =
+                    ((((size_t)b * a.Tpad + t0 + 16 * w + 4 * kg + i) * nblk + blk) * G + g) * N + 16 * nb + r;
+                a.dBp[o] = accb[nb][i];
+                a.dCp[o] = accc[nb][i];
+            }
     }
-    // dB, dC of this head block: part[b][t][blk][g][n] (fp32)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const size_t o = ((((size_t)b * a.Tpad + t0 + 16 * w + 4 * kg + i) * nblk + blk) * G + g) * N + 16 * nb + r;
-            a.dBp[o] = accb[nb][i];
-            a.dCp[o] = accc[nb][i];
-        }
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_fin: one work-group per head; each thread takes whole tiles of one
-// batch element: Lambda from the tile's end value down its tokens, ddt =
-// x.v + A Lambda, and the sums dA = sum dt Lambda, dD = sum dy.x (fixed
-// assignment and order: deterministic).
+// k_bwd_fin: one wavefront per (batch, head, tile), a lane per token: Lambda
+// down the tile from its end value (a suffix sum across the lanes), ddt =
+// x.v + A Lambda, and the tile's shares of dA = sum dt Lambda and
+// dD = sum dy.x. k_bwd_heads then adds the shares up per head in a fixed
+// order (deterministic).
 // ---------------------------------------------------------------------------
 template <typename TI>
 __global__ __launch_bounds__(256) void k_bwd_fin(BwdFinArgs a) {
-    __shared__ float part[256];
-    const int h = blockIdx.x, tid = threadIdx.x;
-    const int H = a.H, T = a.T, nt = a.ntiles;
-    const float Ah = a.A[h];
-    const TI *dtp = reinterpret_cast<const TI *>(a.dt);
-    TI *ddt = reinterpret_cast<TI *>(a.ddt);
-    float sdA = 0.f, sdD = 0.f;
-    for (int bt = tid; bt < a.batch * nt; bt += 256) {
-        const int b = bt / nt, tau = bt - b * nt;
-        const size_t bh = (size_t)b * H + h;
-        const float *q = a.qbuf + bh * a.Tpad, *rr = a.rbuf + bh * a.Tpad, *xy = a.xybuf + bh * a.Tpad;
-        float run = a.lamb[bh * nt + tau];
-        const int t0 = tau * kBT, t1 = min(T, t0 + kBT);
-        for (int t = t1 - 1; t >= t0; --t) {
-            run += q[t];
-            const size_t o = ((size_t)b * T + t) * H + h;
-            ddt[o] = Traits<TI>::from_f32(rr[t] + Ah * run);
-            sdA += Traits<TI>::to_f32(dtp[o]) * run;
-            sdD += xy[t];
-        }
+    const int lane = threadIdx.x & 63;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b H + h) ntiles + tau
+    const int nt = a.ntiles;
+    if (wid >= (int64_t)a.batch * a.H * nt) return;
+    const int tau = (int)(wid % nt);
+    const int64_t bh = wid / nt;
+    const int h = (int)(bh % a.H), b = (int)(bh / a.H);
+    const int t = tau * kBT + lane;
+    const bool real = t < a.T;
+    const size_t o = (size_t)bh * a.Tpad + t;
+    const size_t od = ((size_t)b * a.T + t) * a.H + h;
+    const float q = real ? a.qbuf[o] : 0.f;
+    float run = q;  // suffix sum over the lanes at and after this one
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float v = __shfl_down(run, m);
+        if (lane + m < 64) run += v;
     }
-    auto block_sum = [&](float v) {
-        part[tid] = v;
-        __syncthreads();
-        for (int s = 128; s > 0; s >>= 1) {
-            if (tid < s) part[tid] += part[tid + s];
-            __syncthreads();
+    run += a.lamb[wid];
+    float sdA = 0.f, sdD = 0.f;
+    if (real) {
+        reinterpret_cast<TI *>(a.ddt)[od] = Traits<TI>::from_f32(a.rbuf[o] + a.A[h] * run);
+        sdA = Traits<TI>::to_f32(reinterpret_cast<const TI *>(a.dt)[od]) * run;
+        sdD = a.xybuf[o];
+    }
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+        sdA += __shfl_xor(sdA, m);
+        sdD += __shfl_xor(sdD, m);
+    }
+    if (lane == 0) {
+        a.dApart[wid] = sdA;
+        a.dDpart[wid] = sdD;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_bwd_heads(const float *__restrict__ dApart, const float *__restrict__ dDpart,
+                                                   float *__restrict__ dA, float *__restrict__ dD, int batch, int H,
+                                                   int nt) {
+    __shared__ float sa[256], sd[256];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    float va = 0.f, vd = 0.f;
+    for (int i = tid; i < batch * nt; i += 256) {
+        const int b = i / nt, tau = i - b * nt;
+        const size_t o = ((size_t)b * H + h) * nt + tau;
+        va += dApart[o];
+        vd += dDpart[o];
+    }
+    sa[tid] = va;
+    sd[tid] = vd;
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+        if (tid < st) {
+            sa[tid] += sa[tid + st];
+            sd[tid] += sd[tid + st];
         }
-        const float r = part[0];
         __syncthreads();
-        return r;
-    };
-    sdA = block_sum(sdA);
-    sdD = block_sum(sdD);
+    }
     if (tid == 0) {
-        a.dA[h] = sdA;
-        a.dD[h] = sdD;
+        dA[h] = sa[0];
+        dD[h] = sd[0];
     }
 }
 
@@ -739,12 +915,17 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
         ta.H = (int)f.H; ta.G = (int)f.G; ta.T = (int)f.T; ta.Tpad = (int)f.Tpad; ta.ntiles = ntiles;
         ta.tpc = (int)(f.Q / kBT); ta.nblk = w.nblk;
         const int64_t tiles = f.batch * ntiles * f.G * w.nblk;
-        if (launch(k_bwd_tile<TI, P, N>, dim3((unsigned)tiles), dim3(256), s, ta) != hipSuccess) return SSD_ERR_HIP;
+        if (launch(k_bwd_tile<TI, P, N>, dim3((unsigned)tiles), dim3(512), s, ta) != hipSuccess) return SSD_ERR_HIP;
         BwdFinArgs fa = {};
         fa.qbuf = w.qbuf; fa.rbuf = w.rbuf; fa.xybuf = w.xybuf; fa.lamb = w.lamb; fa.dt = f.dt; fa.A = f.A;
-        fa.ddt = w.ddt; fa.dA = w.dA; fa.dD = w.dD;
+        fa.ddt = w.ddt;
         fa.batch = (int)f.batch; fa.T = (int)f.T; fa.Tpad = (int)f.Tpad; fa.H = (int)f.H; fa.ntiles = ntiles;
-        if (launch(k_bwd_fin<TI>, dim3((unsigned)f.H), dim3(256), s, fa) != hipSuccess) return SSD_ERR_HIP;
+        fa.dApart = w.dApart; fa.dDpart = w.dDpart;
+        const int64_t waves = f.batch * f.H * ntiles;
+        if (launch(k_bwd_fin<TI>, dim3((unsigned)((waves + 3) / 4)), dim3(256), s, fa) != hipSuccess ||
+            launch(k_bwd_heads, dim3((unsigned)f.H), dim3(256), s, (const float *)w.dApart, (const float *)w.dDpart,
+                   w.dA, w.dD, (int)f.batch, (int)f.H, ntiles) != hipSuccess)
+            return SSD_ERR_HIP;
         const int64_t n = f.batch * f.T * f.G * N;
         return launch(k_bwd_sum_bc<TI>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, (const float *)w.dBp,
                       (const float *)w.dCp, (TI *)w.dB, (TI *)w.dC, f.batch, (int)f.T, (int)f.Tpad, w.nblk,

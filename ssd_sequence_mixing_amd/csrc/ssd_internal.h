@@ -112,7 +112,7 @@ struct BwdFinArgs {             // k_bwd_fin
     const void *dt;
     const float *A;
     void *ddt;
-    float *dA, *dD;
+    float *dApart, *dDpart;     // (batch, H, ntiles) shares of dA, dD
     int batch, T, Tpad, H, ntiles;
 };
 
@@ -123,7 +123,8 @@ struct BwdArgs {
     void *dX, *ddt, *dB, *dC;
     float *dA, *dD, *dinit;     // dinit may be null
     void *Hst, *Est;            // workspace, storage type
-    float *lamb, *rbuf, *qbuf, *xybuf, *dBp, *dCp;  // workspace, fp32
+    float *lamb, *dApart, *dDpart;                  // workspace, fp32, (batch, H, ntiles) each
+    float *rbuf, *qbuf, *xybuf, *dBp, *dCp;          // workspace, fp32
     int nblk;                   // head blocks per group
 };
 

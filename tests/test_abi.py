@@ -247,7 +247,7 @@ def test_bwd_workspace_query():
     while 4 * 32 * nblk < 512:
         nblk *= 2
     part = 4 * 2048 * nblk * 128 * 4
-    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == fwd + 2 * st + lamb + 3 * tok + 2 * part
+    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == fwd + 2 * st + 3 * lamb + 3 * tok + 2 * part
     assert q(4, 2048, 64, 64, 256, 1, 256, BF16) == ctypes.c_size_t(-1).value   # N 256: not covered
     assert q(4, 2048, 64, 128, 64, 1, 256, BF16) == ctypes.c_size_t(-1).value   # P 128: not covered
     assert q(4, 2048, 64, 64, 128, 1, 256, F32) == ctypes.c_size_t(-1).value
