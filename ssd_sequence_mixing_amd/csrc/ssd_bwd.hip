@@ -220,9 +220,9 @@ struct TileRegs {
 };
 
 // ---------------------------------------------------------------------------
-// k_state_pass: one work-group (4 wavefronts) per (batch, head) walks the
+// k_state_pass: one work-group (8 wavefronts) per (batch, head) walks the
 // tiles (backwards when kRev) with the P x N state in matrix-core
-// accumulators, wave w owning the state's columns n in blocks w, w + 4, ...
+// accumulators, wave w owning the state's columns n in blocks w, w + 8, ...
 // Before each tile it stores the state it carries into Sst[tile] ([p][n],
 // storage type); after the last one it writes the state (fp32) to `out`.
 //   forward: S <- 2^{cs_e - cs_r} S + sum_t 2^{cs_e - cs'_t} x_t B_t^T
@@ -230,11 +230,12 @@ struct TileRegs {
 // (U = X or dY, V = B or C).
 // ---------------------------------------------------------------------------
 template <typename TI, int P, int N, bool kRev>
-__global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
+__global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
     constexpr int ES = Tr::kBytes, PAD = 16 / ES, T_LD = kBT + PAD;
-    constexpr int PB = P / 16, NB = N / 16, NBW = (NB + 3) / 4;
+    constexpr int NW = 8, NTH = 64 * NW;  // wavefronts; wave w owns n-blocks w, w + NW, ...
+    constexpr int PB = P / 16, NB = N / 16, NBW = (NB + NW - 1) / NW;
     __shared__ __attribute__((aligned(16))) TI UT[P * T_LD];
     __shared__ __attribute__((aligned(16))) TI VT[N * T_LD];
     __shared__ float WT[kBT];
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
     for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
-            const int nb = w + 4 * j;
+            const int nb = w + NW * j;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (a.init && nb < NB)
                 v = *reinterpret_cast<const f32x4 *>(a.init + ((size_t)bh * P + 16 * pb + r) * N + 16 * nb + 4 * kg);
@@ -263,8 +264,8 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
     const int ntiles = a.ntiles;
     // a tile's U, V, per-token exponent terms (and, forward, the adjoint
     // arriving at it), loaded two tiles ahead into one of two register sets
-    TileRegs<TI, kBT, P, 256> ur[2];
-    TileRegs<TI, kBT, N, 256> vr[2];
+    TileRegs<TI, kBT, P, NTH> ur[2];
+    TileRegs<TI, kBT, N, NTH> vr[2];
     float wcs[2] = {0.f, 0.f};                   // this thread's token term (tid < 64)
     float pcs_r[2] = {0.f, 0.f}, pcs_e[2] = {0.f, 0.f};
     TI e4[2][PB][NBW][4];
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
             for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
                 for (int j = 0; j < NBW; ++j) {
-                    const int nb = w + 4 * j;
+                    const int nb = w + NW * j;
                     if (nb < NB) lds_ld4<TI>(e4[S][pb][j], E + (16 * pb + r) * N + 16 * nb + 4 * kg);
                 }
         }
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
         for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
-                const int nb = w + 4 * j;
+                const int nb = w + NW * j;
                 if (nb < NB) store4<TI>(dst + (16 * pb + r) * N + 16 * nb + 4 * kg, acc[pb][j]);
             }
         const float cs_r = pcs_r[S], cs_e = pcs_e[S];
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
             for (int pb = 0; pb < PB; ++pb) ua[pb] = Tr::lds_frag(UT + (16 * pb + r) * T_LD + 32 * k2 + 8 * kg);
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
-                const int nb = w + 4 * j;
+                const int nb = w + NW * j;
                 if (nb < NB) {
                     const frag vb = Tr::lds_frag(VT + (16 * nb + r) * T_LD + 32 * k2 + 8 * kg);
 #pragma unroll
@@ -345,7 +346,7 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
             for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
                 for (int j = 0; j < NBW; ++j) {
-                    const int nb = w + 4 * j;
+                    const int nb = w + NW * j;
                     if (nb < NB) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) part += Tr::to_f32(ee[pb][j][i]) * acc[pb][j][i];
@@ -355,7 +356,12 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
             for (int m = 32; m > 0; m >>= 1) part += __shfl_xor(part, m);
             if (lane == 0) WT[w] = part;  // WT is free until the next tile's weights
             __syncthreads();
-            if (tid == 0) a.lamb[(size_t)bh * ntiles + tau] = (WT[0] + WT[1]) + (WT[2] + WT[3]);
+            if (tid == 0) {
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < NW; ++q) sum += WT[q];
+                a.lamb[(size_t)bh * ntiles + tau] = sum;
+            }
         }
         __syncthreads();
     };
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(256) void k_state_pass(StatePassArgs a) {
         for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
-                const int nb = w + 4 * j;
+                const int nb = w + NW * j;
                 if (nb < NB)
                     *reinterpret_cast<f32x4 *>(a.out + ((size_t)bh * P + 16 * pb + r) * N + 16 * nb + 4 * kg) =
                         acc[pb][j];
@@ -904,10 +910,10 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
         sp.Tpad = (int)f.Tpad; sp.ntiles = ntiles; sp.tpc = (int)(f.Q / kBT);
         const dim3 grid_bh((unsigned)(f.batch * f.H));
         sp.U = w.dY; sp.V = f.C; sp.init = w.dF; sp.Sst = w.Est; sp.out = w.dinit;
-        if (launch(k_state_pass<TI, P, N, true>, grid_bh, dim3(256), s, sp) != hipSuccess) return SSD_ERR_HIP;
+        if (launch(k_state_pass<TI, P, N, true>, grid_bh, dim3(512), s, sp) != hipSuccess) return SSD_ERR_HIP;
         sp.U = f.X; sp.V = f.B; sp.init = f.init; sp.Sst = w.Hst; sp.out = nullptr;
         sp.Est = w.Est; sp.lamb = w.lamb;
-        if (launch(k_state_pass<TI, P, N, false>, grid_bh, dim3(256), s, sp) != hipSuccess) return SSD_ERR_HIP;
+        if (launch(k_state_pass<TI, P, N, false>, grid_bh, dim3(512), s, sp) != hipSuccess) return SSD_ERR_HIP;
         BwdTileArgs ta = {};
         ta.X = f.X; ta.dY = w.dY; ta.B = f.B; ta.C = f.C; ta.dt = f.dt; ta.D = f.D;
         ta.Hst = w.Hst; ta.Est = w.Est; ta.cs2 = f.cs2; ta.dtf = f.dtf;
