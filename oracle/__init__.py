@@ -20,7 +20,7 @@ import numpy as np
 
 from .backward import bwd  # noqa: F401
 from .dual import dual_form, decay_mask  # noqa: F401
-from .fused import dt_prologue, gate, silu, softplus  # noqa: F401
+from .fused import causal_conv1d, conv_silu, dt_prologue, gate, silu, softplus  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")

@@ -198,3 +198,28 @@ def test_silu_gate_pins():
     # for large z the gate passes y * z (sigmoid -> 1), for very negative z it closes
     assert np.allclose(oracle.gate(y, np.full(3, 50.0)), 50.0 * y)
     assert np.max(np.abs(oracle.gate(y, np.full(3, -50.0)))) < 1e-19
+
+
+def test_causal_conv1d_pins():
+    import oracle
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((2, 13, 5))
+    w = rng.standard_normal((5, 4))
+    bias = rng.standard_normal(5)
+    out = oracle.causal_conv1d(x, w, bias)
+    # each channel is numpy's full convolution with the reversed taps, first T samples
+    for b in range(2):
+        for c in range(5):
+            ref = np.convolve(x[b, :, c], w[c, ::-1])[:13] + bias[c]
+            assert np.max(np.abs(out[b, :, c] - ref)) < 1e-12
+    # the last tap alone is the identity; the first alone a 3-token delay
+    e = np.zeros((5, 4)); e[:, 3] = 1.0
+    assert np.allclose(oracle.causal_conv1d(x, e, np.zeros(5)), x)
+    d = np.zeros((5, 4)); d[:, 0] = 1.0
+    sh = oracle.causal_conv1d(x, d, np.zeros(5))
+    assert np.allclose(sh[:, 3:], x[:, :-3]) and not np.any(sh[:, :3])
+    # causal: changing token 7 leaves outputs before it unchanged
+    x2 = x.copy(); x2[:, 7] += 1.0
+    assert np.array_equal(oracle.causal_conv1d(x2, w, bias)[:, :7], out[:, :7])
+    # conv_silu is SiLU of it
+    assert np.allclose(oracle.conv_silu(x, w, bias), out / (1 + np.exp(-out)))
