@@ -10,8 +10,9 @@ storage), with inputs resident in HBM. Three independent input / output /
 workspace sets rotate (444 MB together, more than the 256 MB Infinity Cache),
 so no step reads the previous step's data from the cache. The decode step is
 timed after the forward: 1000 ssd_step calls on the 256 x 64 x 64 x 128 fp32
-state, then 20 backward passes (ssd_chunk_scan_bwd) of the forward workload,
-reported beside the forward. Prints one JSON line.
+state, then 50 forwards with the fused layer prologue / epilogue
+(ssd_chunk_scan_fwd_fused) and 20 backward passes (ssd_chunk_scan_bwd) of
+the forward workload, reported beside the forward. Prints one JSON line.
 
 The oracle is timed beside the GPU on a bounded sample of the same workload
 (whole batch elements, about ten seconds of host work) for the cpu_baseline
@@ -131,6 +132,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for counter runs: 5 walk launches, then 5 element-wise negations of a "
@@ -303,6 +305,36 @@ def main():
                          "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": dacc["bytes"],
                          "kernel": "k_step"}
         del state, dsets
+
+    if not args.no_fused:
+        # the forward with the layer's fused prologue and epilogue (causal conv1d +
+        # SiLU on X, softplus(dt + bias), Y * SiLU(z)) on the same workload
+        t = sets[0]
+        rng = np.random.default_rng(8)
+        cw = up((0.5 * rng.standard_normal((H * P, 4))).astype(np.float32))
+        cb = up((0.1 * rng.standard_normal(H * P)).astype(np.float32))
+        dtb = up((0.5 * rng.standard_normal(H)).astype(np.float32))
+        zz = torch.empty_like(t["X"]).normal_()
+        Yf = torch.empty_like(t["X"])
+        Ff = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dev)
+        def fused():
+            return ssd.ssd_chunk_scan_fwd_fused(t["X"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk,
+                                                conv_w=cw, conv_b=cb, dt_bias=dtb, dt_softplus=1, z=zz, Y=Yf,
+                                                final_state=Ff, workspace=t["W"], stream=stream)
+        for _ in range(5):
+            fused()
+        torch.cuda.synchronize()
+        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fs.record(stream)
+        for _ in range(50):
+            fused()
+        fe.record(stream)
+        torch.cuda.synchronize()
+        ms_f = fs.elapsed_time(fe) / 50
+        out["fused"] = {"workload": out["config"]["workload"] + ", conv1d(4)+SiLU on X, softplus(dt+bias), "
+                                    "Y*SiLU(z)", "ms_per_call": ms_f, "tokens_per_s": Bz * T / (ms_f / 1e3),
+                        "vs_plain_forward": ms_f / ms_step}
+        del zz, Yf, Ff
 
     bwd_ok = not args.no_backward and cfg.dtype == "bf16"
     if bwd_ok:

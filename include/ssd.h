@@ -230,6 +230,34 @@ ssd_status ssd_chunk_scan_fwd_gated(const void *X, const void *dt, const float *
                                     ssd_dtype dtype, void *workspace, size_t workspace_bytes,
                                     void *stream);
 
+/*
+ * The gated forward with the layer's input activation fused in as well: X
+ * arrives before the causal convolution over time and the SiLU that the SSD
+ * theory page's selective-SSM layer (section 4.1) applies to the scan's
+ * input; the Mamba explainer page's block structure (section 4.1) gives the
+ * 4-token window. Read as depthwise: for channel c = h * headdim + p,
+ *
+ *   X'[b,t,h,p] = SiLU(conv_b[c] + sum_{k<4} conv_w[c][k] X[b, t-3+k, h, p]),
+ *
+ * X = 0 before each sequence's first token, in fp32 from the stored X; X'
+ * (rounded to the storage type) is the scan's input and the D skip's.
+ *
+ *   conv_w (nheads * headdim, 4) float32, 16-byte aligned, or NULL (no
+ *          convolution: exactly ssd_chunk_scan_fwd_gated)
+ *   conv_b (nheads * headdim) float32, or NULL (zero bias); must be NULL when
+ *          conv_w is
+ * Other arguments as ssd_chunk_scan_fwd_gated. B, C and dt are taken as given
+ * (the page's listing derives them from the activated input outside the
+ * core). SSD_ERR_UNSUPPORTED where the walk cannot also hold the taps in LDS.
+ */
+ssd_status ssd_chunk_scan_fwd_fused(const void *X, const float *conv_w, const float *conv_b,
+                                    const void *dt, const float *dt_bias, int dt_softplus,
+                                    const float *A, const void *B, const void *C, const float *D,
+                                    const void *z, int64_t chunk, void *Y, float *final_state,
+                                    int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                    int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const float *dt_bias,
                           int dt_softplus, const float *A, const void *B, const void *C,
                           const float *D, const void *z, void *y, int64_t batch, int64_t nheads,

@@ -17,7 +17,7 @@ __all__ = [
     "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_chunk_scan_prepare",
     "ssd_chunk_scan_walk", "ssd_step", "ssd_chunk_scan_varlen_workspace_bytes",
     "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_gated", "ssd_step_gated",
-    "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "EXPORTS",
+    "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -31,7 +31,7 @@ EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk
            "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step",
            "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen",
            "ssd_chunk_scan_fwd_gated", "ssd_step_gated", "ssd_chunk_scan_bwd_workspace_bytes",
-           "ssd_chunk_scan_bwd")
+           "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused")
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -107,6 +107,9 @@ def load():
     lib.ssd_chunk_scan_fwd_varlen.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_varlen.argtypes = ([_V] * 6 + [_I, _V] + [_I] * 3 + [_V, _V, _V] + [_I] * 4 +
                                               [ctypes.c_int, _V, ctypes.c_size_t, _V])
+    lib.ssd_chunk_scan_fwd_fused.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_fused.argtypes = ([_V] * 5 + [ctypes.c_int] + [_V] * 5 + [_I, _V, _V] + [_I] * 6 +
+                                             [ctypes.c_int, _V, ctypes.c_size_t, _V])
     lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [_I] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
@@ -303,6 +306,31 @@ def ssd_chunk_scan_fwd_gated(X, dt, A, B, C, D, chunk: int, *, dt_bias=None, dt_
                                       H, P, N, G, code, _ptr(workspace), nbytes, _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_gated")
+    return Y, final_state
+
+
+def ssd_chunk_scan_fwd_fused(X, dt, A, B, C, D, chunk: int, *, conv_w=None, conv_b=None, dt_bias=None,
+                             dt_softplus: int = 0, z=None, Y=None, final_state=None, want_final: bool = True,
+                             workspace=None, stream=None):
+    """ssd_chunk_scan_fwd_gated with the input activation fused in: X is taken before the
+    causal 4-tap depthwise convolution (conv_w (H*P, 4), conv_b (H*P) fp32) and SiLU."""
+    import torch
+    lib = load()
+    bsz, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    code = _dtype_code(X)
+    if Y is None:
+        Y = torch.empty_like(X)
+    if final_state is None and want_final:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=X.device)
+    need = ssd_chunk_scan_fwd_workspace_bytes(bsz, T, H, P, N, G, chunk, code)
+    workspace, nbytes = _workspace(workspace, need, X.device)
+    st = lib.ssd_chunk_scan_fwd_fused(_ptr(X), _ptr(conv_w), _ptr(conv_b), _ptr(dt), _ptr(dt_bias),
+                                      int(dt_softplus), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), chunk,
+                                      _ptr(Y), _ptr(final_state), bsz, T, H, P, N, G, code, _ptr(workspace),
+                                      nbytes, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_fused")
     return Y, final_state
 
 

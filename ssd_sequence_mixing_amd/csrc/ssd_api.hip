@@ -245,7 +245,20 @@ ssd_status ssd_chunk_scan_fwd_gated(const void *X, const void *dt, const float *
                                     int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                                     int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
                                     size_t workspace_bytes, void *stream) {
+    return ssd_chunk_scan_fwd_fused(X, nullptr, nullptr, dt, dt_bias, dt_softplus, A, B, C, D, z, chunk, Y,
+                                    final_state, batch, seqlen, nheads, headdim, dstate, ngroups, dtype, workspace,
+                                    workspace_bytes, stream);
+}
+
+ssd_status ssd_chunk_scan_fwd_fused(const void *X, const float *conv_w, const float *conv_b, const void *dt,
+                                    const float *dt_bias, int dt_softplus, const float *A, const void *B,
+                                    const void *C, const float *D, const void *z, int64_t chunk, void *Y,
+                                    float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
+                                    int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                                    void *workspace, size_t workspace_bytes, void *stream) {
     if (dt_softplus < 0 || dt_softplus > 2) return SSD_ERR_UNSUPPORTED;
+    if (!conv_w && conv_b) return SSD_ERR_NULL;
+    if (!aligned16(conv_w) || ((uintptr_t)conv_b & 3u) != 0) return SSD_ERR_ALIGN;
     const bool empty = (batch == 0 || seqlen == 0);
     // an empty problem reads no input, so its input pointers may be NULL
     if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
@@ -253,6 +266,7 @@ ssd_status ssd_chunk_scan_fwd_gated(const void *X, const void *dt, const float *
     ssd_status st =
         check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
     if (st != SSD_OK) return st;
+    if (conv_w && !ssd::walk_conv_fits(dtype, chunk, headdim / lay.plan.ns, dstate)) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
         !aligned16(D) || !aligned16(Y) || !aligned16(final_state) || !aligned16(dt_bias) || !aligned16(z))
         return SSD_ERR_ALIGN;
@@ -265,6 +279,7 @@ ssd_status ssd_chunk_scan_fwd_gated(const void *X, const void *dt, const float *
                           workspace);
     f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y; f.final_state = final_state;
     f.dt_bias = dt_bias; f.softplus = dt_softplus; f.z = z;
+    f.conv_w = conv_w; f.conv_b = conv_b;
     if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
     return ssd::launch_walk(f, s);
 }

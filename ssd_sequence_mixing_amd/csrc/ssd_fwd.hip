@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
 // four consecutive n of one row p: the LDS copy and the final state are
 // written four elements at a time.
 // ---------------------------------------------------------------------------
-template <typename TI, int Q, int PW, int N, int TT>
+template <typename TI, int Q, int PW, int N, int TT, bool kConv = false>
 struct WalkCfg {
     static constexpr int ES = Traits<TI>::kBytes;
     static constexpr int NTT = TT / 64;              // 16-row blocks per output wave
@@ -295,11 +295,14 @@ struct WalkCfg {
     static constexpr int HS_OFF = CS_OFF + CS_BYTES;
     static constexpr int HS_BYTES = PW * HS_LD * ES;
     static constexpr int BT_BYTES = N * BT_LD * ES;
-    static constexpr int BASE = HS_OFF + HS_BYTES + BT_BYTES;
+    // the fused input convolution's taps and bias for this slice's columns (fp32)
+    static constexpr int CW_BYTES = kConv ? PW * 5 * 4 : 0;
+    static constexpr int BASE = HS_OFF + HS_BYTES + BT_BYTES + CW_BYTES;
     static constexpr bool kBT2 = BASE + BT_BYTES <= 160 * 1024;             // double B^T
     static constexpr bool kHS2 = BASE + (kBT2 ? BT_BYTES : 0) + HS_BYTES <= 160 * 1024;
     static constexpr int BT_OFF = HS_OFF + (kHS2 ? 2 : 1) * HS_BYTES;
-    static constexpr int LDS = BT_OFF + (kBT2 ? 2 : 1) * BT_BYTES;
+    static constexpr int CW_OFF = BT_OFF + (kBT2 ? 2 : 1) * BT_BYTES;
+    static constexpr int LDS = CW_OFF + CW_BYTES;
     static constexpr bool kFits = LDS <= 160 * 1024 && Q % TT == 0;
     static constexpr bool kMidSync = !kBT2 || !kHS2;
     // loads run two tiles ahead of the staging when a chunk has an even
@@ -344,10 +347,14 @@ __device__ __forceinline__ void wave_lds_order() { __builtin_amdgcn_fence(__ATOM
 
 // kStateOnly: the state waves alone (256 threads), for the first pass of a
 // sequence split: each segment's end state from its own entering state.
-template <typename TI, int Q, int PW, int N, int TT, bool kStateOnly>
+// kConv: X arrives before the layer's causal convolution (4 taps per
+// channel, with bias) and SiLU; the state waves apply both while staging
+// each tile, reading the 3 tokens before it as well (zeros before the
+// sequence's first token).
+template <typename TI, int Q, int PW, int N, int TT, bool kStateOnly, bool kConv>
 __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkArgs a) {
     using Tr = Traits<TI>;
-    using Cfg = WalkCfg<TI, Q, PW, N, TT>;
+    using Cfg = WalkCfg<TI, Q, PW, N, TT, kConv>;
     using frag = typename Tr::frag;
     constexpr int ES = Cfg::ES, NT = Cfg::NT, NTT = Cfg::NTT, KB = Cfg::KB, PB = Cfg::PB, NB = Cfg::NB;
     constexpr int NBW = Cfg::NBW, NK = Cfg::NK, TQ = Cfg::TQ;
@@ -360,6 +367,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);  // [buf][cs2 Q | cs' Q]
     TI *HSB = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);        // [copy][p][n]
     TI *BTB = reinterpret_cast<TI *>(smem + Cfg::BT_OFF);        // [copy][n][token], weighted
+    float *CWL = reinterpret_cast<float *>(smem + Cfg::CW_OFF);  // conv taps [col][4], then bias [col]
 
     const int H = a.H, G = a.G, T = a.T, nC = a.nC, P = a.P, NS = a.NS;
     const int ntiles = nC * NT;
@@ -392,6 +400,9 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     float *out_mat = kStateOnly ? a.seg + (bhs * (S - 1) + seg) * P * N
                                 : ((seg == S - 1 && a.final_state) ? a.final_state + bhs * P * N : nullptr);
 
+    // which role stages X: the output waves in the full walk without the
+    // input convolution, else the state waves
+    constexpr bool kXOut = !kStateOnly && !kConv;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
     const bool out_wave = !kStateOnly && wv < 4;
@@ -417,6 +428,14 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     for (int k = tid; k < Q; k += NTH) {
         CSB[k] = cs_row[cb * Q + k];
         CSB[Q + k] = cp_row[cb * Q + k];
+    }
+    if constexpr (kConv) {
+        for (int k = tid; k < PW; k += NTH) {
+            const int col = h * P + p0 + k;
+            *reinterpret_cast<f32x4 *>(CWL + 4 * k) = *reinterpret_cast<const f32x4 *>(a.conv_w + 4 * (size_t)col);
+            CWL[4 * PW + k] = a.conv_b ? a.conv_b[col] : 0.f;
+        }
+        __syncthreads();  // the state waves stage a tile before their first barrier
     }
     if constexpr (N % 32 != 0) {
         constexpr int PADN = NK * 32 - N;
@@ -450,14 +469,14 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         // C rows and the C B^T rows of the next tile are loaded while this one
         // is computed (C right after its last use, C B^T after the diagonal).
         frag cf[NTT][NK], gd[NTT][KB];
-        auto load_c = [&](int tt) {  // C rows of the tile at token tt
+        auto load_c = [&](int tt) __attribute__((always_inline)) {  // C rows of the tile at token tt
             const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
 #pragma unroll
             for (int j = 0; j < NTT; ++j)
 #pragma unroll
                 for (int kk = 0; kk < NK; ++kk) cf[j][kk] = Tr::load_frag_s(rc, vc[j][kk], sb);
         };
-        auto load_g = [&](int tau) {  // this wave's rows of the tile's C B^T
+        auto load_g = [&](int tau) __attribute__((always_inline)) {  // this wave's rows of the tile's C B^T
             const uint32_t sg = (uint32_t)((gbase + tau) * (size_t)(TT * TT * ES));
 #pragma unroll
             for (int j = 0; j < NTT; ++j)
@@ -480,7 +499,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
             const int v = lane + 64 * k;
             vz[k] = oob_if(v >= 16 * VPR, (uint32_t)(v / VPR) * x_tok + (uint32_t)((v % VPR) * 16));
         }
-        auto load_z = [&](int tt) {  // z pieces of the tile at token tt
+        auto load_z = [&](int tt) __attribute__((always_inline)) {  // z pieces of the tile at token tt
 #pragma unroll
             for (int j = 0; j < NTT; ++j) {
                 const uint32_t sz = (uint32_t)(tt + 16 * rbk[j]) * x_tok + hp0;
@@ -488,6 +507,74 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                 for (int k = 0; k < NZ; ++k) zq[j][k] = buf_ld128s(rz, vz[k], sz);
             }
         };
+        // With kXOut, X of the tile after this one is staged by the output
+        // waves (the state waves, which carry the recurrence, are the busier
+        // role): units of 4 tokens x 8 columns, loaded a tile ahead of their
+        // staging. (With the input convolution the state waves keep it: its
+        // arithmetic made the output waves the slower role.)
+        auto ox_unit = [&](int k) __attribute__((always_inline)) {
+            return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (tid + 256 * k < UX);
+        };
+        frag oxr[RX][4], oxh[RX][kConv ? 3 : 1];
+        auto load_x = [&](int tt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < RX; ++k) {
+                const int u = tid + 256 * k;
+                const int tq = u % TQ;
+                const uint32_t col = hp0 + (uint32_t)(8 * ((u / TQ) % (PW / 8)) * ES);
+                const uint32_t vxo = oob_if(!ox_unit(k), (uint32_t)(4 * tq) * x_tok + col);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oxr[k][i] = Tr::load_frag_s(rx, vxo + i * x_tok, (uint32_t)tt * x_tok);
+                if constexpr (kConv) {
+                    const int row0 = tt + 4 * tq - 3;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+                        oxh[k][i] = Tr::load_frag(
+                            rx, oob_if(!ox_unit(k) || row0 + i < 0, (uint32_t)(row0 + i) * x_tok + col));
+                }
+            }
+        };
+        auto stage_x = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < RX; ++k)
+                if (ox_unit(k)) {
+                    const int u = tid + 256 * k;
+                    const int tq = u % TQ, po = (u / TQ) % (PW / 8);
+                    if constexpr (kConv) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int c = 8 * po + e;
+                            const f32x4 wv = *reinterpret_cast<const f32x4 *>(CWL + 4 * c);
+                            const float bv = CWL[4 * PW + c];
+                            float xv[7];  // tokens 4 tq - 3 .. 4 tq + 3 of this column
+#pragma unroll
+                            for (int i = 0; i < 3; ++i) xv[i] = Tr::frag_get(oxh[k][i], e);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) xv[3 + i] = Tr::frag_get(oxr[k][i], e);
+                            float yv[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = bv + wv[0] * xv[i] + wv[1] * xv[i + 1] + wv[2] * xv[i + 2] +
+                                                wv[3] * xv[i + 3];
+                                yv[i] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
+                            }
+                            lds_store4<TI>(XT + c * X_LD + slot * TT + 4 * tq, Tr::from_f32(yv[0]),
+                                           Tr::from_f32(yv[1]), Tr::from_f32(yv[2]), Tr::from_f32(yv[3]));
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            lds_store4<TI>(XT + (8 * po + e) * X_LD + slot * TT + 4 * tq, oxr[k][0][e],
+                                           oxr[k][1][e], oxr[k][2][e], oxr[k][3][e]);
+                    }
+                }
+        };
+        if constexpr (kXOut) {
+            const int tile_b = cb * NT;
+            load_x(tile_b * TT);
+            stage_x(tile_b & 1);
+            load_x(min(tile_b + 1, last_tile) * TT);
+        }
         load_c(cb * Q);
         __builtin_amdgcn_sched_barrier(0);
         load_g(cb * NT);
@@ -499,7 +586,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
             const int t0 = c * Q;
             const float *CSL = CSB + ((c - cb) & 1) * 2 * Q;  // cs2 of this chunk
             const float *CPL = CSL + Q;                       // cs' of this chunk
-            static_for<NT>([&](auto Ic) {
+            static_for<NT>([&](auto Ic) __attribute__((always_inline)) {
                 constexpr int I = decltype(Ic)::value;
                 const int tile0 = I * TT;  // chunk-local
                 const int tau = c * NT + I;
@@ -614,15 +701,22 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                         buf_st128s(d, ry, (uint32_t)rl * x_tok + (uint32_t)(cv * 16), sy);
                     }
                 }
+                // X of the next tile into the other slot, then the loads of the one after
+                if constexpr (kXOut) stage_x((tau + 1) & 1);
                 load_z(min(tau + 1, last_tile) * TT);
+                if constexpr (kXOut) load_x(min(tau + 2, last_tile) * TT);
                 __syncthreads();
             });
         }
     } else {
         // ===================== state waves =====================
         // staging units are wave-uniform whenever their count is a multiple of 64
-        auto x_unit = [&](int k) { return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (st + 256 * k < UX); };
-        auto b_unit = [&](int k) { return (UB % 64 == 0) ? (64 * w + 256 * k < UB) : (st + 256 * k < UB); };
+        auto x_unit = [&](int k) __attribute__((always_inline)) {
+            return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (st + 256 * k < UX);
+        };
+        auto b_unit = [&](int k) __attribute__((always_inline)) {
+            return (UB % 64 == 0) ? (64 * w + 256 * k < UB) : (st + 256 * k < UB);
+        };
         // Every lane issues every load, a lane without a unit at an
         // out-of-range offset (it reads zeros and moves no data), and tiles
         // past the end reload the last one: with no load under a branch, the
@@ -641,17 +735,27 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         }
         constexpr int kDepth = Cfg::kDepth;
         frag xr[kDepth][RX][4], br[kDepth][RB][4];
+        frag xh[kDepth][RX][kConv ? 3 : 1];  // the 3 tokens before each X unit (conv)
         f32x4 bcp[kDepth][RB];   // cs' of the B unit's 4 tokens
         float xce[kDepth] = {};  // cs2 of the tile's last token
         const rsrc_t rcs = make_rsrc(cs_row, (uint32_t)a.Tpad * 4u);
-        auto issue_stage = [&](int tt, auto Sc) {  // X, B and log-decays of the tile at token tt
+        auto issue_stage = [&](int tt, auto Sc) __attribute__((always_inline)) {  // X, B and log-decays of the tile at token tt
             constexpr int S = decltype(Sc)::value;
             const uint32_t sx = (uint32_t)tt * x_tok + hp0;
             const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
 #pragma unroll
-            for (int k = 0; k < RX; ++k) {
+            for (int k = 0; k < (kXOut ? 0 : RX); ++k) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xr[S][k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
+                if constexpr (kConv) {
+                    const int u = st + 256 * k;
+                    const int row0 = tt + 4 * (u % TQ) - 3;  // token of halo row 0
+                    const uint32_t col = hp0 + (uint32_t)(8 * ((u / TQ) % (PW / 8)) * ES);
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+                        xh[S][k][i] = Tr::load_frag(
+                            rx, oob_if(!x_unit(k) || row0 + i < 0, (uint32_t)(row0 + i) * x_tok + col));
+                }
             }
             // a vector load: a scalar one would hold up every LDS wait (both
             // count in lgkmcnt) until it returns
@@ -663,18 +767,42 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                 bcp[S][k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % TQ));
             }
         };
-        auto stage = [&](auto Sc, int slot) {  // into X slot `slot` and the matching B^T copy
+        auto stage = [&](auto Sc, int slot) __attribute__((always_inline)) {  // into X slot `slot` and the matching B^T copy
             constexpr int S = decltype(Sc)::value;
             TI *BT = BTB + (kBT2 ? slot : 0) * N * BT_LD;
+            // (when kXOut the output waves stage X)
 #pragma unroll
-            for (int k = 0; k < RX; ++k)
+            for (int k = 0; k < (kXOut ? 0 : RX); ++k)
                 if (x_unit(k)) {
                     const int u = st + 256 * k;
                     const int tq = u % TQ, po = (u / TQ) % (PW / 8);
+                    if constexpr (kConv) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        lds_store4<TI>(XT + (8 * po + e) * X_LD + slot * TT + 4 * tq, xr[S][k][0][e],
-                                       xr[S][k][1][e], xr[S][k][2][e], xr[S][k][3][e]);
+                        for (int e = 0; e < 8; ++e) {
+                            const int c = 8 * po + e;
+                            const f32x4 wv = *reinterpret_cast<const f32x4 *>(CWL + 4 * c);
+                            const float bv = CWL[4 * PW + c];
+                            float xv[7];  // tokens 4 tq - 3 .. 4 tq + 3 of this column
+#pragma unroll
+                            for (int i = 0; i < 3; ++i) xv[i] = Tr::frag_get(xh[S][k][i], e);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) xv[3 + i] = Tr::frag_get(xr[S][k][i], e);
+                            float yv[4];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float v = bv + wv[0] * xv[i] + wv[1] * xv[i + 1] + wv[2] * xv[i + 2] +
+                                                wv[3] * xv[i + 3];
+                                yv[i] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
+                            }
+                            lds_store4<TI>(XT + c * X_LD + slot * TT + 4 * tq, Tr::from_f32(yv[0]),
+                                           Tr::from_f32(yv[1]), Tr::from_f32(yv[2]), Tr::from_f32(yv[3]));
+                        }
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            lds_store4<TI>(XT + (8 * po + e) * X_LD + slot * TT + 4 * tq, xr[S][k][0][e],
+                                           xr[S][k][1][e], xr[S][k][2][e], xr[S][k][3][e]);
+                    }
                 }
 #pragma unroll
             for (int k = 0; k < RB; ++k)
@@ -696,7 +824,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         };
         // transposed state: hacc[pb][j][i] = h[p = 16pb + r][n = 16(w + 4j) + 4kg + i]
         f32x4 hacc[PB][NBW];
-        auto write_hs = [&](TI *HSw) {
+        auto write_hs = [&](TI *HSw) __attribute__((always_inline)) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
@@ -728,7 +856,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         for (int c = cb; c < ce; ++c) {
             const int t0 = c * Q;
             const float *CSL = CSB + ((c - cb) & 1) * 2 * Q;  // cs2 of this chunk
-            static_for<NT>([&](auto Ic) {
+            static_for<NT>([&](auto Ic) __attribute__((always_inline)) {
                 constexpr int I = decltype(Ic)::value;
                 const int tile0 = I * TT;
                 const int tau = c * NT + I;
@@ -804,7 +932,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
 // place: slot s ends up holding the state entering segment s + 1. One thread
 // per 4 state elements.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_seg_scan(float *__restrict__ seg, const float *__restrict__ cs2,
+static __global__ __launch_bounds__(256) void k_seg_scan(float *__restrict__ seg, const float *__restrict__ cs2,
                                                   int64_t bh_count, int PN, int S, int cps, int nC, int Q,
                                                   int Tpad) {
     const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // f32x4 index
@@ -828,12 +956,12 @@ __global__ __launch_bounds__(256) void k_seg_scan(float *__restrict__ seg, const
 // ---------------------------------------------------------------------------
 // host side: the plan (column slices, tile size) and the launches
 // ---------------------------------------------------------------------------
-template <typename TI, int Q, int PW, int N, int TT>
+template <typename TI, int Q, int PW, int N, int TT, bool kConv = false>
 static constexpr bool fits() {
     if constexpr (Q % TT != 0) {
         return false;
     } else {
-        return WalkCfg<TI, Q, PW, N, TT>::kFits;
+        return WalkCfg<TI, Q, PW, N, TT, kConv>::kFits;
     }
 }
 
@@ -886,6 +1014,7 @@ static int tile_q(int64_t Q, int64_t PW, int64_t N) {
 // stage the whole B tile and build the whole masked C B^T block.
 constexpr int kCUs = 256;
 
+#ifndef SSD_CONV_TU
 int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64_t Q, int64_t nC,
              bool segments, WalkPlan *plan) {
     const int64_t walks = batch * H;
@@ -909,6 +1038,8 @@ int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64
     return 0;
 }
 
+#endif  // SSD_CONV_TU
+
 template <typename TI, int Q, int N, int TT>
 static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
     PrepArgs a;
@@ -929,9 +1060,9 @@ static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
 // A split sequence (S > 1) takes three launches: the state-only walk of
 // segments 0..S-2, the scan of their end states, the full walk of all S
 // segments each from its entering state.
-template <typename TI, int Q, int PW, int N, int TT>
-static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
-    if constexpr (!fits<TI, Q, PW, N, TT>()) {
+template <typename TI, int Q, int PW, int N, int TT, bool kConv>
+static ssd_status run_walk_c(const FwdArgs &f, hipStream_t s) {
+    if constexpr (!fits<TI, Q, PW, N, TT, kConv>()) {
         return SSD_ERR_UNSUPPORTED;
     } else {
         WalkArgs wa;
@@ -941,11 +1072,12 @@ static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
         wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
         wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg;
         wa.cu = f.cu; wa.total = (int)f.total; wa.z = f.z;
+        wa.conv_w = f.conv_w; wa.conv_b = f.conv_b;
         const int64_t heads = f.batch * f.H * f.ns;
         if (f.S > 1) {
             wa.SL = f.S - 1;
-            if (launch(k_chunk_walk<TI, Q, PW, N, TT, true>, dim3((unsigned)(heads * wa.SL)), dim3(256), s, wa) !=
-                hipSuccess)
+            if (launch(k_chunk_walk<TI, Q, PW, N, TT, true, kConv>, dim3((unsigned)(heads * wa.SL)), dim3(256), s,
+                       wa) != hipSuccess)
                 return SSD_ERR_HIP;
             const int64_t n4 = f.batch * f.H * f.P * f.N / 4;
             if (f.S > 2 && launch(k_seg_scan, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, f.seg,
@@ -954,43 +1086,61 @@ static ssd_status run_walk(const FwdArgs &f, hipStream_t s) {
                 return SSD_ERR_HIP;
         }
         wa.SL = f.S;
-        return launch(k_chunk_walk<TI, Q, PW, N, TT, false>, dim3((unsigned)(heads * f.S)), dim3(512), s, wa) ==
-                       hipSuccess
+        return launch(k_chunk_walk<TI, Q, PW, N, TT, false, kConv>, dim3((unsigned)(heads * f.S)), dim3(512), s,
+                      wa) == hipSuccess
                    ? SSD_OK
                    : SSD_ERR_HIP;
     }
 }
 
-template <typename TI, int Q, int PW, int N>
+template <typename TI, int Q, int PW, int N, bool kConv>
 static ssd_status walk_t(const FwdArgs &f, hipStream_t s) {
     switch (f.tt) {
-        case 64: return run_walk<TI, Q, PW, N, 64>(f, s);
+        case 64: return run_walk_c<TI, Q, PW, N, 64, kConv>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
-template <typename TI, int Q, int PW>
+template <typename TI, int Q, int PW, bool kConv>
 static ssd_status walk_n(const FwdArgs &f, hipStream_t s) {
     switch (f.N) {
-        case 16: return walk_t<TI, Q, PW, 16>(f, s);
-        case 32: return walk_t<TI, Q, PW, 32>(f, s);
-        case 64: return walk_t<TI, Q, PW, 64>(f, s);
-        case 128: return walk_t<TI, Q, PW, 128>(f, s);
-        case 256: return walk_t<TI, Q, PW, 256>(f, s);
+        case 16: return walk_t<TI, Q, PW, 16, kConv>(f, s);
+        case 32: return walk_t<TI, Q, PW, 32, kConv>(f, s);
+        case 64: return walk_t<TI, Q, PW, 64, kConv>(f, s);
+        case 128: return walk_t<TI, Q, PW, 128, kConv>(f, s);
+        case 256: return walk_t<TI, Q, PW, 256, kConv>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
-template <typename TI, int Q>
+template <typename TI, int Q, bool kConv>
 static ssd_status walk_p(const FwdArgs &f, hipStream_t s) {
     switch (f.P / f.ns) {
-        case 16: return walk_n<TI, Q, 16>(f, s);
-        case 32: return walk_n<TI, Q, 32>(f, s);
-        case 64: return walk_n<TI, Q, 64>(f, s);
-        case 128: return walk_n<TI, Q, 128>(f, s);
+        case 16: return walk_n<TI, Q, 16, kConv>(f, s);
+        case 32: return walk_n<TI, Q, 32, kConv>(f, s);
+        case 64: return walk_n<TI, Q, 64, kConv>(f, s);
+        case 128: return walk_n<TI, Q, 128, kConv>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
+
+template <typename TI, bool kConv>
+static ssd_status walk_q(const FwdArgs &f, hipStream_t s) {
+    switch (f.Q) {
+        case 64: return walk_p<TI, 64, kConv>(f, s);
+        case 128: return walk_p<TI, 128, kConv>(f, s);
+        case 256: return walk_p<TI, 256, kConv>(f, s);
+        default: return SSD_ERR_UNSUPPORTED;
+    }
+}
+
+#ifdef SSD_CONV_TU
+// This translation unit (ssd_walk_conv.hip) holds only the walks with the
+// fused input convolution, so that they compile in parallel with the rest.
+ssd_status launch_walk_conv(const FwdArgs &f, hipStream_t s) {
+    return f.dtype == SSD_BF16 ? walk_q<bf16, true>(f, s) : walk_q<float, true>(f, s);
+}
+#else
 
 template <typename TI, int Q, int N>
 static ssd_status prepare_t(const FwdArgs &f, hipStream_t s) {
@@ -1012,22 +1162,60 @@ static ssd_status prepare_n(const FwdArgs &f, hipStream_t s) {
     }
 }
 
-template <typename TI, bool kWalk>
-static ssd_status dispatch_q(const FwdArgs &f, hipStream_t s) {
+template <typename TI>
+static ssd_status prepare_q(const FwdArgs &f, hipStream_t s) {
     switch (f.Q) {
-        case 64: return kWalk ? walk_p<TI, 64>(f, s) : prepare_n<TI, 64>(f, s);
-        case 128: return kWalk ? walk_p<TI, 128>(f, s) : prepare_n<TI, 128>(f, s);
-        case 256: return kWalk ? walk_p<TI, 256>(f, s) : prepare_n<TI, 256>(f, s);
+        case 64: return prepare_n<TI, 64>(f, s);
+        case 128: return prepare_n<TI, 128>(f, s);
+        case 256: return prepare_n<TI, 256>(f, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }
 
+template <typename TI, int Q, int PW>
+static bool conv_fits_n(int64_t N) {
+    switch (N) {
+        case 16: return fits<TI, Q, PW, 16, 64, true>();
+        case 32: return fits<TI, Q, PW, 32, 64, true>();
+        case 64: return fits<TI, Q, PW, 64, 64, true>();
+        case 128: return fits<TI, Q, PW, 128, 64, true>();
+        case 256: return fits<TI, Q, PW, 256, 64, true>();
+        default: return false;
+    }
+}
+
+template <typename TI, int Q>
+static bool conv_fits_q(int64_t PW, int64_t N) {
+    switch (PW) {
+        case 16: return conv_fits_n<TI, Q, 16>(N);
+        case 32: return conv_fits_n<TI, Q, 32>(N);
+        case 64: return conv_fits_n<TI, Q, 64>(N);
+        case 128: return conv_fits_n<TI, Q, 128>(N);
+        default: return false;
+    }
+}
+
+bool walk_conv_fits(ssd_dtype dt, int64_t Q, int64_t PW, int64_t N) {
+    auto q = [&](auto T0) -> bool {
+        using TI = decltype(T0);
+        switch (Q) {
+            case 64: return conv_fits_q<TI, 64>(PW, N);
+            case 128: return conv_fits_q<TI, 128>(PW, N);
+            case 256: return conv_fits_q<TI, 256>(PW, N);
+            default: return false;
+        }
+    };
+    return dt == SSD_BF16 ? q(bf16{}) : q(float{});
+}
+
 ssd_status launch_prepare(const FwdArgs &f, hipStream_t s) {
-    return f.dtype == SSD_BF16 ? dispatch_q<bf16, false>(f, s) : dispatch_q<float, false>(f, s);
+    return f.dtype == SSD_BF16 ? prepare_q<bf16>(f, s) : prepare_q<float>(f, s);
 }
 
 ssd_status launch_walk(const FwdArgs &f, hipStream_t s) {
-    return f.dtype == SSD_BF16 ? dispatch_q<bf16, true>(f, s) : dispatch_q<float, true>(f, s);
+    if (f.conv_w) return launch_walk_conv(f, s);
+    return f.dtype == SSD_BF16 ? walk_q<bf16, false>(f, s) : walk_q<float, false>(f, s);
 }
+#endif  // SSD_CONV_TU
 
 }  // namespace ssd

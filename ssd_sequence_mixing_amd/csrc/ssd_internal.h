@@ -21,6 +21,8 @@ struct FwdArgs {
     const float *dt_bias;      // fused prologue: dt = [softplus](dt + dt_bias[h]); null = no bias
     int softplus;
     const void *z;             // fused epilogue: Y *= silu(z), z shaped like X; null = no gate
+    const float *conv_w;       // fused input activation: X <- silu(causal conv of X), taps (H P, 4); null = none
+    const float *conv_b;       // its bias (H P), or null (zero)
     ssd_dtype dtype;
     float *cs2, *dtf;          // workspace: (batch, H, Tpad) each
     void *Gbuf;                // workspace: (batch, G, Tpad / tt, tt, tt) in the storage type
@@ -69,6 +71,7 @@ struct WalkArgs {
     const int *cu;             // see FwdArgs
     int total;
     const void *z;             // see FwdArgs
+    const float *conv_w, *conv_b;  // see FwdArgs
     uint32_t g_bytes;
 };
 
@@ -135,8 +138,12 @@ ssd_status launch_bwd(const BwdArgs &w, hipStream_t s);
 
 // Phase 1: chunk-local log-decay prefix sums and C B^T tiles into the workspace.
 ssd_status launch_prepare(const FwdArgs &f, hipStream_t s);
+// Whether the walk with the fused input convolution fits LDS for a column slice.
+bool walk_conv_fits(ssd_dtype dt, int64_t Q, int64_t PW, int64_t N);
 // Phase 2: the chunk walk (reads the prepared workspace).
 ssd_status launch_walk(const FwdArgs &f, hipStream_t s);
+// The walk with the fused input convolution (f.conv_w set; ssd_walk_conv.hip).
+ssd_status launch_walk_conv(const FwdArgs &f, hipStream_t s);
 // One recurrent decode step.
 ssd_status launch_step(const StepArgs &a, hipStream_t s);
 

@@ -278,3 +278,19 @@ def test_bwd_workspace_and_empty():
     assert bwd(wsb=1000) == EWS
     assert bwd(wsp=P16 + 16) == EALIGN
     assert bwd(batch=0, wsp=None, wsb=0) == OK
+
+
+def fused(X=P16, cw=P16, cb=P16, dt=P16, bias=None, mode=0, A=P16, B=P16, C=P16, D=P16, z=None, chunk=256,
+          Y=P16, fin=P16, batch=4, T=2048, H=64, P=64, N=128, G=1, dtype=BF16, wsp=P16 * 16, wsb=1 << 40):
+    return ssd.raw_call("ssd_chunk_scan_fwd_fused", X, cw, cb, dt, bias, mode, A, B, C, D, z, chunk, Y, fin,
+                        batch, T, H, P, N, G, dtype, wsp, wsb, None)
+
+
+def test_fused_argument_checks():
+    assert fused(cw=None) == ENULL            # a bias without taps
+    assert fused(cw=P16 + 4) == EALIGN
+    assert fused(cb=P16 + 2) == EALIGN
+    assert fused(mode=3) == EUNSUP
+    assert fused(X=None) == ENULL
+    assert fused(wsp=None) == EWS
+    assert fused(batch=0, wsp=None, wsb=0) == OK

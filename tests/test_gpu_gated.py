@@ -145,3 +145,86 @@ def test_gated_step(ssd, dtype, mode):
     log(f"[gated step] {dtype} mode={mode}: y {rel(to_np(y), y_ref):.2e} state "
         f"{rel(st.cpu().numpy(), s_ref):.2e}")
     assert rel(to_np(y), y_ref) <= tol and rel(st.cpu().numpy(), s_ref) <= tol
+
+
+def conv_inputs(cfg, seed):
+    """Taps ~ N(0, 0.5^2) per channel and bias ~ N(0, 0.1^2): the conv keeps the
+    workload's input scale."""
+    rng = np.random.default_rng(seed)
+    C = cfg.nheads * cfg.headdim
+    w = (0.5 * rng.standard_normal((C, 4))).astype(np.float32)
+    b = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    return w, b
+
+
+def oracle_conv_x(X32, w, b):
+    """oracle.conv_silu over the channels c = h * P + p."""
+    Bz, T, H, P = X32.shape
+    return oracle.conv_silu(X32.reshape(Bz, T, H * P), w, b).reshape(Bz, T, H, P)
+
+
+@pytest.mark.parametrize("dtype,chunk,with_bias,gated", [
+    ("bf16", 128, True, True), ("bf16", 64, False, False), ("f32", 64, True, False),
+])
+def test_fused_conv_forward(ssd, dtype, chunk, with_bias, gated):
+    import torch
+    base = si.CONFIGS["l1p3b_bf16"] if dtype == "bf16" else si.CONFIGS["tiny_f32"]
+    cfg = dataclasses.replace(base, name="conv", batch=2, seqlen=333, nheads=4,
+                              headdim=64 if dtype == "bf16" else 32, dstate=128 if dtype == "bf16" else 32,
+                              ngroups=2, seed=76)
+    inp = raw_inputs(cfg, 77)
+    w, b = conv_inputs(cfg, 78)
+    mode = 1 if gated else 0
+    if not gated:
+        inp["dtraw"], inp["dtraw32"] = inp["dt"], inp["dt32"]
+    log(f"[conv] {dtype} chunk={chunk} bias={with_bias} gated={gated}")
+    Xc = oracle_conv_x(inp["X32"], w, b if with_bias else np.zeros_like(b))
+    tol = TOL[dtype]
+    errs = []
+    for D_zero in (False, True):
+        Dv = np.zeros_like(inp["D"]) if D_zero else inp["D"]
+        dt = oracle.dt_prologue(inp["dtraw32"], inp["bias"] if gated else None, mode)
+        Yr, Fr, _ = oracle.fwd(Xc, dt, inp["A"], inp["B32"], inp["C32"], Dv, cfg.ngroups)
+        if gated and not D_zero:
+            Yr = oracle.gate(Yr, inp["z32"])
+        Y, F = ssd.ssd_chunk_scan_fwd_fused(
+            to_dev(inp["X"]), to_dev(inp["dtraw"]), to_dev(inp["A"]), to_dev(inp["B"]), to_dev(inp["C"]),
+            to_dev(Dv), chunk, conv_w=to_dev(w), conv_b=to_dev(b) if with_bias else None,
+            dt_bias=to_dev(inp["bias"]) if gated else None, dt_softplus=mode,
+            z=to_dev(inp["z"]) if (gated and not D_zero) else None)
+        torch.cuda.synchronize()
+        errs += [rel(to_np(Y), Yr), rel(F.cpu().numpy(), Fr)]
+    log(f"    rel err Y={errs[0]:.2e} final={errs[1]:.2e} Y(D=0, no gate)={errs[2]:.2e}")
+    assert all(np.isfinite(e) and e <= tol for e in errs), errs
+
+
+def test_fused_conv_split_sequence(ssd):
+    """Few heads and a long sequence: the walk splits it into segments, whose
+    state-only pass applies the convolution too (tokens before each segment
+    come from the previous one)."""
+    import torch
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="conv_seg", batch=1, seqlen=2048, nheads=2,
+                              headdim=32, dstate=64, ngroups=1, seed=79)
+    inp = si.make_fwd_inputs(cfg)
+    w, b = conv_inputs(cfg, 80)
+    Xc = oracle_conv_x(inp["X32"], w, b)
+    Yr, Fr, _ = oracle.fwd(Xc, inp["dt32"], inp["A"], inp["B32"], inp["C32"], inp["D"], 1)
+    log("[conv] split sequence")
+    Y, F = ssd.ssd_chunk_scan_fwd_fused(to_dev(inp["X"]), to_dev(inp["dt"]), to_dev(inp["A"]), to_dev(inp["B"]),
+                                        to_dev(inp["C"]), to_dev(inp["D"]), 64, conv_w=to_dev(w), conv_b=to_dev(b))
+    torch.cuda.synchronize()
+    e = (rel(to_np(Y), Yr), rel(F.cpu().numpy(), Fr))
+    log(f"    rel err Y={e[0]:.2e} final={e[1]:.2e}")
+    assert e[0] <= TOL["bf16"] and e[1] <= TOL["bf16"], e
+
+
+def test_fused_without_conv_is_the_gated_forward(ssd):
+    import torch
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="fused_id", batch=1, seqlen=200, nheads=4, seed=81)
+    inp = raw_inputs(cfg, 82)
+    args = [to_dev(inp[k]) for k in ("X", "dtraw", "A", "B", "C", "D")]
+    kw = dict(dt_bias=to_dev(inp["bias"]), dt_softplus=1, z=to_dev(inp["z"]))
+    Y1, F1 = ssd.ssd_chunk_scan_fwd_gated(*args, 256, **kw)
+    Y2, F2 = ssd.ssd_chunk_scan_fwd_fused(*args, 256, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(F1, F2)
