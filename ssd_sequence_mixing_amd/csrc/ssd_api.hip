@@ -121,7 +121,7 @@ ssd_status empty_final_state(float *final_state, const float *init, int64_t n, h
 struct BwdLayout {
     FwdLayout fl;
     int nblk;
-    int64_t ntiles, st_bytes, lamb_bytes, tok_bytes, part_bytes, total;
+    int64_t ntiles, st_bytes, lamb_bytes, share_bytes, tok_bytes, part_bytes, total;
 };
 
 // Head blocks per group: the fewest (a divisor of the group's head count)
@@ -144,12 +144,14 @@ ssd_status check_bwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     lay->nblk = bwd_blocks(batch, lay->ntiles, ngroups, nheads / ngroups);
     lay->st_bytes = align256(batch * nheads * lay->ntiles * headdim * dstate * es);
     lay->lamb_bytes = align256(batch * nheads * lay->ntiles * 4);
+    lay->share_bytes = align256(batch * nheads * lay->ntiles * 8 * 4);  // Lambda shares, 8 per tile
     lay->tok_bytes = align256(batch * nheads * Tpad * 4);
     lay->part_bytes = align256(batch * Tpad * lay->nblk * ngroups * dstate * 4);
     const int64_t fwd = 2 * lay->fl.cs_bytes + lay->fl.g_bytes + lay->fl.seg_bytes;
     lay->total = (batch == 0 || seqlen == 0)
                      ? 0
-                     : fwd + 2 * lay->st_bytes + 3 * lay->lamb_bytes + 3 * lay->tok_bytes + 2 * lay->part_bytes;
+                     : fwd + 2 * lay->st_bytes + lay->share_bytes + 2 * lay->lamb_bytes + 3 * lay->tok_bytes +
+                           2 * lay->part_bytes;
     return SSD_OK;
 }
 
@@ -404,7 +406,7 @@ ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, con
     char *ws = static_cast<char *>(workspace) + 2 * lay.fl.cs_bytes + lay.fl.g_bytes + lay.fl.seg_bytes;
     w.Hst = ws; ws += lay.st_bytes;
     w.Est = ws; ws += lay.st_bytes;
-    w.lamb = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
+    w.lamb = reinterpret_cast<float *>(ws); ws += lay.share_bytes;
     w.dApart = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
     w.dDpart = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
     w.rbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;

@@ -354,14 +354,8 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
                 }
 #pragma unroll
             for (int m = 32; m > 0; m >>= 1) part += __shfl_xor(part, m);
-            if (lane == 0) WT[w] = part;  // WT is free until the next tile's weights
-            __syncthreads();
-            if (tid == 0) {
-                float sum = 0.f;
-#pragma unroll
-                for (int q = 0; q < NW; ++q) sum += WT[q];
-                a.lamb[(size_t)bh * ntiles + tau] = sum;
-            }
+            // one share per wavefront, added up by k_bwd_fin in a fixed order
+            if (lane == 0) a.lamb[((size_t)bh * ntiles + tau) * NW + w] = part;
         }
         __syncthreads();
     };
@@ -801,7 +795,10 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdFinArgs a) {
         const float v = __shfl_down(run, m);
         if (lane + m < 64) run += v;
     }
-    run += a.lamb[wid];
+    {
+        const float *lp = a.lamb + wid * 8;  // the state pass's 8 wavefront shares
+        run += ((lp[0] + lp[1]) + (lp[2] + lp[3])) + ((lp[4] + lp[5]) + (lp[6] + lp[7]));
+    }
     float sdA = 0.f, sdD = 0.f;
     if (real) {
         reinterpret_cast<TI *>(a.ddt)[od] = Traits<TI>::from_f32(a.rbuf[o] + a.A[h] * run);

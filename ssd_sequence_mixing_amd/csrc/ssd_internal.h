@@ -95,7 +95,8 @@ struct StatePassArgs {          // k_state_pass
     void *Sst;                  // (batch, H, ntiles, P, N) storage type: the state entering each tile
     float *out;                 // state after the last tile walked (fp32), or null
     const void *Est;            // forward pass: the adjoints arriving at each tile (storage type)
-    float *lamb;                // forward pass: (batch, H, ntiles) <E_tile, state after the tile>
+    float *lamb;                // forward pass: (batch, H, ntiles, 8) per-wavefront shares of
+                                // <E_tile, state after the tile>
     int H, G, T, Tpad, ntiles, tpc;  // tpc: 64-token tiles per chunk
 };
 

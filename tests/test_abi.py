@@ -242,12 +242,13 @@ def test_bwd_workspace_query():
     fwd = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
     st = 4 * 64 * 32 * 64 * 128 * 2            # states per 64-token tile, bf16
     lamb = 4 * 64 * 32 * 4
+    shares = 8 * lamb
     tok = 4 * 64 * 2048 * 4
     nblk = 1                                    # 4 x 32 tiles x 1 group x 4 blocks = 512 work-groups
     while 4 * 32 * nblk < 512:
         nblk *= 2
     part = 4 * 2048 * nblk * 128 * 4
-    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == fwd + 2 * st + 3 * lamb + 3 * tok + 2 * part
+    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == fwd + 2 * st + shares + 2 * lamb + 3 * tok + 2 * part
     assert q(4, 2048, 64, 64, 256, 1, 256, BF16) == ctypes.c_size_t(-1).value   # N 256: not covered
     assert q(4, 2048, 64, 128, 64, 1, 256, BF16) == ctypes.c_size_t(-1).value   # P 128: not covered
     assert q(4, 2048, 64, 64, 128, 1, 256, F32) == ctypes.c_size_t(-1).value
