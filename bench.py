@@ -95,26 +95,27 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(inp, cfg, budget_s=10.0):
+def cpu_baseline(inp, cfg, budget_s=10.0, max_passes=200):
+    """Oracle throughput on this host: whole batch elements of the workload, one
+    at a time, repeated over the batch until about budget_s of wall time."""
     import numpy as np
 
     import oracle
+    per_b = [[np.ascontiguousarray(inp[k][b:b + 1], dtype=np.float64) for k in ("X32", "dt32", "B32", "C32")]
+             for b in range(cfg.batch)]
     done_tokens, elapsed, used = 0, 0.0, 0
-    for b in range(cfg.batch):
-        sl = slice(b, b + 1)
-        args = [np.ascontiguousarray(inp[k][sl], dtype=np.float64) for k in ("X32", "dt32", "B32", "C32")]
+    while elapsed < budget_s and used < max_passes * cfg.batch:
+        args = per_b[used % cfg.batch]
         t0 = time.perf_counter()
         oracle.fwd(args[0], args[1], inp["A"], args[2], args[3], inp["D"], cfg.ngroups)
         elapsed += time.perf_counter() - t0
         done_tokens += cfg.seqlen
         used += 1
-        if elapsed >= budget_s:
-            break
     return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{used} of {cfg.batch} batch elements of the same workload "
-                      f"({done_tokens} tokens x {cfg.nheads} heads), fp64 sequential recurrence, "
-                      f"{elapsed:.2f} s wall"}
+            "sample": f"{used} single-sequence forwards cycling over the {cfg.batch} batch elements of the "
+                      f"same workload ({done_tokens} tokens x {cfg.nheads} heads), fp64 sequential "
+                      f"recurrence, {elapsed:.2f} s wall"}
 
 
 def main():
