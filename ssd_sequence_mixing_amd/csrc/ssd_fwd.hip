@@ -148,7 +148,8 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
 
 // ---------------------------------------------------------------------------
 // tile_cb: G[b, g, tile] = C_tile B_tile^T (TT x TT, row = query token i,
-// column = key token j) for one band of 64 rows of one tile per work-group,
+// column = key token j), with the entries j > i stored as zero (the causal
+// mask of the diagonal block), for one band of 64 rows of one tile per work-group,
 // wave w owning rows 16w..16w+15 of the band. Only the column blocks the walk
 // reads (up to the band's diagonal) are formed. The product is formed
 // transposed (B rows as the A operand) so that each lane holds four
@@ -211,6 +212,10 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
             for (int cb = 0; cb < 4; ++cb) acc[cb] = Tr::mma(bk[cb][kk], cq[kk], acc[cb]);
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
+            // causal mask: entries above the diagonal (key after query) are stored as 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (64 * cgp + 16 * cb + 4 * kg + i > row) acc[cb][i] = 0.f;
             const uint32_t off = (uint32_t)((tile + row * TT + 64 * cgp + 16 * cb + 4 * kg) * ES);
             if constexpr (ES == 2) {
                 const bf16x4 v = {(bf16)acc[cb][0], (bf16)acc[cb][1], (bf16)acc[cb][2], (bf16)acc[cb][3]};
@@ -264,6 +269,12 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
 // four consecutive n of one row p: the LDS copy and the final state are
 // written four elements at a time.
 // ---------------------------------------------------------------------------
+// Largest decay over one tile, in base-2 log units (cs2 before the tile minus
+// cs2 at its last token), for which the walk factors the diagonal block's
+// weights: the weighted X is then at most dt x 2^64, far inside the fp32 and
+// bf16 range. Tiles that decay faster take the per-element weights.
+constexpr float kFDMax = 64.f;
+
 template <typename TI, int Q, int PW, int N, int TT, bool kConv = false>
 struct WalkCfg {
     static constexpr int ES = Traits<TI>::kBytes;
@@ -288,7 +299,11 @@ struct WalkCfg {
     static constexpr bool kHSReg = PB * NK * ES <= 32;  // state fragments held in registers
     static constexpr int XT_OFF = 0;
     static constexpr int X_BYTES = PW * X_LD * ES;
-    static constexpr int YS_OFF = XT_OFF + X_BYTES;
+    // walks without the input convolution keep a second, weighted X copy
+    // (two slots, the layout of X) for the factored diagonal block
+    static constexpr bool kXW = !kConv;
+    static constexpr int XW_OFF = XT_OFF + X_BYTES;
+    static constexpr int YS_OFF = XW_OFF + (kXW ? X_BYTES : 0);
     static constexpr int YS_BYTES = TT * YS_LD * ES;
     static constexpr int CS_OFF = YS_OFF + YS_BYTES;  // 2 x (cs2[Q], cs'[Q]) fp32
     static constexpr int CS_BYTES = 2 * 2 * Q * 4;
@@ -363,6 +378,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     constexpr bool kHSReg = Cfg::kHSReg, kBT2 = Cfg::kBT2, kHS2 = Cfg::kHS2, kMidSync = Cfg::kMidSync;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
     TI *XT = reinterpret_cast<TI *>(smem + Cfg::XT_OFF);  // [p][slot*TT + token]
+    TI *XW = reinterpret_cast<TI *>(smem + Cfg::XW_OFF);  // weighted X, same layout (kFD)
     TI *YS = reinterpret_cast<TI *>(smem + Cfg::YS_OFF);
     float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);  // [buf][cs2 Q | cs' Q]
     TI *HSB = reinterpret_cast<TI *>(smem + Cfg::HS_OFF);        // [copy][p][n]
@@ -400,9 +416,9 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     float *out_mat = kStateOnly ? a.seg + (bhs * (S - 1) + seg) * P * N
                                 : ((seg == S - 1 && a.final_state) ? a.final_state + bhs * P * N : nullptr);
 
-    // which role stages X: the output waves in the full walk without the
-    // input convolution, else the state waves
-    constexpr bool kXOut = !kStateOnly && !kConv;
+    // factored diagonal block and state update (see kFDMax): the state waves
+    // also stage a weighted X copy and stage B^T unweighted
+    constexpr bool kFD = !kStateOnly && !kConv && Cfg::kXW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
     const bool out_wave = !kStateOnly && wv < 4;
@@ -507,74 +523,6 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                 for (int k = 0; k < NZ; ++k) zq[j][k] = buf_ld128s(rz, vz[k], sz);
             }
         };
-        // With kXOut, X of the tile after this one is staged by the output
-        // waves (the state waves, which carry the recurrence, are the busier
-        // role): units of 4 tokens x 8 columns, loaded a tile ahead of their
-        // staging. (With the input convolution the state waves keep it: its
-        // arithmetic made the output waves the slower role.)
-        auto ox_unit = [&](int k) __attribute__((always_inline)) {
-            return (UX % 64 == 0) ? (64 * w + 256 * k < UX) : (tid + 256 * k < UX);
-        };
-        frag oxr[RX][4], oxh[RX][kConv ? 3 : 1];
-        auto load_x = [&](int tt) __attribute__((always_inline)) {
-#pragma unroll
-            for (int k = 0; k < RX; ++k) {
-                const int u = tid + 256 * k;
-                const int tq = u % TQ;
-                const uint32_t col = hp0 + (uint32_t)(8 * ((u / TQ) % (PW / 8)) * ES);
-                const uint32_t vxo = oob_if(!ox_unit(k), (uint32_t)(4 * tq) * x_tok + col);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) oxr[k][i] = Tr::load_frag_s(rx, vxo + i * x_tok, (uint32_t)tt * x_tok);
-                if constexpr (kConv) {
-                    const int row0 = tt + 4 * tq - 3;
-#pragma unroll
-                    for (int i = 0; i < 3; ++i)
-                        oxh[k][i] = Tr::load_frag(
-                            rx, oob_if(!ox_unit(k) || row0 + i < 0, (uint32_t)(row0 + i) * x_tok + col));
-                }
-            }
-        };
-        auto stage_x = [&](int slot) __attribute__((always_inline)) {
-#pragma unroll
-            for (int k = 0; k < RX; ++k)
-                if (ox_unit(k)) {
-                    const int u = tid + 256 * k;
-                    const int tq = u % TQ, po = (u / TQ) % (PW / 8);
-                    if constexpr (kConv) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int c = 8 * po + e;
-                            const f32x4 wv = *reinterpret_cast<const f32x4 *>(CWL + 4 * c);
-                            const float bv = CWL[4 * PW + c];
-                            float xv[7];  // tokens 4 tq - 3 .. 4 tq + 3 of this column
-#pragma unroll
-                            for (int i = 0; i < 3; ++i) xv[i] = Tr::frag_get(oxh[k][i], e);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) xv[3 + i] = Tr::frag_get(oxr[k][i], e);
-                            float yv[4];
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const float v = bv + wv[0] * xv[i] + wv[1] * xv[i + 1] + wv[2] * xv[i + 2] +
-                                                wv[3] * xv[i + 3];
-                                yv[i] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
-                            }
-                            lds_store4<TI>(XT + c * X_LD + slot * TT + 4 * tq, Tr::from_f32(yv[0]),
-                                           Tr::from_f32(yv[1]), Tr::from_f32(yv[2]), Tr::from_f32(yv[3]));
-                        }
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            lds_store4<TI>(XT + (8 * po + e) * X_LD + slot * TT + 4 * tq, oxr[k][0][e],
-                                           oxr[k][1][e], oxr[k][2][e], oxr[k][3][e]);
-                    }
-                }
-        };
-        if constexpr (kXOut) {
-            const int tile_b = cb * NT;
-            load_x(tile_b * TT);
-            stage_x(tile_b & 1);
-            load_x(min(tile_b + 1, last_tile) * TT);
-        }
         load_c(cb * Q);
         __builtin_amdgcn_sched_barrier(0);
         load_g(cb * NT);
@@ -624,37 +572,64 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                 // from here on
                 if constexpr (kMidSync) __syncthreads();
                 load_c(min(tau + 1, last_tile) * TT);  // past the end: a harmless reload
+                // Diagonal block. Factored tiles split the weight 2^(cs_i - cs'_j) as
+                // 2^(cs_i - cs_ref) 2^(cs_ref - cs'_j): the second factor is on the
+                // weighted X copy, the first on the whole row after the block (state
+                // term included), the mask is already in C B^T, so C B^T goes into the
+                // matrix cores as loaded. Other tiles weight C B^T per element and
+                // scale the state term before the block. The matrix-core ops and both
+                // scalings run on every path (one scaling by 1): only the per-element
+                // weighting, which reads no accumulator, sits under the branch.
+                const bool fd = kFD && (cs_ref - CSL[tile0 + TT - 1] <= kFDMax);
+                float fr[NTT][4];
 #pragma unroll
-                for (int j = 0; j < NTT; ++j) {
-                    const int rows0 = tile0 + 16 * rbk[j];
+                for (int j = 0; j < NTT; ++j)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const float f = fast_exp2(CSL[rows0 + 4 * kg + i] - cs_ref);
+                        fr[j][i] = fast_exp2(CSL[tile0 + 16 * rbk[j] + 4 * kg + i] - cs_ref);
 #pragma unroll
-                        for (int pb = 0; pb < PB; ++pb) acc[j][pb][i] *= f;
+                        for (int pb = 0; pb < PB; ++pb) acc[j][pb][i] *= fd ? 1.f : fr[j][i];
                     }
-                    // diagonal block: weight exp2(cs_i - cs'_j) per element, j > i selected to zero
-                    const int irow = rows0 + r;  // chunk-local token of this lane's A row
-                    const float cs_i = CSL[irow];
+                if (!fd) {
+#pragma unroll
+                    for (int j = 0; j < NTT; ++j) {
+                        const int irow = tile0 + 16 * rbk[j] + r;  // chunk-local token of this lane's A row
+                        const float cs_i = CSL[irow];
+#pragma unroll
+                        for (int k2 = 0; k2 < KB; ++k2) {
+                            if (32 * k2 > 16 * rbk[j] + 15) continue;  // wave-uniform: above the diagonal
+                            const int j0 = tile0 + 32 * k2 + 8 * kg;
+                            const f32x4 cpa = *reinterpret_cast<const f32x4 *>(CPL + j0);
+                            const f32x4 cpb = *reinterpret_cast<const f32x4 *>(CPL + j0 + 4);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float cpj = e < 4 ? cpa[e] : cpb[e - 4];
+                                const float v = Tr::frag_get(gd[j][k2], e) * fast_exp2(cs_i - cpj);
+                                Tr::frag_set(gd[j][k2], e, (j0 + e <= irow) ? v : 0.f);
+                            }
+                        }
+                    }
+                }
+                const TI *XD = (fd ? XW : XT) + (tau & 1) * TT;
+#pragma unroll
+                for (int j = 0; j < NTT; ++j) {
 #pragma unroll
                     for (int k2 = 0; k2 < KB; ++k2) {
                         if (32 * k2 > 16 * rbk[j] + 15) continue;  // wave-uniform: above the diagonal
-                        const int j0 = tile0 + 32 * k2 + 8 * kg;
-                        const f32x4 cpa = *reinterpret_cast<const f32x4 *>(CPL + j0);
-                        const f32x4 cpb = *reinterpret_cast<const f32x4 *>(CPL + j0 + 4);
-                        frag ma;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float cpj = e < 4 ? cpa[e] : cpb[e - 4];
-                            const float v = Tr::frag_get(gd[j][k2], e) * fast_exp2(cs_i - cpj);
-                            Tr::frag_set(ma, e, (j0 + e <= irow) ? v : 0.f);
-                        }
 #pragma unroll
                         for (int pb = 0; pb < PB; ++pb) {
-                            const frag xb = Tr::lds_frag(XTc + (16 * pb + r) * X_LD + 32 * k2 + 8 * kg);
-                            acc[j][pb] = Tr::mma(ma, xb, acc[j][pb]);
+                            const frag xb = Tr::lds_frag(XD + (16 * pb + r) * X_LD + 32 * k2 + 8 * kg);
+                            acc[j][pb] = Tr::mma(gd[j][k2], xb, acc[j][pb]);
                         }
                     }
+                }
+                if constexpr (kFD) {
+#pragma unroll
+                    for (int j = 0; j < NTT; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int pb = 0; pb < PB; ++pb) acc[j][pb][i] *= fd ? fr[j][i] : 1.f;
                 }
                 load_g(min(tau + 1, last_tile));
                 // skip term, staging through this wave's own rows, store
@@ -678,9 +653,11 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                     const uint32_t sy = (uint32_t)(t0 + tile0 + 16 * rbk[j]) * x_tok + hp0;
 #pragma unroll
                     for (int k = 0; k < NZ; ++k) {
+                        // lanes past the block's vectors run along (no lane-divergent
+                        // branch): clamped row, out-of-range store (dropped)
                         const int v = lane + 64 * k;
-                        if (NZ * 64 > 16 * VPR && v >= 16 * VPR) break;
-                        const int rl = v / VPR, cv = v % VPR;
+                        const bool vin = !(NZ * 64 > 16 * VPR) || v < 16 * VPR;
+                        const int rl = min(v / VPR, 15), cv = v % VPR;
                         u32x4 d = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(YS) +
                                                                    (16 * rbk[j] + rl) * YS_LD * ES + cv * 16);
                         if (gate) {  // fused output gate y * silu(z), in fp32
@@ -698,13 +675,10 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                                 d = __builtin_bit_cast(u32x4, yv);
                             }
                         }
-                        buf_st128s(d, ry, (uint32_t)rl * x_tok + (uint32_t)(cv * 16), sy);
+                        buf_st128s(d, ry, oob_if(!vin, (uint32_t)rl * x_tok + (uint32_t)(cv * 16)), sy);
                     }
                 }
-                // X of the next tile into the other slot, then the loads of the one after
-                if constexpr (kXOut) stage_x((tau + 1) & 1);
                 load_z(min(tau + 1, last_tile) * TT);
-                if constexpr (kXOut) load_x(min(tau + 2, last_tile) * TT);
                 __syncthreads();
             });
         }
@@ -738,13 +712,17 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         frag xh[kDepth][RX][kConv ? 3 : 1];  // the 3 tokens before each X unit (conv)
         f32x4 bcp[kDepth][RB];   // cs' of the B unit's 4 tokens
         float xce[kDepth] = {};  // cs2 of the tile's last token
+        // (kFD) cs' of the X unit's 4 tokens, and cs2 before the tile: the
+        // reference of the weighted X, 0 at a chunk's first tile
+        f32x4 xcp[kDepth][kFD ? RX : 1];
+        float xcr[kDepth] = {};
         const rsrc_t rcs = make_rsrc(cs_row, (uint32_t)a.Tpad * 4u);
         auto issue_stage = [&](int tt, auto Sc) __attribute__((always_inline)) {  // X, B and log-decays of the tile at token tt
             constexpr int S = decltype(Sc)::value;
             const uint32_t sx = (uint32_t)tt * x_tok + hp0;
             const uint32_t sb = (uint32_t)(tt * G + g) * (uint32_t)(N * ES);
 #pragma unroll
-            for (int k = 0; k < (kXOut ? 0 : RX); ++k) {
+            for (int k = 0; k < RX; ++k) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xr[S][k][i] = Tr::load_frag_s(rx, vx[k] + i * x_tok, sx);
                 if constexpr (kConv) {
@@ -760,6 +738,13 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
             // a vector load: a scalar one would hold up every LDS wait (both
             // count in lgkmcnt) until it returns
             xce[S] = __builtin_bit_cast(float, buf_ld32(rcs, (uint32_t)(tt + TT - 1) * 4u));
+            if constexpr (kFD) {
+                const float ref = __builtin_bit_cast(float, buf_ld32(rcs, (uint32_t)max(tt - 1, 0) * 4u));
+                xcr[S] = (tt % Q == 0) ? 0.f : ref;
+#pragma unroll
+                for (int k = 0; k < RX; ++k)
+                    xcp[S][k] = *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * ((st + 256 * k) % TQ));
+            }
 #pragma unroll
             for (int k = 0; k < RB; ++k) {
 #pragma unroll
@@ -770,12 +755,15 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
         auto stage = [&](auto Sc, int slot) __attribute__((always_inline)) {  // into X slot `slot` and the matching B^T copy
             constexpr int S = decltype(Sc)::value;
             TI *BT = BTB + (kBT2 ? slot : 0) * N * BT_LD;
-            // (when kXOut the output waves stage X)
+            // Where the units do not fill whole wavefronts, every lane runs the
+            // staging (no lane-divergent branch) and lanes without a unit write
+            // into the rows' padding columns, which nothing reads.
 #pragma unroll
-            for (int k = 0; k < (kXOut ? 0 : RX); ++k)
-                if (x_unit(k)) {
+            for (int k = 0; k < RX; ++k)
+                if (UX % 64 != 0 || x_unit(k)) {
                     const int u = st + 256 * k;
                     const int tq = u % TQ, po = (u / TQ) % (PW / 8);
+                    const int xcol = x_unit(k) ? slot * TT + 4 * tq : 2 * TT;  // padding: 2 TT .. 2 TT + PAD - 1
                     if constexpr (kConv) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
@@ -794,28 +782,56 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                                                 wv[3] * xv[i + 3];
                                 yv[i] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
                             }
-                            lds_store4<TI>(XT + c * X_LD + slot * TT + 4 * tq, Tr::from_f32(yv[0]),
-                                           Tr::from_f32(yv[1]), Tr::from_f32(yv[2]), Tr::from_f32(yv[3]));
+                            lds_store4<TI>(XT + c * X_LD + xcol, Tr::from_f32(yv[0]), Tr::from_f32(yv[1]),
+                                           Tr::from_f32(yv[2]), Tr::from_f32(yv[3]));
                         }
                     } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            lds_store4<TI>(XT + (8 * po + e) * X_LD + slot * TT + 4 * tq, xr[S][k][0][e],
-                                           xr[S][k][1][e], xr[S][k][2][e], xr[S][k][3][e]);
+                            lds_store4<TI>(XT + (8 * po + e) * X_LD + xcol, xr[S][k][0][e], xr[S][k][1][e],
+                                           xr[S][k][2][e], xr[S][k][3][e]);
+                        if constexpr (kFD) {
+                            // x_j 2^(cs_ref - cs'_j) = dt_j x_j 2^(cs_ref - cs_j), at most
+                            // dt_j x_j 2^kFDMax in the tiles that use it
+                            if (xcr[S] - xce[S] <= kFDMax) {
+                                float cw[4];
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) cw[i] = fast_exp2(xcr[S] - xcp[S][k][i]);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e)
+                                    lds_store4<TI>(XW + (8 * po + e) * X_LD + xcol,
+                                                   Tr::from_f32(Tr::frag_get(xr[S][k][0], e) * cw[0]),
+                                                   Tr::from_f32(Tr::frag_get(xr[S][k][1], e) * cw[1]),
+                                                   Tr::from_f32(Tr::frag_get(xr[S][k][2], e) * cw[2]),
+                                                   Tr::from_f32(Tr::frag_get(xr[S][k][3], e) * cw[3]));
+                            }
+                        }
                     }
                 }
+            // factored tiles take B^T as it is (their weights are on X)
+            const bool braw = kFD && (xcr[S] - xce[S] <= kFDMax);
+            // (the same padding rule as for X: B^T rows have TT + PAD columns)
 #pragma unroll
             for (int k = 0; k < RB; ++k)
-                if (b_unit(k)) {
+                if ((UB % 64 != 0 || b_unit(k)) && braw) {
                     const int u = st + 256 * k;
                     const int tq = u % TQ, no = (u / TQ) % (N / 8);
+                    const int bcol = b_unit(k) ? 4 * tq : TT;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + bcol, br[S][k][0][e], br[S][k][1][e],
+                                       br[S][k][2][e], br[S][k][3][e]);
+                } else if (UB % 64 != 0 || b_unit(k)) {
+                    const int u = st + 256 * k;
+                    const int tq = u % TQ, no = (u / TQ) % (N / 8);
+                    const int bcol = b_unit(k) ? 4 * tq : TT;
                     // the state update's weights w_j = exp2(cs_e - cs'_j) <= dt_j
                     float sc[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) sc[i] = fast_exp2(xce[S] - bcp[S][k][i]);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + 4 * tq,
+                        lds_store4<TI>(BT + (8 * no + e) * BT_LD + bcol,
                                        Tr::from_f32(Tr::frag_get(br[S][k][0], e) * sc[0]),
                                        Tr::from_f32(Tr::frag_get(br[S][k][1], e) * sc[1]),
                                        Tr::from_f32(Tr::frag_get(br[S][k][2], e) * sc[2]),
@@ -873,16 +889,22 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                 const TI *BT = BTB + (kBT2 ? slot : 0) * N * BT_LD;
                 const float cs_ref = (I > 0) ? CSL[tile0 - 1] : 0.f;
                 const float dec = fast_exp2(CSL[tile0 + TT - 1] - cs_ref);
+                // factored tile: h_e = dec (h + B^T Xw); else h_e = dec h + Bw^T X.
+                // Both scalings always run (one of them by 1): a branch next to the
+                // matrix-core ops left the accumulators read too early on one path.
+                const bool fd = kFD && (cs_ref - CSL[tile0 + TT - 1] <= kFDMax);
+                const float pre = fd ? 1.f : dec, post = fd ? dec : 1.f;
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
-                    for (int j = 0; j < NBW; ++j) hacc[pb][j] *= dec;
+                    for (int j = 0; j < NBW; ++j) hacc[pb][j] *= pre;
+                const TI *XS = (fd ? XW : XT) + slot * TT;
 #pragma unroll
                 for (int k2 = 0; k2 < KB; ++k2) {
                     frag xa[PB];
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb)
-                        xa[pb] = Tr::lds_frag(XT + (16 * pb + r) * X_LD + slot * TT + 32 * k2 + 8 * kg);
+                        xa[pb] = Tr::lds_frag(XS + (16 * pb + r) * X_LD + 32 * k2 + 8 * kg);
 #pragma unroll
                     for (int j = 0; j < NBW; ++j) {
                         const int nb = w + 4 * j;
@@ -892,6 +914,12 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
                             for (int pb = 0; pb < PB; ++pb) hacc[pb][j] = Tr::mma(bb, xa[pb], hacc[pb][j]);
                         }
                     }
+                }
+                if constexpr (kFD) {
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+                        for (int j = 0; j < NBW; ++j) hacc[pb][j] *= post;
                 }
                 // a single B^T copy, or a single state copy, is read up to here
                 if constexpr (kMidSync) __syncthreads();

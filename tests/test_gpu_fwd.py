@@ -18,11 +18,11 @@ from tests.gpu_util import TOL, gpu_fwd, log, oracle_fwd, rel, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def check_full(ssd, cfg, chunk=None, tag=""):
+def check_full(ssd, cfg, chunk=None, tag="", inp=None):
     chunk = chunk or cfg.chunk
     log(f"[fwd full] {cfg.name}{tag} chunk={chunk} shape=(b{cfg.batch},T{cfg.seqlen},H{cfg.nheads},"
         f"P{cfg.headdim},N{cfg.dstate},G{cfg.ngroups}) {cfg.dtype}")
-    inp = si.make_fwd_inputs(cfg)
+    inp = si.make_fwd_inputs(cfg) if inp is None else inp
     tol = TOL[cfg.dtype]
     Yg, Fg = gpu_fwd(ssd, inp, chunk)
     Yr, Fr = oracle_fwd(inp, cfg.ngroups)
@@ -71,6 +71,34 @@ def test_f32_head_and_state_sizes(ssd, P, N):
 @pytest.mark.parametrize("name", ["s2_a_zero", "s3_ragged", "s4_groups", "s5_large_dt"])
 def test_stress_workloads(ssd, name):
     check_full(ssd, si.STRESS[name])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiles_switching_between_diagonal_forms(ssd, dtype):
+    """A 64-token tile whose decay is at most 2^64 takes the factored diagonal
+    block, a faster-decaying one the per-element weights. Step sizes that jump
+    between small and large inside the sequence make neighbouring tiles, and the
+    tiles on either side of a chunk boundary, switch between the two."""
+    base = "tiny_f32" if dtype == "f32" else "l1p3b_bf16"
+    cfg = dataclasses.replace(si.CONFIGS[base], name=f"mixed_decay_{dtype}", batch=2, seqlen=700, nheads=4,
+                              headdim=32, dstate=64, seed=41)
+    inp = si.make_fwd_inputs(cfg)
+    dt = inp["dt32"].copy()
+    for lo, hi in ((70, 150), (250, 262), (400, 600)):
+        dt[:, lo:hi, :] = 0.6
+    if dtype == "bf16":
+        inp["dt"] = si.bf16_round_bits(dt)
+        inp["dt32"] = si.bf16_bits_to_f32(inp["dt"])
+    else:
+        inp["dt"] = inp["dt32"] = dt
+    # tile decays (base-2 log units), to show that both forms occur
+    dec = -inp["A"][None, None, :] * inp["dt32"] * np.log2(np.e)
+    T = cfg.seqlen
+    tiles = np.add.reduceat(dec, np.arange(0, T, 64), axis=1)
+    n_fast, n_slow = int(np.sum(tiles <= 60)), int(np.sum(tiles > 70))
+    log(f"    tiles decaying within 2^60: {n_fast}, beyond 2^70: {n_slow}")
+    assert n_fast > 0 and n_slow > 0
+    check_full(ssd, cfg, chunk=128, inp=inp)
 
 
 def test_short_sequences(ssd):
