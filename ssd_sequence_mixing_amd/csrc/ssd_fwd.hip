@@ -24,8 +24,9 @@
 //                 weight dt_j exp2(cs_i - cs_j) of token j seen from token i is
 //                 one exponential, exp2(cs_i - cs'_j).
 //   tile_cb       per (batch, tile, group): G = C B^T of the tile's 64 tokens
-//                 (matrix cores). It depends on the group only, so it is
-//                 formed once and shared by every head of the group.
+//                 (matrix cores), stored with the entries above the diagonal
+//                 zeroed. It depends on the group only, so it is formed once
+//                 and shared by every head of the group.
 //   k_chunk_walk  per (batch, head): walks the tiles in order with the state
 //                 held in matrix-core accumulators. For tile rows i it forms
 //                   Y_i = exp2(cs_i - cs_r) C_i h_r^T          (state -> output)
@@ -37,9 +38,14 @@
 //                 the state cross HBM once; the state never leaves the chip
 //                 until the final state is written.
 //
-// Masks are never stored: every decay factor above is <= 1, and on the
-// diagonal tile the mask is built per element in registers, with j > i
-// selected to zero before the exponential is used.
+// In a tile whose decay cs_r - cs_e is at most kFDMax the weights are
+// factored about the tile's start: exp2(cs_i - cs'_j) = exp2(cs_i - cs_r)
+// exp2(cs_r - cs'_j). The second factor goes on a weighted copy of X,
+// Xw_j = exp2(cs_r - cs'_j) x_j, so that
+//   Y_i = exp2(cs_i - cs_r) (C_i h_r^T + sum_j G_ij Xw_j) + D x_i
+//   h   <- exp2(cs_e - cs_r) (h + Xw^T B)
+// with G already masked: no weight is formed per element. Other tiles use
+// the per-element form above, where every factor is <= dt.
 #include <utility>
 
 #include "ssd_common.h"
@@ -255,14 +261,14 @@ __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
 //     128-token tiles, 7 - w, which balances the triangular diagonal work):
 //     C rows and the tile's C B^T rows come from global memory one tile
 //     ahead; the state at the tile's start comes from an LDS copy; form the
-//     state term, the masked diagonal block and the skip term; store Y
-//     through a per-wave LDS staging area.
+//     state term, the diagonal block and the skip term; store Y through a
+//     per-wave LDS staging area.
 //   state waves (4-7), a quarter of the state's rows n each: X, B and
 //     log-decays come from global memory two tiles ahead (one when a chunk
 //     has an odd tile count); update h with this tile, write h as the next
-//     tile's LDS copy, and stage the next tile's X and B^T into the other
-//     LDS slots. The decay weights w_j of the state update are applied to
-//     B^T as it is staged, so one copy of X serves both roles.
+//     tile's LDS copy, and stage the next tile's X, weighted X (factored
+//     tiles) and B^T (weighted by w_j in the other tiles) into the other
+//     LDS slots.
 // One barrier per tile; a second one where LDS cannot hold two copies of
 // B^T or of the state.
 // The state is accumulated transposed (h^T[n][p]) so that each lane holds
