@@ -306,8 +306,11 @@ struct WalkCfg {
     static constexpr int XT_OFF = 0;
     static constexpr int X_BYTES = PW * X_LD * ES;
     // walks without the input convolution keep a second, weighted X copy
-    // (two slots, the layout of X) for the factored diagonal block
-    static constexpr bool kXW = !kConv;
+    // (two slots, the layout of X) for the factored diagonal block, up to
+    // N = 128: with N = 256 the state waves, which stage it, are the busier
+    // role and the per-element form was measured faster (walk 356 vs 383 us
+    // on the 16K-token shape)
+    static constexpr bool kXW = !kConv && N <= 128;
     static constexpr int XW_OFF = XT_OFF + X_BYTES;
     static constexpr int YS_OFF = XW_OFF + (kXW ? X_BYTES : 0);
     static constexpr int YS_BYTES = TT * YS_LD * ES;
