@@ -239,6 +239,11 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
     __shared__ __attribute__((aligned(16))) TI UT[P * T_LD];
     __shared__ __attribute__((aligned(16))) TI VT[N * T_LD];
     __shared__ float WT[kBT];
+    // the state each tile stores goes through LDS ([p][n], padded rows) so that
+    // it leaves as whole 16-byte row pieces: written straight from the
+    // accumulators each store instruction would cover 16 rows x 32 bytes
+    constexpr int S_LD = N + PAD;
+    __shared__ __attribute__((aligned(16))) TI SS[P * S_LD];
 
     const int H = a.H, G = a.G, T = a.T;
     const int bh = blockIdx.x, b = bh / H, h = bh - b * H, g = (h * G) / H;
@@ -300,11 +305,20 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
 #pragma unroll
             for (int j = 0; j < NBW; ++j) {
                 const int nb = w + NW * j;
-                if (nb < NB) store4<TI>(dst + (16 * pb + r) * N + 16 * nb + 4 * kg, acc[pb][j]);
+                if (nb < NB) store4<TI>(SS + (16 * pb + r) * S_LD + 16 * nb + 4 * kg, acc[pb][j]);
             }
         const float cs_r = pcs_r[S], cs_e = pcs_e[S];
         if (tid < kBT) WT[tid] = kRev ? fast_exp2(wcs[S] - cs_r) : fast_exp2(cs_e - wcs[S]);
-        __syncthreads();  // WT visible; the previous tile's reads of UT / VT are done
+        __syncthreads();  // SS and WT visible; the previous tile's reads of UT / VT are done
+        {
+            constexpr int VPRS = N * ES / 16;  // 16-byte pieces per state row
+#pragma unroll
+            for (int v = tid; v < P * VPRS; v += NTH) {
+                const int p = v / VPRS, c = v % VPRS;
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(dst) + (size_t)p * N * ES + c * 16) =
+                    *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(SS) + p * S_LD * ES + c * 16);
+            }
+        }
         ur[S].template store_T<false>(UT, T_LD, tid, [](int) { return 1.f; });
         vr[S].template store_T<true>(VT, T_LD, tid, [&](int q) { return WT[q]; });
         __syncthreads();
