@@ -78,6 +78,29 @@ def test_decode_state_sizes(ssd, N):
     run_decode(ssd, cfg, [(b, h) for b in range(2) for h in range(4)], 5, {1, 5})
 
 
+def test_decode_full_size_whole_state(ssd):
+    """Batch 256: the whole y and the whole state after steps 1 and 10 against
+    the oracle run on the whole state."""
+    import torch
+    cfg = si.DECODE
+    log(f"[step] {cfg.name} whole-tensor check at steps 1 and 10")
+    d = si.make_decode_inputs(cfg)
+    state = to_dev(d["state0"])
+    A, D = to_dev(d["A"]), to_dev(d["D"])
+    sets = [{k: to_dev(v) for k, v in st.items() if not k.endswith("32")} for st in d["sets"]]
+    s_ref = d["state0"].astype(np.float64)
+    tol = TOL["bf16"]
+    for k in range(10):
+        st, hs = sets[k % cfg.nsets], d["sets"][k % cfg.nsets]
+        y = ssd.ssd_step(state, st["x"], st["dt"], A, st["B"], st["C"], D)
+        y_ref = oracle.step(s_ref, hs["x32"], hs["dt32"], d["A"], hs["B32"], hs["C32"], d["D"], cfg.ngroups)
+        if k + 1 in (1, 10):
+            torch.cuda.synchronize()
+            e = (rel(to_np(y), y_ref), rel(state.cpu().numpy(), s_ref))
+            log(f"    step {k + 1}: rel err y={e[0]:.2e} state={e[1]:.2e} (tol {tol})")
+            assert e[0] <= tol and e[1] <= tol, (k + 1, e)
+
+
 def test_decode_full_size_1000_steps(ssd):
     cfg = si.DECODE
     samples = [(0, 0), (17, 33), (128, 63), (255, 5)]
