@@ -9,16 +9,17 @@
 // One work-group per (batch, head, column slice of PW columns), 8 wavefronts
 // in two roles, each role split 2 x 2 by (a, b), b the half of the columns:
 //   state waves 4-7 keep the state block h[p in half b][n in half a] in fp32
-//     matrix-core accumulators, update it per tile from the weighted X and
-//     B^T in LDS, and publish it in bf16 (4 KB per wave at P 64, N 128) as
-//     the operand of the next tile's state -> output product. They also stage
-//     B^T for the next tile (B loaded two tiles ahead).
+//     matrix-core accumulators, update it per tile from X^T and B^T in LDS,
+//     and publish it in bf16 (4 KB per wave at P 64, N 128) as the operand of
+//     the next tile's state -> output product. They also stage B^T for the
+//     next tile (B loaded two tiles ahead).
 //   output waves 0-3 form the transposed output Y^T[p in half b][i] for the
 //     tokens i of half a: state -> output from the published state (both n
 //     halves of its columns), the diagonal block from C B^T and the weighted
-//     X, the skip term, the gate, and the store. They also stage, for the
-//     next tile, the C rows (whole lines, into LDS) and X weighted by its
-//     decay factors, written token-major (X^T) for the two products whose
+//     X, the skip term and the gate; the output goes through LDS and leaves
+//     as whole rows during the next tile. They also stage, for the next
+//     tile, the C rows (whole lines, into LDS) and X weighted by its decay
+//     factors, written token-major (X^T) for the two products whose
 //     contraction runs over tokens.
 // Each SIMD runs one wavefront of each role; one barrier per tile.
 //
@@ -39,9 +40,9 @@
 // a tile whose decay cs_r - cs_e is at most kFDMax is factored about its
 // start, X~_j = 2^(cs_r - cs'_j) x_j,
 //   Y_i = 2^(cs_i - cs_r) (C_i h_r + sum_j G_ij X~_j) + D x_i,  h_e = 2^(cs_e - cs_r) (h_r + X~^T B);
-// other tiles take the weights referenced to the tile's end for the state,
-// X^_j = 2^(cs_e - cs'_j) x_j <= dt_j x_j, h_e = 2^(cs_e - cs_r) h_r + X^^T B, and
-// per-element weights G_ij 2^(cs_i - cs'_j) on the plain X for the diagonal block.
+// other tiles keep X as it is and put the weights elsewhere: on B^T for the
+// state, Bw_j = 2^(cs_e - cs'_j) B_j <= dt_j B_j, h_e = 2^(cs_e - cs_r) h_r + X^T Bw,
+// and per element on C B^T for the diagonal block, G_ij 2^(cs_i - cs'_j).
 #include <type_traits>
 #include <utility>
 
@@ -71,12 +72,17 @@ struct RsCfg {
     static constexpr int XCH_BYTES = 4 * XF * 64 * 16;
     static constexpr int CLD = N + 8;             // row length of the C tile
     static constexpr int C_BYTES = TT * CLD * 2;
-    static constexpr int XW_OFF = 0;                      // weighted X^T, 2 slots
-    static constexpr int XP_OFF = XW_OFF + 2 * XT_BYTES;  // plain X^T (per-element tiles), 2 slots
-    static constexpr int BT_OFF = XP_OFF + 2 * XT_BYTES;  // B^T, 2 slots
+    static constexpr int YLD = PW + 8;            // row length of the output staging tile
+    static constexpr int YS_BYTES = TT * YLD * 2;
+    static constexpr int XW_OFF = 0;                      // X^T (weighted in factored tiles), 2 slots
+    static constexpr int YS_OFF = XW_OFF + 2 * XT_BYTES;  // output rows, 2 slots
+    static constexpr int BT_OFF = YS_OFF + 2 * YS_BYTES;  // B^T (weighted in the other tiles), 2 slots
     static constexpr int XCH_OFF = BT_OFF + 2 * BT_BYTES; // state exchange, 2 slots
     static constexpr int C_OFF = XCH_OFF + 2 * XCH_BYTES; // C, 2 slots
-    static constexpr int CS_OFF = C_OFF + 2 * C_BYTES;
+    static constexpr int XRLD = PW + 8;           // row length of the token-major X tile (skip term)
+    static constexpr int XR_BYTES = TT * XRLD * 2;
+    static constexpr int XR_OFF = C_OFF + 2 * C_BYTES;    // X rows, 2 slots
+    static constexpr int CS_OFF = XR_OFF + 2 * XR_BYTES;
     static constexpr int CS_BYTES = 2 * 2 * Q * 4;       // 2 chunks x (cs2, cs')
     static constexpr int LDS = CS_OFF + CS_BYTES;
     // staging units (256 lanes of one role each)
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
     constexpr bool kCsLds = Cfg::kCsLds;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
     bf16 *XW = reinterpret_cast<bf16 *>(smem + Cfg::XW_OFF);
-    bf16 *XP = reinterpret_cast<bf16 *>(smem + Cfg::XP_OFF);
+    bf16 *YSB = reinterpret_cast<bf16 *>(smem + Cfg::YS_OFF);
     bf16 *BTB = reinterpret_cast<bf16 *>(smem + Cfg::BT_OFF);
     char *XCH = smem + Cfg::XCH_OFF;
     float *CSB = reinterpret_cast<float *>(smem + Cfg::CS_OFF);
@@ -213,7 +219,6 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
     if (wv < 4) {
         // ============================ output waves ============================
         const float Dh = a.D[h];
-        const rsrc_t ry = make_rsrc(reinterpret_cast<char *>(a.Y) + x0, (uint32_t)xslab);
         const rsrc_t rg = make_rsrc(a.Gbuf, a.g_bytes);
         const rsrc_t rcm = make_rsrc(reinterpret_cast<const char *>(a.C) + b0, (uint32_t)bslab);
         const rsrc_t rz = make_rsrc(reinterpret_cast<const char *>(a.z) + (kGate ? x0 : 0),
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         }
         using xvec = typename std::conditional<(PBH >= 2), u32x4, u32x2>::type;
         frag gf[IB][KS];          // C B^T fragments: k-step ks covers tokens 32 ks + 8 kg .. + 7
-        xvec xq[IB][NPQ], zq[IB][NPQ];
+        xvec zq[IB][NPQ];
         auto load_g = [&](int tau) __attribute__((always_inline)) {
             const uint32_t sg = (uint32_t)((gbase + tau) * (size_t)(TT * TT * 2));
 #pragma unroll
@@ -243,20 +248,20 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 for (int ks = 0; ks < KS; ++ks)
                     gf[ib][ks] = Tr::load_frag_s(rg, oob_if(ks > ah, vgo[ib] + ks * 64), sg);
         };
-        auto load_xz = [&](int tt) __attribute__((always_inline)) {
-            const uint32_t sx = (uint32_t)tt * x_tok + hp0;
+        auto load_z = [&](int tt) __attribute__((always_inline)) {
+            if constexpr (kGate) {
+                const uint32_t sx = (uint32_t)tt * x_tok + hp0;
 #pragma unroll
-            for (int ib = 0; ib < IB; ++ib)
+                for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
-                for (int q = 0; q < NPQ; ++q) {
-                    if constexpr (PBH >= 2) {
-                        xq[ib][q] = buf_ld128s(rx, vy[ib][q], sx);
-                        if constexpr (kGate) zq[ib][q] = buf_ld128s(rz, vy[ib][q], sx);
-                    } else {
-                        xq[ib][q] = __builtin_amdgcn_raw_buffer_load_b64(rx, vy[ib][q], sx, 0);
-                        if constexpr (kGate) zq[ib][q] = __builtin_amdgcn_raw_buffer_load_b64(rz, vy[ib][q], sx, 0);
+                    for (int q = 0; q < NPQ; ++q) {
+                        if constexpr (PBH >= 2) {
+                            zq[ib][q] = buf_ld128s(rz, vy[ib][q], sx);
+                        } else {
+                            zq[ib][q] = __builtin_amdgcn_raw_buffer_load_b64(rz, vy[ib][q], sx, 0);
+                        }
                     }
-                }
+            }
         };
         // C staging: this wave loads 16 of the 32 rows its token half needs
         // (rows 32 ah + 16 bh ..) a tile ahead as whole lines, and writes them
@@ -304,29 +309,30 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         auto stage_x = [&](auto Sc, int slot, float cr, float ce, auto &&cpk) __attribute__((always_inline)) {
             constexpr int Sx = decltype(Sc)::value;
             const bool fd = (cr - ce <= kRsFDMax);
-            // factored: X~_j = 2^(cs_r - cs'_j) x_j; otherwise X^_j = 2^(cs_e - cs'_j) x_j
-            const float ref = fd ? cr : ce;
             bf16 *XWs = XW + slot * PW * LD;
-            bf16 *XPs = XP + slot * PW * LD;
+            bf16 *XRs = reinterpret_cast<bf16 *>(smem + Cfg::XR_OFF + slot * Cfg::XR_BYTES);
 #pragma unroll
             for (int k = 0; k < RX; ++k) {
                 const int u = st + 256 * k;
                 if (u >= Cfg::UX) continue;  // wave-uniform (UX is a multiple of 64)
                 const int tq = rs_unit_tq(u), c4 = rs_unit_col(u);
+                // the unit's 4 tokens x 4 columns as they are, for the skip term
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x2 *>(XRs + (4 * tq + i) * Cfg::XRLD + 4 * c4) = xr[Sx][k][i];
+                // factored tiles: X~_j = 2^(cs_r - cs'_j) x_j; the others: x_j as it is
                 const f32x4 cp = cpk(k);
                 float cw[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) cw[i] = fast_exp2(ref - cp[i]);
+                for (int i = 0; i < 4; ++i) cw[i] = fd ? fast_exp2(cr - cp[i]) : 1.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     // column 4 c4 + e, its 4 tokens 4 tq .. 4 tq + 3: half of 16-byte piece tq / 2
                     float xv[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xv[i] = (e & 1) ? bf16_hi(xr[Sx][k][i][e >> 1]) : bf16_lo(xr[Sx][k][i][e >> 1]);
-                    const int off = xw_off(4 * c4 + e, tq >> 1) + 4 * (tq & 1);
-                    *reinterpret_cast<u32x2 *>(XWs + off) =
+                    *reinterpret_cast<u32x2 *>(XWs + xw_off(4 * c4 + e, tq >> 1) + 4 * (tq & 1)) =
                         u32x2{pack_bf16x2(xv[0] * cw[0], xv[1] * cw[1]), pack_bf16x2(xv[2] * cw[2], xv[3] * cw[3])};
-                    if (!fd) *reinterpret_cast<u32x2 *>(XPs + off) = u32x2{pack_bf16x2(xv[0], xv[1]), pack_bf16x2(xv[2], xv[3])};
                 }
             }
         };
@@ -340,6 +346,23 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
             });
         };
 
+        // The output rows of tile tau, staged in LDS slot tau % 2 by all four
+        // output waves, leave as whole rows at the start of tile tau + 1: 16
+        // rows per wave, PW / 8 lanes per row.
+        const rsrc_t ry = make_rsrc(reinterpret_cast<char *>(a.Y) + x0, (uint32_t)xslab);
+        constexpr int YP = PW / 8;             // 16-byte pieces per row
+        constexpr int YRI = 64 / YP;           // rows per store instruction
+        auto store_y = [&](int tau) __attribute__((always_inline)) {
+            const bf16 *YSs = YSB + (tau & 1) * TT * Cfg::YLD;
+            const uint32_t sy = (uint32_t)(tau * TT) * x_tok + hp0;
+#pragma unroll
+            for (int k = 0; k < 16 / YRI; ++k) {
+                const int row = 16 * wv + YRI * k + lane / YP, pc = lane % YP;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(YSs + row * Cfg::YLD + 8 * pc);
+                buf_st128s(v, ry, (uint32_t)row * x_tok + (uint32_t)(16 * pc), sy);
+            }
+        };
+
         const int tile_b = cb * NT;
         load_cs(tile_b * TT);
         issue_x(tile_b * TT, std::integral_constant<int, 0>{});
@@ -348,10 +371,9 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         if constexpr (kDepth == 2) issue_x(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
         load_g(tile_b);
         __builtin_amdgcn_sched_barrier(0);
-        load_xz(tile_b * TT);
+        load_z(tile_b * TT);
         __syncthreads();
         for (int c = cb; c < ce; ++c) {
-            const int t0 = c * Q;
             const float *CSL = CSB + ((c - cb) & 1) * 2 * Q;
             const float *CPL = CSL + Q;
             rs_static_for<NT>([&](auto Ic) __attribute__((always_inline)) {
@@ -361,6 +383,8 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 const int slot = tau & 1;
                 load_cs(min(tau + 1, last_tile) * TT);
                 issue_x(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
+                // the previous tile's output (its rows were completed before the barrier)
+                if (tau > cb * NT) store_y(tau - 1);
                 // the state at the tile's start, rows p of half bh, both n halves
                 frag hs[2][NM][PBH];
 #pragma unroll
@@ -383,6 +407,23 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 float cs_i[IB];
 #pragma unroll
                 for (int ib = 0; ib < IB; ++ib) cs_i[ib] = CSL[tile0 + 32 * ah + 16 * ib + r];
+                // the next tile's weighted X into the other slots, while this
+                // tile's operands arrive (its X slot was last read a tile ago)
+                {
+                    constexpr int SxN = kDepth == 2 ? ((I + 1) & 1) : 0;
+                    if constexpr (kCsLds) {
+                        // (after the last tile this stages data nobody reads)
+                        const float *CSn = (I + 1 < NT) ? CSL : CSB + ((c + 1 - cb) & 1) * 2 * Q;
+                        const int tn = ((I + 1) % NT) * TT;
+                        const float cr = (I + 1 < NT) ? CSn[tn - 1] : 0.f;
+                        stage_x(std::integral_constant<int, SxN>{}, (tau + 1) & 1, cr, CSn[tn + TT - 1],
+                                [&](int k) __attribute__((always_inline)) {
+                                    return *reinterpret_cast<const f32x4 *>(CSn + Q + tn + 4 * rs_unit_tq(st + 256 * k));
+                                });
+                    } else {
+                        stage_x_global(std::integral_constant<int, SxN>{}, min(tau + 1, last_tile));
+                    }
+                }
                 // state -> output: Y^T[p][i] = sum_n h[p][n] C[i][n]
                 f32x4 yacc[IB][PBH];
 #pragma unroll
@@ -397,8 +438,8 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                         for (int ib = 0; ib < IB; ++ib)
                             yacc[ib][pb] = Tr::mma(hs[kk / NM][kk % NM][pb], cf[ib][kk], yacc[ib][pb]);
                 const bool fd = (cs_ref - cs_end <= kRsFDMax);
-                // the diagonal block's X: weighted (factored tiles) or plain
-                const bf16 *XD = (fd ? XW : XP) + slot * PW * LD;
+                // the diagonal block's X (weighted in factored tiles)
+                const bf16 *XD = XW + slot * PW * LD;
                 frag xd[KS][PBH];
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
@@ -449,7 +490,8 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 load_g(min(tau + 1, last_tile));
                 // skip term, gate, store. Pairs of p-blocks swap halves between
                 // lanes 16 apart, after which a lane holds 8 consecutive columns of its token.
-                const uint32_t sy = (uint32_t)(t0 + tile0) * x_tok + hp0;
+                const bf16 *XRs = reinterpret_cast<const bf16 *>(smem + Cfg::XR_OFF + slot * Cfg::XR_BYTES);
+                bf16 *YSs = YSB + slot * TT * Cfg::YLD;
 #pragma unroll
                 for (int ib = 0; ib < IB; ++ib)
 #pragma unroll
@@ -468,7 +510,9 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) y[i] = yacc[ib][0][i];
                         }
-                        const xvec xv = xq[ib][q];
+                        // x of this lane's token and columns, from the X rows staged in LDS
+                        const xvec xv = *reinterpret_cast<const xvec *>(
+                            XRs + (32 * ah + 16 * ib + r) * Cfg::XRLD + PH * bh + 32 * q + pbase);
 #pragma unroll
                         for (int e = 0; e < NE; e += 2) {
                             y[e] += Dh * bf16_lo(xv[e / 2]);
@@ -486,31 +530,17 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                         xvec o;
 #pragma unroll
                         for (int e = 0; e < NE; e += 2) o[e / 2] = pack_bf16x2(y[e], y[e + 1]);
-                        if constexpr (PBH >= 2) {
-                            buf_st128s(o, ry, vy[ib][q], sy);
-                        } else {
-                            buf_st64s(o, ry, vy[ib][q], sy);
-                        }
+                        *reinterpret_cast<xvec *>(YSs + (32 * ah + 16 * ib + r) * Cfg::YLD + PH * bh + 32 * q + pbase) = o;
                     }
-                load_xz(min(tau + 1, last_tile) * TT);
-                // the next tile's X and C into the other slots
-                constexpr int SxN = kDepth == 2 ? ((I + 1) & 1) : 0;
-                if constexpr (kCsLds) {
-                    // (after the last tile this stages data nobody reads)
-                    const float *CSn = (I + 1 < NT) ? CSL : CSB + ((c + 1 - cb) & 1) * 2 * Q;
-                    const int tn = ((I + 1) % NT) * TT;
-                    const float cr = (I + 1 < NT) ? CSn[tn - 1] : 0.f;
-                    stage_x(std::integral_constant<int, SxN>{}, (tau + 1) & 1, cr, CSn[tn + TT - 1],
-                            [&](int k) __attribute__((always_inline)) {
-                                return *reinterpret_cast<const f32x4 *>(CSn + Q + tn + 4 * rs_unit_tq(st + 256 * k));
-                            });
-                } else {
-                    stage_x_global(std::integral_constant<int, SxN>{}, min(tau + 1, last_tile));
-                }
+                load_z(min(tau + 1, last_tile) * TT);
+                // the next tile's C rows into the other slot
                 store_cs((tau + 1) & 1);
                 __syncthreads();
             });
         }
+        // the last tile's output (the state waves pass the same barrier)
+        __syncthreads();
+        if (ce > cb) store_y(ce * NT - 1);
     } else {
         // ============================ state waves ============================
         const rsrc_t rbm = make_rsrc(reinterpret_cast<const char *>(a.B) + b0, (uint32_t)bslab);
@@ -558,31 +588,60 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) br[Sx][k][i] = buf_ld128s(rbm, vb[k] + i * b_tok, sb);
         };
-        auto stage_b = [&](auto Sc, int slot) __attribute__((always_inline)) {
+        // writes B^T of a tile into slot `slot`: as it is in factored tiles,
+        // weighted by w_j = 2^(cs_e - cs'_j) in the others; cr / ce: cs2 before
+        // the tile and at its last token, cpk(k): cs' of unit k's 4 tokens
+        auto stage_b = [&](auto Sc, int slot, float cr, float ce, auto &&cpk) __attribute__((always_inline)) {
             constexpr int Sx = decltype(Sc)::value;
+            const bool fd = (cr - ce <= kRsFDMax);
             bf16 *BT = BTB + slot * N * LD;
 #pragma unroll
             for (int k = 0; k < RB; ++k) {
                 const int u = st + 256 * k;
                 if (u >= Cfg::UB) continue;  // wave-uniform (UB is a multiple of 64)
                 const int tq = rs_unit_tq(u), c8 = rs_unit_col(u);
+                if (fd) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // element e of the 8 n of this unit, for its 4 tokens
-                    uint32_t w[4];
+                    for (int e = 0; e < 8; ++e) {
+                        // element e of the 8 n of this unit, for its 4 tokens
+                        uint32_t w[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) w[i] = br[Sx][k][i][e >> 1];
-                    // tokens 0 and 1 in the low and high halves of the first word, 2 and 3 of the second
-                    const u32x2 v = (e & 1) ? u32x2{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)}
-                                            : u32x2{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
-                    *reinterpret_cast<u32x2 *>(BT + bt_off(rs_row_of_n(8 * c8 + e), tq >> 1) + 4 * (tq & 1)) = v;
+                        for (int i = 0; i < 4; ++i) w[i] = br[Sx][k][i][e >> 1];
+                        // tokens 0 and 1 in the low and high halves of the first word, 2 and 3 of the second
+                        const u32x2 v = (e & 1) ? u32x2{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)}
+                                                : u32x2{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
+                        *reinterpret_cast<u32x2 *>(BT + bt_off(rs_row_of_n(8 * c8 + e), tq >> 1) + 4 * (tq & 1)) = v;
+                    }
+                } else {
+                    const f32x4 cp = cpk(k);
+                    float wt[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) wt[i] = fast_exp2(ce - cp[i]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float bv[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            bv[i] = ((e & 1) ? bf16_hi(br[Sx][k][i][e >> 1]) : bf16_lo(br[Sx][k][i][e >> 1])) * wt[i];
+                        *reinterpret_cast<u32x2 *>(BT + bt_off(rs_row_of_n(8 * c8 + e), tq >> 1) + 4 * (tq & 1)) =
+                            u32x2{pack_bf16x2(bv[0], bv[1]), pack_bf16x2(bv[2], bv[3])};
+                    }
                 }
             }
+        };
+        // stages a tile whose log-decays are read from global memory
+        auto stage_b_global = [&](auto Sc, int tau) __attribute__((always_inline)) {
+            const int tt = tau * TT;
+            const float cr = (tt % Q == 0) ? 0.f : cs_row[tt - 1];
+            const float ce = cs_row[tt + TT - 1];
+            stage_b(Sc, tau & 1, cr, ce, [&](int k) __attribute__((always_inline)) {
+                return *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * rs_unit_tq(st + 256 * k));
+            });
         };
         const int tile_b = cb * NT;
         publish(tile_b & 1);
         issue_b(tile_b * TT, std::integral_constant<int, 0>{});
-        stage_b(std::integral_constant<int, 0>{}, tile_b & 1);
+        stage_b_global(std::integral_constant<int, 0>{}, tile_b);
         if constexpr (kDepth == 2) issue_b(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
         __syncthreads();
         float csn = 0.f, cpn = 0.f;
@@ -603,7 +662,25 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                     cpn = cp_row[kn];
                 }
                 issue_b(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
-                // state update: h^T[n][p] (+)= sum_j B^T[n][j] X~[j][p]
+                // the next tile's B^T into the other slot first (it was last read a
+                // tile ago), while the output waves read their operands
+                {
+                    constexpr int SxN = kDepth == 2 ? ((I + 1) & 1) : 0;
+                    if constexpr (kCsLds) {
+                        // (after the last tile this stages data nobody reads)
+                        const float *CSn = (I + 1 < NT) ? CSL : CSB + ((c + 1 - cb) & 1) * 2 * Q;
+                        const int tn = ((I + 1) % NT) * TT;
+                        const float cr = (I + 1 < NT) ? CSn[tn - 1] : 0.f;
+                        stage_b(std::integral_constant<int, SxN>{}, (tau + 1) & 1, cr, CSn[tn + TT - 1],
+                                [&](int k) __attribute__((always_inline)) {
+                                    return *reinterpret_cast<const f32x4 *>(CSn + Q + tn + 4 * rs_unit_tq(st + 256 * k));
+                                });
+                    } else {
+                        stage_b_global(std::integral_constant<int, SxN>{}, min(tau + 1, last_tile));
+                    }
+                }
+                // state update: factored tiles h <- dec (h + B^T X~), the others
+                // h <- dec h + Bw^T X
                 const float cs_ref = (I > 0) ? CSL[tile0 - 1] : 0.f;
                 const float cs_end = CSL[tile0 + TT - 1];
                 const bool fd = (cs_ref - cs_end <= kRsFDMax);
@@ -641,11 +718,10 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                         CSN[Q + st] = cpn;
                     }
                 }
-                // (after the last tile this stages a reload into slots nobody reads)
-                stage_b(std::integral_constant<int, kDepth == 2 ? ((I + 1) & 1) : 0>{}, (tau + 1) & 1);
                 __syncthreads();
             });
         }
+        __syncthreads();  // pairs with the output waves' barrier before the last rows leave
         if (out_mat) {
 #pragma unroll
             for (int nb = 0; nb < NBH; ++nb)
@@ -676,8 +752,9 @@ static ssd_status run_walk_rs(const FwdArgs &f, hipStream_t s) {
         wa.cu = f.cu; wa.total = (int)f.total; wa.z = f.z;
         wa.conv_w = nullptr; wa.conv_b = nullptr;
         const int64_t heads = f.batch * f.H * f.ns;
-        const hipError_t e = f.z ? launch(k_walk_rs<Q, PW, N, true>, dim3((unsigned)(heads * f.S)), dim3(512), s, wa)
-                                 : launch(k_walk_rs<Q, PW, N, false>, dim3((unsigned)(heads * f.S)), dim3(512), s, wa);
+        const dim3 grid((unsigned)(heads * f.S));
+        const hipError_t e = f.z ? launch(k_walk_rs<Q, PW, N, true>, grid, dim3(512), s, wa)
+                                 : launch(k_walk_rs<Q, PW, N, false>, grid, dim3(512), s, wa);
         return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }
 }
