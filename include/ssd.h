@@ -27,7 +27,8 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers are DEVICE pointers owned by the caller. The library allocates
- *    nothing and keeps no pointer after a call returns. All tensors are
+ *    nothing and keeps no pointer after a call returns (one exception,
+ *    ssd_chunk_scan_fwd_noalloc, uses a static device buffer of its own). All tensors are
  *    contiguous, row-major, 16-byte aligned. Outputs must not alias inputs.
  *  - A and D are float32 of shape (H). States are always float32.
  *    X, dt, B, C and Y (x, y in the step) share one storage type `dtype`:
@@ -40,7 +41,8 @@
  *    a failed check returns its code and touches nothing. A HIP launch
  *    error is returned as SSD_ERR_HIP; faults during execution surface at
  *    the caller's next synchronisation. No call aborts, throws or prints.
- *  - Calls are stateless and thread-safe.
+ *  - Calls are stateless and thread-safe (ssd_chunk_scan_fwd_noalloc: see
+ *    there).
  */
 #ifndef SSD_H_
 #define SSD_H_
@@ -59,7 +61,9 @@ typedef enum {
     SSD_ERR_UNSUPPORTED = 3, /* a valid shape this build has no kernel for (see below) */
     SSD_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than the query returns */
     SSD_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned */
-    SSD_ERR_HIP = 6          /* the HIP runtime reported an error at launch */
+    SSD_ERR_HIP = 6,         /* the HIP runtime reported an error at launch */
+    SSD_ERR_TOO_LARGE = 7    /* ssd_chunk_scan_fwd_noalloc: the problem needs more workspace
+                                than SSD_NOALLOC_SCRATCH_BYTES */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -308,6 +312,33 @@ ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, con
                               int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                               int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/*
+ * ssd_chunk_scan_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. The workspace lives in a static device
+ * array of SSD_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on each
+ * GPU it runs on until the process ends; the call allocates nothing (no
+ * hipMalloc, no allocating library routine). The caller still passes every
+ * input and output. Arguments, shapes, alignment, results and errors are
+ * those of ssd_chunk_scan_fwd; a problem whose workspace
+ * (ssd_chunk_scan_fwd_workspace_bytes) exceeds the array returns
+ * SSD_ERR_TOO_LARGE before anything is enqueued. It runs on the current
+ * device, which `stream` must belong to.
+ *
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (on different streams, or from different threads onto different
+ * streams) race and give wrong results; calls enqueued on one stream, or
+ * ordered by events, are safe. Nothing in the array needs to start at zero:
+ * each call writes every byte of it that it later reads.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *X, const void *dt, const float *A, const void *B,
+                                      const void *C, const float *D, int64_t chunk, void *Y,
+                                      float *final_state, int64_t batch, int64_t seqlen,
+                                      int64_t nheads, int64_t headdim, int64_t dstate,
+                                      int64_t ngroups, ssd_dtype dtype, void *stream);
 
 #ifdef __cplusplus
 }

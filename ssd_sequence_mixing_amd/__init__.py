@@ -17,7 +17,8 @@ __all__ = [
     "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk_scan_fwd", "ssd_chunk_scan_prepare",
     "ssd_chunk_scan_walk", "ssd_step", "ssd_chunk_scan_varlen_workspace_bytes",
     "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_gated", "ssd_step_gated",
-    "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused", "EXPORTS",
+    "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused",
+    "ssd_chunk_scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -31,7 +32,10 @@ EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk
            "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step",
            "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen",
            "ssd_chunk_scan_fwd_gated", "ssd_step_gated", "ssd_chunk_scan_bwd_workspace_bytes",
-           "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused")
+           "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused", "ssd_chunk_scan_fwd_noalloc")
+
+# SSD_NOALLOC_SCRATCH_BYTES: the static workspace of ssd_chunk_scan_fwd_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _V = ctypes.c_void_p
 _I = ctypes.c_int64
@@ -110,6 +114,8 @@ def load():
     lib.ssd_chunk_scan_fwd_fused.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_fused.argtypes = ([_V] * 5 + [ctypes.c_int] + [_V] * 5 + [_I, _V, _V] + [_I] * 6 +
                                              [ctypes.c_int, _V, ctypes.c_size_t, _V])
+    lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [_V] * 6 + [_I, _V, _V] + [_I] * 6 + [ctypes.c_int, _V]
     lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ssd_chunk_scan_bwd_workspace_bytes.argtypes = [_I] * 7 + [ctypes.c_int]
     lib.ssd_chunk_scan_bwd.restype = ctypes.c_int
@@ -183,6 +189,22 @@ def ssd_chunk_scan_fwd(X, dt, A, B, C, D, chunk: int, Y=None, final_state=None, 
                                 _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd")
+    return Y, final_state
+
+
+def ssd_chunk_scan_fwd_noalloc(X, dt, A, B, C, D, chunk: int, Y, final_state=None, *, stream=None):
+    """ssd_chunk_scan_fwd with the library's static workspace: the C call
+    allocates nothing, so the caller passes Y (and final_state, or None to
+    skip it) already allocated. Calls that may overlap on one GPU race on the
+    shared workspace. Returns (Y, final_state)."""
+    lib = load()
+    bsz, T, H, P = X.shape
+    G, N = B.shape[2], B.shape[3]
+    st = lib.ssd_chunk_scan_fwd_noalloc(_ptr(X), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), chunk,
+                                        _ptr(Y), _ptr(final_state), bsz, T, H, P, N, G, _dtype_code(X),
+                                        _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_chunk_scan_fwd_noalloc")
     return Y, final_state
 
 

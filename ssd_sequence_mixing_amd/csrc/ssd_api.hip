@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "ssd_common.h"
 #include "ssd_internal.h"
@@ -160,6 +161,73 @@ __global__ void k_zero(float *p, int64_t n) {
     if (i < n) p[i] = 0.f;
 }
 
+// The forward's workspace for callers that cannot allocate
+// (ssd_chunk_scan_fwd_noalloc): one array per GPU, loaded with the library's
+// code and held until the process ends. Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol); it
+// passes the device address hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each GPU, once looked up
+
+// The address of the current GPU's copy of `scratch`, looked up once per GPU.
+ssd_status scratch_of_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
+
+// The forward with every option (ssd_chunk_scan_fwd_fused's arguments). With
+// use_scratch the workspace arguments are ignored and the current GPU's
+// `scratch` serves instead; problems needing more return SSD_ERR_TOO_LARGE.
+ssd_status fwd_impl(const void *X, const float *conv_w, const float *conv_b, const void *dt,
+                    const float *dt_bias, int dt_softplus, const float *A, const void *B, const void *C,
+                    const float *D, const void *z, int64_t chunk, void *Y, float *final_state, int64_t batch,
+                    int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                    ssd_dtype dtype, void *workspace, size_t workspace_bytes, bool use_scratch, void *stream) {
+    if (dt_softplus < 0 || dt_softplus > 2) return SSD_ERR_UNSUPPORTED;
+    if (!conv_w && conv_b) return SSD_ERR_NULL;
+    if (!aligned16(conv_w) || ((uintptr_t)conv_b & 3u) != 0) return SSD_ERR_ALIGN;
+    const bool empty = (batch == 0 || seqlen == 0);
+    // an empty problem reads no input, so its input pointers may be NULL
+    if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
+    FwdLayout lay;
+    ssd_status st =
+        check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
+    if (st != SSD_OK) return st;
+    if (conv_w && !ssd::walk_conv_fits(dtype, chunk, headdim / lay.plan.ns, dstate)) return SSD_ERR_UNSUPPORTED;
+    if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(D) || !aligned16(Y) || !aligned16(final_state) || !aligned16(dt_bias) || !aligned16(z))
+        return SSD_ERR_ALIGN;
+    if (use_scratch) {
+        if ((size_t)lay.total > (size_t)SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_TOO_LARGE;
+        workspace = nullptr;
+        workspace_bytes = SSD_NOALLOC_SCRATCH_BYTES;
+        if (lay.total > 0 && (st = scratch_of_current_device(&workspace)) != SSD_OK) return st;
+    }
+    if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (batch == 0) return SSD_OK;
+    if (seqlen == 0)
+        return empty_final_state(final_state, nullptr, batch * nheads * headdim * dstate, s);
+    FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
+                          workspace);
+    f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y; f.final_state = final_state;
+    f.dt_bias = dt_bias; f.softplus = dt_softplus; f.z = z;
+    f.conv_w = conv_w; f.conv_b = conv_b;
+    if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
+    return ssd::launch_walk(f, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,6 +241,8 @@ const char *ssd_status_string(ssd_status s) {
         case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
         case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN: pointer not 16-byte aligned";
         case SSD_ERR_HIP: return "SSD_ERR_HIP: HIP runtime error at launch";
+        case SSD_ERR_TOO_LARGE:
+            return "SSD_ERR_TOO_LARGE: the problem needs more workspace than the library's static scratch holds";
     }
     return "SSD_ERR_UNKNOWN";
 }
@@ -258,32 +328,17 @@ ssd_status ssd_chunk_scan_fwd_fused(const void *X, const float *conv_w, const fl
                                     float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
                                     int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
                                     void *workspace, size_t workspace_bytes, void *stream) {
-    if (dt_softplus < 0 || dt_softplus > 2) return SSD_ERR_UNSUPPORTED;
-    if (!conv_w && conv_b) return SSD_ERR_NULL;
-    if (!aligned16(conv_w) || ((uintptr_t)conv_b & 3u) != 0) return SSD_ERR_ALIGN;
-    const bool empty = (batch == 0 || seqlen == 0);
-    // an empty problem reads no input, so its input pointers may be NULL
-    if (!empty && (!X || !dt || !A || !B || !C || !D || !Y)) return SSD_ERR_NULL;
-    FwdLayout lay;
-    ssd_status st =
-        check_fwd_shape(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, (int)dtype, &lay);
-    if (st != SSD_OK) return st;
-    if (conv_w && !ssd::walk_conv_fits(dtype, chunk, headdim / lay.plan.ns, dstate)) return SSD_ERR_UNSUPPORTED;
-    if (!aligned16(X) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
-        !aligned16(D) || !aligned16(Y) || !aligned16(final_state) || !aligned16(dt_bias) || !aligned16(z))
-        return SSD_ERR_ALIGN;
-    if ((st = check_workspace(lay, workspace, workspace_bytes)) != SSD_OK) return st;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (batch == 0) return SSD_OK;
-    if (seqlen == 0)
-        return empty_final_state(final_state, nullptr, batch * nheads * headdim * dstate, s);
-    FwdArgs f = make_args(lay, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype,
-                          workspace);
-    f.X = X; f.dt = dt; f.A = A; f.B = B; f.C = C; f.D = D; f.Y = Y; f.final_state = final_state;
-    f.dt_bias = dt_bias; f.softplus = dt_softplus; f.z = z;
-    f.conv_w = conv_w; f.conv_b = conv_b;
-    if ((st = ssd::launch_prepare(f, s)) != SSD_OK) return st;
-    return ssd::launch_walk(f, s);
+    return fwd_impl(X, conv_w, conv_b, dt, dt_bias, dt_softplus, A, B, C, D, z, chunk, Y, final_state, batch,
+                    seqlen, nheads, headdim, dstate, ngroups, dtype, workspace, workspace_bytes, false, stream);
+}
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *X, const void *dt, const float *A, const void *B,
+                                      const void *C, const float *D, int64_t chunk, void *Y,
+                                      float *final_state, int64_t batch, int64_t seqlen, int64_t nheads,
+                                      int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype,
+                                      void *stream) {
+    return fwd_impl(X, nullptr, nullptr, dt, nullptr, 0, A, B, C, D, nullptr, chunk, Y, final_state, batch,
+                    seqlen, nheads, headdim, dstate, ngroups, dtype, nullptr, 0, true, stream);
 }
 
 size_t ssd_chunk_scan_varlen_workspace_bytes(int64_t num_seqs, int64_t max_seqlen, int64_t nheads,

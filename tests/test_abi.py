@@ -17,7 +17,7 @@ import ssd_sequence_mixing_amd as ssd
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ssd.h")
 
-OK, ENULL, ESHAPE, EUNSUP, EWS, EALIGN, EHIP = range(7)
+OK, ENULL, ESHAPE, EUNSUP, EWS, EALIGN, EHIP, ETOOLARGE = range(8)
 F32, BF16 = ssd.SSD_F32, ssd.SSD_BF16
 P16 = 0x10000  # a fake, 16-byte-aligned device address
 
@@ -49,7 +49,7 @@ def test_library_exports_with_nm():
 
 
 def test_status_strings():
-    for code in range(7):
+    for code in range(8):
         s = ssd.ssd_status_string(code)
         assert s.startswith("SSD_OK" if code == 0 else "SSD_ERR")
     assert "UNKNOWN" in ssd.ssd_status_string(99)
@@ -115,6 +115,50 @@ def test_fwd_workspace_checks():
 
 def test_fwd_empty_batch_returns_ok_without_work():
     assert fwd(batch=0, wsp=None, wsb=0) == OK
+
+
+def fwd_noalloc(X=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, chunk=256, Y=P16, fin=P16, batch=4, T=2048,
+                H=64, P=64, N=128, G=1, dtype=BF16, stream=None):
+    return ssd.raw_call("ssd_chunk_scan_fwd_noalloc", X, dt, A, B, C, D, chunk, Y, fin, batch, T, H, P, N,
+                        G, dtype, stream)
+
+
+@pytest.mark.parametrize("field", ["X", "dt", "A", "B", "C", "D", "Y"])
+def test_fwd_noalloc_null(field):
+    assert fwd_noalloc(**{field: None}) == ENULL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ESHAPE), (dict(H=64, G=3), ESHAPE), (dict(chunk=32), EUNSUP), (dict(P=48), EUNSUP),
+    (dict(dtype=F32, P=128, N=256, chunk=256), EUNSUP),
+])
+def test_fwd_noalloc_shape_checks(kw, code):
+    assert fwd_noalloc(**kw) == code
+
+
+@pytest.mark.parametrize("field", ["X", "B", "Y", "fin"])
+def test_fwd_noalloc_alignment(field):
+    assert fwd_noalloc(**{field: P16 + 4}) == EALIGN
+
+
+def test_fwd_noalloc_rejects_problems_beyond_its_scratch():
+    limit = ssd.NOALLOC_SCRATCH_BYTES
+    # the 16K-token, N = 256 workload fits (36 MiB); 8 such sequences do not
+    assert ws(1, 16384, 64, 64, 256, 8, 256, BF16) <= limit
+    assert ws(8, 16384, 64, 64, 256, 8, 256, BF16) > limit
+    assert fwd_noalloc(batch=8, T=16384, N=256, G=8) == ETOOLARGE
+    # the workspace query decides: a shape just past the limit is refused
+    T = 2048
+    while ws(4, T, 64, 64, 128, 1, 256, BF16) <= limit:
+        T += 2048
+    assert fwd_noalloc(T=T) == ETOOLARGE
+    assert fwd_noalloc(batch=0) == OK  # nothing to do, nothing looked up
+
+
+def test_noalloc_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ssd.NOALLOC_SCRATCH_BYTES
 
 
 def step(state=P16, x=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, y=P16, batch=256, H=64, P=64,
