@@ -8,15 +8,19 @@ i.e. ssd_chunk_scan_fwd) over one batch of the 1.3B-layer workload
 (batch 4, T 2048, 64 heads, P 64, N 128, one group, chunk 256, bf16
 storage), with inputs resident in HBM. Three independent input / output /
 workspace sets rotate (444 MB together, more than the 256 MB Infinity Cache),
-so no step reads the previous step's data from the cache. The decode step is
-timed after the forward: 1000 ssd_step calls on the 256 x 64 x 64 x 128 fp32
-state, then 50 forwards with the fused layer prologue / epilogue
-(ssd_chunk_scan_fwd_fused) and 20 backward passes (ssd_chunk_scan_bwd) of
-the forward workload, reported beside the forward. Prints one JSON line.
+so no step reads the previous step's data from the cache. The K timed steps
+run back to back between two events; events at the boundaries of R equal
+sub-blocks give the median per-step time beside the mean. The 125M-layer and
+16K-token shapes are timed the same way (fewer steps) and reported under
+"shapes". The decode step is timed after the forward: 1000 ssd_step calls on
+the 256 x 64 x 64 x 128 fp32 state, then 50 forwards with the fused layer
+prologue / epilogue (ssd_chunk_scan_fwd_fused) and 20 backward passes
+(ssd_chunk_scan_bwd) of the forward workload, reported beside the forward.
+Prints one JSON line.
 
 The oracle is timed beside the GPU on a bounded sample of the same workload
-(whole batch elements, about ten seconds of host work) for the cpu_baseline
-field.
+(whole batch elements, about ten seconds of host work on all host threads,
+and one batch element on a single thread) for the cpu_baseline field.
 """
 from __future__ import annotations
 
@@ -36,8 +40,12 @@ METRIC = "SSD fwd tokens/s + % bf16 MFMA roofline (h=64,P=64,N=128,T=2048); deco
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "walk_l1p3b_traffic.txt")
+# the walk of the bf16 shapes with P 64 and N <= 128 (k_walk_rs)
+WALK_KERNEL = "k_walk_rs"
 WALK_SOURCES = [os.path.join(ROOT, "ssd_sequence_mixing_amd", "csrc", f)
-                for f in ("ssd_fwd.hip", "ssd_common.h")]
+                for f in ("ssd_walk_rs.hip", "ssd_common.h")]
+WORKLOAD_NAMES = {"l1p3b_bf16": "ssd_fwd 1.3B-layer shape", "l125m_bf16": "ssd_fwd 125M-layer shape",
+                  "long16k_bf16": "ssd_fwd 16K-token shape"}
 
 
 def fwd_accounting(cfg, chunk):
@@ -95,6 +103,70 @@ def read_traffic():
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+_SINGLE_THREAD_SNIPPET = """
+import json, sys, time
+sys.path.insert(0, {root!r})
+import numpy as np
+import ssd_inputs as si
+import oracle
+cfg = si.CONFIGS[{workload!r}]
+inp = si.make_fwd_inputs(cfg)
+args = [np.ascontiguousarray(inp[k][:1], dtype=np.float64) for k in ("X32", "dt32", "B32", "C32")]
+t0 = time.perf_counter()
+oracle.fwd(args[0], args[1], inp["A"], args[2], args[3], inp["D"], cfg.ngroups)
+dt = time.perf_counter() - t0
+print(json.dumps({{"seconds": dt, "tokens": cfg.seqlen, "threads": oracle.num_threads()}}))
+"""
+
+
+def cpu_single_thread(workload: str):
+    """The oracle on one batch element of the workload with one OpenMP thread,
+    in a child process (the thread count is fixed when the oracle loads)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        p = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_SNIPPET.format(root=ROOT, workload=workload)],
+                           env=env, capture_output=True, text=True, timeout=120)
+        r = json.loads(p.stdout.strip().splitlines()[-1])
+    except Exception as e:  # noqa: BLE001  (reported, not fatal)
+        return {"error": str(e)[:200]}
+    return {"value": r["tokens"] / r["seconds"], "unit": "tokens/s", "cores": r["threads"],
+            "sample": f"one sequence of the workload ({r['tokens']} tokens) on one thread, "
+                      f"{r['seconds']:.2f} s wall"}
+
+
+def device_info(torch):
+    """GPU model, ROCm / HIP versions and the clocks rocm-smi reports."""
+    import subprocess
+    prop = torch.cuda.get_device_properties(0)
+    info = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
+            "compute_units": prop.multi_processor_count, "hbm_bytes": prop.total_memory,
+            "hip_runtime": torch.version.hip}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    try:
+        p = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
+        info["clocks"] = [l.strip() for l in p.stdout.splitlines()
+                          if ("sclk" in l or "mclk" in l or "fclk" in l) and "GPU[" in l][:8]
+    except Exception:  # noqa: BLE001  (optional)
+        info["clocks"] = None
+    return info
+
+
 def cpu_baseline(inp, cfg, budget_s=10.0, max_passes=200):
     """Oracle throughput on this host: whole batch elements of the workload, one
     at a time, repeated over the batch until about budget_s of wall time."""
@@ -112,7 +184,7 @@ def cpu_baseline(inp, cfg, budget_s=10.0, max_passes=200):
         done_tokens += cfg.seqlen
         used += 1
     return {"value": done_tokens / elapsed, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{used} single-sequence forwards cycling over the {cfg.batch} batch elements of the "
                       f"same workload ({done_tokens} tokens x {cfg.nheads} heads), fp64 sequential "
                       f"recurrence, {elapsed:.2f} s wall"}
@@ -134,6 +206,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the 125M-layer and 16K-token shapes")
+    ap.add_argument("--repeats", type=int, default=10,
+                    help="sub-blocks of the timed steps for the median per-step time")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="for counter runs: 5 walk launches, then 5 element-wise negations of a "
@@ -164,28 +239,87 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    def make_sets(cfg, chunk, nsets):
+        code = ssd.SSD_BF16 if cfg.dtype == "bf16" else ssd.SSD_F32
+        Bz, T, H, P, N, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+        need = ssd.ssd_chunk_scan_fwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
+        sets, first_inp = [], None
+        for k in range(nsets):
+            inp = si.make_fwd_inputs(dataclasses.replace(cfg, seed=cfg.seed + 1000 * k))
+            if k == 0:
+                first_inp = inp
+            t = {n: up(inp[n]) for n in ("X", "dt", "B", "C", "A", "D")}
+            t["Y"] = torch.empty_like(t["X"])
+            t["F"] = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dev)
+            t["W"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            p = {n: v.data_ptr() for n, v in t.items()}
+            t["prep"] = (p["dt"], p["A"], p["B"], p["C"], chunk, Bz, T, H, P, N, G, code, p["W"], need, sptr)
+            t["walk"] = (p["X"], p["B"], p["C"], p["D"], None, chunk, p["Y"], p["F"], Bz, T, H, P, N, G, code,
+                         p["W"], need, sptr)
+            sets.append(t)
+        return sets, first_inp
+
+    def step(t):
+        st = lib.ssd_chunk_scan_prepare(*t["prep"])
+        st = st or lib.ssd_chunk_scan_walk(*t["walk"])
+        if st:
+            raise ssd.SSDError(st, "forward")
+
+    def time_forward(sets, K, warmup, R):
+        """K whole steps between two events, with events only at the boundaries
+        of R equal sub-blocks (an event between two kernels adds a few us of gap,
+        so none sits between the launches of a sub-block); then the same K steps
+        with an event around each kernel, for the per-kernel durations."""
+        for i in range(warmup):
+            step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        R = max(1, min(R, K))
+        bounds = [round(K * j / R) for j in range(R + 1)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+        torch.cuda.synchronize()
+        t_wall0 = time.perf_counter()
+        evs[0].record(stream)
+        for j in range(R):
+            for i in range(bounds[j], bounds[j + 1]):
+                step(sets[i % len(sets)])
+            evs[j + 1].record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t_wall0
+        ms_total = evs[0].elapsed_time(evs[R])
+        per_block = [evs[j].elapsed_time(evs[j + 1]) / (bounds[j + 1] - bounds[j]) for j in range(R)]
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for i in range(K):
+            t, e = sets[i % len(sets)], kev[i]
+            e[0].record(stream)
+            if lib.ssd_chunk_scan_prepare(*t["prep"]):
+                raise RuntimeError("prepare failed")
+            e[1].record(stream)
+            if lib.ssd_chunk_scan_walk(*t["walk"]):
+                raise RuntimeError("walk failed")
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        return {"ms_step": ms_total / K, "median_ms_step": float(np.median(per_block)),
+                "ms_step_blocks": [float(v) for v in per_block], "wall_s": wall_s,
+                "ms_prepare": float(np.mean([e[0].elapsed_time(e[1]) for e in kev])),
+                "ms_walk": float(np.mean([e[1].elapsed_time(e[2]) for e in kev]))}
+
+    def shape_summary(cfg, chunk, tm):
+        acc = fwd_accounting(cfg, chunk)
+        t_s = tm["ms_step"] / 1e3
+        roof_time = max(acc["flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12), acc["bytes"] / (HBM_PEAK_GBS * 1e9))
+        return acc, {"tokens_per_s": acc["tokens"] / t_s, "ms_per_step": tm["ms_step"],
+                     "median_ms_per_step": tm["median_ms_step"], "ms_prepare": tm["ms_prepare"],
+                     "ms_walk": tm["ms_walk"], "roof_frac": roof_time / t_s,
+                     "walk_hbm_frac": acc["walk_bytes"] / (tm["ms_walk"] / 1e3) / 1e9 / HBM_PEAK_GBS}
+
     cfg = si.CONFIGS[args.workload]
     chunk = args.chunk or cfg.chunk
     code = ssd.SSD_BF16 if cfg.dtype == "bf16" else ssd.SSD_F32
     Bz, T, H, P, N, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
-    need = ssd.ssd_chunk_scan_fwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-
-    sets, first_inp = [], None
-    for k in range(args.sets):
-        inp = si.make_fwd_inputs(dataclasses.replace(cfg, seed=cfg.seed + 1000 * k))
-        if k == 0:
-            first_inp = inp
-        t = {n: up(inp[n]) for n in ("X", "dt", "B", "C", "A", "D")}
-        t["Y"] = torch.empty_like(t["X"])
-        t["F"] = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dev)
-        t["W"] = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-        p = {n: v.data_ptr() for n, v in t.items()}
-        t["prep"] = (p["dt"], p["A"], p["B"], p["C"], chunk, Bz, T, H, P, N, G, code, p["W"], need, sptr)
-        t["walk"] = (p["X"], p["B"], p["C"], p["D"], None, chunk, p["Y"], p["F"], Bz, T, H, P, N, G, code,
-                     p["W"], need, sptr)
-        sets.append(t)
+    sets, first_inp = make_sets(cfg, chunk, args.sets)
 
     if args.traffic_probe:
         for i in range(5):
@@ -204,47 +338,9 @@ def main():
                           "walk_algorithmic_bytes": fwd_accounting(cfg, chunk)["walk_bytes"]}), flush=True)
         return
 
-    def step(t):
-        st = lib.ssd_chunk_scan_prepare(*t["prep"])
-        st = st or lib.ssd_chunk_scan_walk(*t["walk"])
-        if st:
-            raise ssd.SSDError(st, "forward")
-
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-
-    # Timed region: K whole steps, bracketed by two events and nothing between
-    # the launches (an event recorded between two kernels adds a few us of gap).
     K = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(K):
-        step(sets[i % len(sets)])
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall0
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / K
-
-    # Per-kernel durations: the same K steps again, with an event on the launch
-    # stream before and after each kernel.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for i in range(K):
-        t = sets[i % len(sets)]
-        e = evs[i]
-        e[0].record(stream)
-        if lib.ssd_chunk_scan_prepare(*t["prep"]):
-            raise RuntimeError("prepare failed")
-        e[1].record(stream)
-        if lib.ssd_chunk_scan_walk(*t["walk"]):
-            raise RuntimeError("walk failed")
-        e[2].record(stream)
-    torch.cuda.synchronize()
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    walk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    tm = time_forward(sets, K, args.warmup, args.repeats)
+    ms_step, prep_ms, walk_ms, wall_s = tm["ms_step"], tm["ms_prepare"], tm["ms_walk"], tm["wall_s"]
 
     acc = fwd_accounting(cfg, chunk)
     t_s = ms_step / 1e3
@@ -270,20 +366,39 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": {"l1p3b_bf16": "ssd_fwd 1.3B-layer shape", "l125m_bf16": "ssd_fwd 125M-layer shape",
-                                "long16k_bf16": "ssd_fwd 16K-token shape"}[args.workload],
+        "config": {"workload": WORKLOAD_NAMES[args.workload],
                    "batch": Bz, "seqlen": T, "nheads": H,
                    "headdim": P, "dstate": N, "ngroups": G, "chunk": chunk, "storage": cfg.dtype,
                    "rotating_sets": len(sets)},
-        "roofline": {"bound": "hbm", "kernel": "k_chunk_walk", "achieved": walk_gbs,
+        "roofline": {"bound": "hbm", "kernel": WALK_KERNEL, "achieved": walk_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": walk_gbs / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": acc["walk_bytes"],
                      "avg_launch_ms": walk_ms},
         "forward": {"ms_prepare": prep_ms, "ms_walk": walk_ms, "wall_s": wall_s,
+                    "median_ms_per_step": tm["median_ms_step"], "repeats": len(tm["ms_step_blocks"]),
+                    "ms_per_step_min": min(tm["ms_step_blocks"]), "ms_per_step_max": max(tm["ms_step_blocks"]),
                     "tflops": tflops, "mfma_frac": mfma_frac, "hbm_gbs": hbm_gbs, "hbm_frac": hbm_frac,
                     "roof_frac": roof_time / t_s, "algorithmic_flops": acc["flops"],
                     "algorithmic_bytes": acc["bytes"]},
+        "device": device_info(torch),
     }
+
+    if not args.no_shapes:
+        # the other two forward workloads, timed the same way with fewer steps
+        out["shapes"] = {}
+        for name, nsets in (("l125m_bf16", 3), ("long16k_bf16", 2)):
+            if name == args.workload:
+                continue
+            c2 = si.CONFIGS[name]
+            s2, _ = make_sets(c2, c2.chunk, nsets)
+            tm2 = time_forward(s2, max(10, K // 4), 5, args.repeats)
+            _, summ = shape_summary(c2, c2.chunk, tm2)
+            summ["workload"] = WORKLOAD_NAMES[name]
+            summ["config"] = {"batch": c2.batch, "seqlen": c2.seqlen, "nheads": c2.nheads, "headdim": c2.headdim,
+                              "dstate": c2.dstate, "ngroups": c2.ngroups, "chunk": c2.chunk}
+            out["shapes"][name] = summ
+            del s2
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         dc = si.DECODE
@@ -384,6 +499,7 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(first_inp, cfg)
+        out["cpu_baseline"]["single_thread"] = cpu_single_thread(args.workload)
     else:
         out["cpu_baseline"] = None
 

@@ -458,6 +458,7 @@ ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, con
     ssd::BwdArgs w = {};
     w.f = make_args(lay.fl, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, workspace);
     w.f.X = X; w.f.dt = dt; w.f.A = A; w.f.B = B; w.f.C = C; w.f.D = D; w.f.init = initial_state;
+    w.f.no_g = true;
     char *ws = static_cast<char *>(workspace) + 2 * lay.fl.cs_bytes + lay.fl.g_bytes + lay.fl.seg_bytes;
     w.Hst = ws; ws += lay.st_bytes;
     w.Est = ws; ws += lay.st_bytes;

@@ -119,35 +119,43 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
         for (int hl = 0; hl < kCumsumHeads; ++hl) tile[hl * LD + t] = v[hl];
     }
     __syncthreads();
-    constexpr int PER = Q / 64;  // tokens per lane
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int hl = w; hl < Hb; hl += 4) {
+    // Thread (head hl, segment sg) takes Q / 16 consecutive tokens: a serial
+    // prefix over them, then an exclusive scan of the 16 segment totals
+    // across the 16 lanes of the head, then 16-byte stores.
+    constexpr int SEG = Q / 16;
+    const int hl = threadIdx.x >> 4, sg = threadIdx.x & 15;
+    if (hl < Hb) {
         const int h = h0 + hl;
         const float a2 = A[h] * kLog2e;
-        float d[PER], s[PER];
+        float d[SEG], sv[SEG];
         float run = 0.f;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            d[k] = tile[hl * LD + lane * PER + k];
+        for (int k = 0; k < SEG; ++k) {
+            d[k] = tile[hl * LD + sg * SEG + k];
             run += d[k] * a2;
-            s[k] = run;
+            sv[k] = run;
         }
-        // exclusive scan of the per-lane sums across the wavefront
         float incl = run;
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float up = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += up;
+        for (int off = 1; off < 16; off <<= 1) {
+            const float up = __shfl_up(incl, off, 16);
+            if (sg >= off) incl += up;
         }
         const float excl = incl - run;
-        float *o = cs2 + ((size_t)b * H + h) * Tpad + t0 + lane * PER;
-        float *od = dtf + ((size_t)b * H + h) * Tpad + t0 + lane * PER;
+        float *o = cs2 + ((size_t)b * H + h) * Tpad + t0 + sg * SEG;
+        float *od = dtf + ((size_t)b * H + h) * Tpad + t0 + sg * SEG;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            o[k] = s[k] + excl;
-            // log2(0) = -inf, so a zero step (or a padded token) gets cs' = +inf
-            // and every factor exp2(x - cs') built from it is exactly 0
-            od[k] = s[k] + excl - __builtin_amdgcn_logf(d[k]);
+        for (int k = 0; k < SEG; k += 4) {
+            f32x4 v, w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = sv[k + e] + excl;
+                // log2(0) = -inf, so a zero step (or a padded token) gets cs' = +inf
+                // and every factor exp2(x - cs') built from it is exactly 0
+                w[e] = v[e] - __builtin_amdgcn_logf(d[k + e]);
+            }
+            *reinterpret_cast<f32x4 *>(o + k) = v;
+            *reinterpret_cast<f32x4 *>(od + k) = w;
         }
     }
 }
@@ -1086,7 +1094,8 @@ static ssd_status run_prepare(const FwdArgs &f, hipStream_t s) {
     a.dt_bias = f.dt_bias; a.softplus = f.softplus;
     a.ntiles = (int)(f.Tpad / TT);
     a.g_bytes = (uint32_t)f.g_bytes;
-    a.cb_blocks = (int)(f.batch * a.ntiles * f.G * (TT / 64));
+    // the backward reads no C B^T tiles
+    a.cb_blocks = f.no_g ? 0 : (int)(f.batch * a.ntiles * f.G * (TT / 64));
     const int64_t hblocks = (f.H + kCumsumHeads - 1) / kCumsumHeads;
     const int64_t blocks = a.cb_blocks + f.batch * hblocks * f.nC;
     return launch(k_prepare<TI, Q, N, TT>, dim3((unsigned)blocks), dim3(256), s, a) == hipSuccess

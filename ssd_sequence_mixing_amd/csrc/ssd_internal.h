@@ -30,6 +30,7 @@ struct FwdArgs {
     int ns, tt;                // walk plan: work-groups per head, tile tokens
     int S, cps;                // walk plan: sequence segments, chunks per segment
     float *seg;                // workspace: (batch, H, S - 1, P, N) fp32 segment states
+    bool no_g;                 // the caller reads no C B^T tiles (the backward): prepare skips them
 };
 
 // How the walk covers a shape: ns work-groups per head (P / ns columns each)
@@ -137,7 +138,8 @@ bool bwd_supported(ssd_dtype dt, int64_t P, int64_t N);
 // The backward launches (after launch_prepare on the same FwdArgs).
 ssd_status launch_bwd(const BwdArgs &w, hipStream_t s);
 
-// Phase 1: chunk-local log-decay prefix sums and C B^T tiles into the workspace.
+// Phase 1: chunk-local log-decay prefix sums and (unless f.no_g) C B^T tiles
+// into the workspace.
 ssd_status launch_prepare(const FwdArgs &f, hipStream_t s);
 // Whether the walk with the fused input convolution fits LDS for a column slice.
 bool walk_conv_fits(ssd_dtype dt, int64_t Q, int64_t PW, int64_t N);
