@@ -86,10 +86,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 // The step-size prologue of a Mamba-2 layer, optionally fused into the core.
 // mode 0: dt = raw + bias; 1: dt = softplus(raw + bias); 2: dt = softplus(raw)
 // + bias (the bias after the softplus, as the Mamba explainer page's
-// training-stability notes write it). softplus(x) = log(1 + e^x), with log1p
-// for accuracy at large negative x and x itself above 20, where e^{-x} is
-// below fp32 resolution.
-__device__ __forceinline__ float softplus_f32(float x) { return x > 20.f ? x : log1pf(expf(x)); }
+// training-stability notes write it). softplus(x) = log(1 + e^x) = log1p(u),
+// u = e^x from the hardware's 2^x: for u < 1/32 the series u - u^2/2 + u^3/3
+// - u^4/4 + u^5/5 (truncation below u^5/6 < 2e-9 relative), else ln 2 log2(1 + u)
+// with the hardware's log2 (rounding 1 + u costs under 3e-6 relative there);
+// x itself above 20, where e^{-x} is below fp32 resolution.
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float softplus_f32(float x) {
+    if (x > 20.f) return x;
+    const float u = __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+    if (u < 0.03125f) return u * (1.f - u * (0.5f - u * (1.f / 3.f - u * (0.25f - u * 0.2f))));
+    return kLn2 * __builtin_amdgcn_logf(1.f + u);
+}
 __device__ __forceinline__ float dt_prologue(float raw, float bias, int mode) {
     if (mode == 1) return softplus_f32(raw + bias);
     if (mode == 2) return softplus_f32(raw) + bias;

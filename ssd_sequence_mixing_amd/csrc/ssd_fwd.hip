@@ -1131,7 +1131,7 @@ static ssd_status run_walk_c(const FwdArgs &f, hipStream_t s) {
                                   (int)f.nC, (int)f.Q, (int)f.Tpad) != hipSuccess)
                 return SSD_ERR_HIP;
         }
-        if (!kConv && walk_rs_supported(f)) return launch_walk_rs(f, s);
+        if (walk_rs_supported(f)) return launch_walk_rs(f, s);
         wa.SL = f.S;
         return launch(k_chunk_walk<TI, Q, PW, N, TT, false, kConv>, dim3((unsigned)(heads * f.S)), dim3(512), s,
                       wa) == hipSuccess

@@ -147,9 +147,9 @@ bool walk_conv_fits(ssd_dtype dt, int64_t Q, int64_t PW, int64_t N);
 ssd_status launch_walk(const FwdArgs &f, hipStream_t s);
 // The walk with the fused input convolution (f.conv_w set; ssd_walk_conv.hip).
 ssd_status launch_walk_conv(const FwdArgs &f, hipStream_t s);
-// The walk with the state kept in the math wavefronts' registers
-// (ssd_walk_rs.hip): bf16 storage, no input convolution, 64-token tiles,
-// column slices of 32 or 64 and N of 64 or 128.
+// The walk with the state kept in the wavefronts that update it
+// (ssd_walk_rs.hip): bf16 storage, 64-token tiles, column slices of 32 or 64
+// and N of 64 or 128, with or without the gate and the input convolution.
 bool walk_rs_supported(const FwdArgs &f);
 ssd_status launch_walk_rs(const FwdArgs &f, hipStream_t s);
 // One recurrent decode step.

@@ -16,9 +16,11 @@
 //   output waves 0-3 form the transposed output Y^T[p in half b][i] for the
 //     tokens i of half a: state -> output from the published state (both n
 //     halves of its columns), the diagonal block from C B^T and the weighted
-//     X, the skip term and the gate; the output goes through LDS and leaves
-//     as whole rows during the next tile. They also stage, for the next
-//     tile, the C rows (whole lines, into LDS) and X weighted by its decay
+//     X, and the skip term; the output goes through LDS and leaves as whole
+//     rows during the next tile, where the gate y SiLU(z) is applied with z
+//     read in the same row pieces. They also stage, for the next tile, the C
+//     rows (whole lines, into LDS), the X rows (after the layer's causal
+//     convolution and SiLU when it is fused in) and X weighted by its decay
 //     factors, written token-major (X^T) for the two products whose
 //     contraction runs over tokens.
 // Each SIMD runs one wavefront of each role; one barrier per tile.
@@ -139,9 +141,16 @@ __device__ __forceinline__ float bits_f32(uint32_t v) { return __builtin_bit_cas
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// The output gate y SiLU(z) = y z / (1 + e^-z) with the hardware's 2^x and
+// reciprocal (each within about 1 ulp in fp32; the result is rounded to bf16):
+// 4 instructions instead of a full-precision exp and divide.
+__device__ __forceinline__ float rs_gate(float y, float z) {
+    return y * z * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * z));
+}
+
 }  // namespace
 
-template <int Q, int PW, int N, bool kGate>
+template <int Q, int PW, int N, bool kGate, bool kConv>
 __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
     using Tr = Traits<bf16>;
     using frag = bf16x8;
@@ -228,18 +237,14 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         // columns of its token per pair of p-blocks: column offset pbase + 32 q.
         constexpr int NPQ = (PBH + 1) / 2;
         const int pbase = (PBH >= 2) ? 16 * (kg & 1) + 8 * (kg >> 1) : 4 * kg;
-        uint32_t vgo[IB], vy[IB][NPQ];
+        uint32_t vgo[IB];
 #pragma unroll
         for (int ib = 0; ib < IB; ++ib) {
             const int il = 32 * ah + 16 * ib + r;  // tile-local token of this lane's column
             vgo[ib] = (uint32_t)((il * TT + 8 * kg) * 2);
-#pragma unroll
-            for (int q = 0; q < NPQ; ++q)
-                vy[ib][q] = (uint32_t)il * x_tok + (uint32_t)((PH * bh + 32 * q + pbase) * 2);
         }
         using xvec = typename std::conditional<(PBH >= 2), u32x4, u32x2>::type;
         frag gf[IB][KS];          // C B^T fragments: k-step ks covers tokens 32 ks + 8 kg .. + 7
-        xvec zq[IB][NPQ];
         auto load_g = [&](int tau) __attribute__((always_inline)) {
             const uint32_t sg = (uint32_t)((gbase + tau) * (size_t)(TT * TT * 2));
 #pragma unroll
@@ -247,21 +252,6 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
                     gf[ib][ks] = Tr::load_frag_s(rg, oob_if(ks > ah, vgo[ib] + ks * 64), sg);
-        };
-        auto load_z = [&](int tt) __attribute__((always_inline)) {
-            if constexpr (kGate) {
-                const uint32_t sx = (uint32_t)tt * x_tok + hp0;
-#pragma unroll
-                for (int ib = 0; ib < IB; ++ib)
-#pragma unroll
-                    for (int q = 0; q < NPQ; ++q) {
-                        if constexpr (PBH >= 2) {
-                            zq[ib][q] = buf_ld128s(rz, vy[ib][q], sx);
-                        } else {
-                            zq[ib][q] = __builtin_amdgcn_raw_buffer_load_b64(rz, vy[ib][q], sx, 0);
-                        }
-                    }
-            }
         };
         // C staging: this wave loads 16 of the 32 rows its token half needs
         // (rows 32 ah + 16 bh ..) a tile ahead as whole lines, and writes them
@@ -294,14 +284,42 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
             vx[k] = oob_if(u >= Cfg::UX, (uint32_t)(4 * rs_unit_tq(u)) * x_tok + (uint32_t)(8 * rs_unit_col(u)));
         }
         u32x2 xr[kDepth][RX][4];
+        // input convolution: the 3 tokens before each unit, and the unit's
+        // columns' taps and bias (a lane's units keep their columns on every tile)
+        u32x2 xhalo[kDepth][RX][kConv ? 3 : 1];
+        f32x4 ctap[RX][kConv ? 4 : 1];
+        float cbias[RX][kConv ? 4 : 1];
+        if constexpr (kConv) {
+#pragma unroll
+            for (int k = 0; k < RX; ++k) {
+                const int u = st + 256 * k;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = h * P + p0 + (u < Cfg::UX ? 4 * rs_unit_col(u) + e : 0);
+                    ctap[k][e] = *reinterpret_cast<const f32x4 *>(a.conv_w + 4 * (size_t)col);
+                    cbias[k][e] = a.conv_b ? a.conv_b[col] : 0.f;
+                }
+            }
+        }
         auto issue_x = [&](int tt, auto Sc) __attribute__((always_inline)) {
             constexpr int Sx = decltype(Sc)::value;
             const uint32_t sx = (uint32_t)tt * x_tok + hp0;
 #pragma unroll
-            for (int k = 0; k < RX; ++k)
+            for (int k = 0; k < RX; ++k) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     xr[Sx][k][i] = __builtin_amdgcn_raw_buffer_load_b64(rx, vx[k] + i * x_tok, sx, 0);
+                if constexpr (kConv) {
+                    const int u = st + 256 * k;
+                    const int row0 = tt + 4 * rs_unit_tq(u) - 3;  // token of halo row 0 (before the sequence: 0)
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+                        xhalo[Sx][k][i] = __builtin_amdgcn_raw_buffer_load_b64(
+                            rx, oob_if(u >= Cfg::UX || row0 + i < 0,
+                                       (uint32_t)(row0 + i) * x_tok + hp0 + (uint32_t)(8 * rs_unit_col(u))),
+                            0, 0);
+                }
+            }
         };
         // writes the weighted X of a tile (and the plain X in per-element
         // tiles) into X slot `slot`; cr / ce: cs2 before the tile and at its
@@ -316,10 +334,40 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 const int u = st + 256 * k;
                 if (u >= Cfg::UX) continue;  // wave-uniform (UX is a multiple of 64)
                 const int tq = rs_unit_tq(u), c4 = rs_unit_col(u);
-                // the unit's 4 tokens x 4 columns as they are, for the skip term
+                // the unit's 4 tokens x 4 columns (after the input convolution
+                // when there is one, rounded to bf16: the scan's input and the
+                // skip term's)
+                u32x2 xin[4];
+                if constexpr (kConv) {
+                    // x' = SiLU(b + w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t)
+                    float xo[4][4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float xv[7];  // tokens 4 tq - 3 .. 4 tq + 3 of column 4 c4 + e
+#pragma unroll
+                        for (int i = 0; i < 3; ++i)
+                            xv[i] = (e & 1) ? bf16_hi(xhalo[Sx][k][i][e >> 1]) : bf16_lo(xhalo[Sx][k][i][e >> 1]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            xv[3 + i] = (e & 1) ? bf16_hi(xr[Sx][k][i][e >> 1]) : bf16_lo(xr[Sx][k][i][e >> 1]);
+                        const f32x4 w = ctap[k][e];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = cbias[k][e] + w[0] * xv[i] + w[1] * xv[i + 1] + w[2] * xv[i + 2] +
+                                            w[3] * xv[i + 3];
+                            xo[i][e] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xin[i] = u32x2{pack_bf16x2(xo[i][0], xo[i][1]), pack_bf16x2(xo[i][2], xo[i][3])};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xin[i] = xr[Sx][k][i];
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<u32x2 *>(XRs + (4 * tq + i) * Cfg::XRLD + 4 * c4) = xr[Sx][k][i];
+                    *reinterpret_cast<u32x2 *>(XRs + (4 * tq + i) * Cfg::XRLD + 4 * c4) = xin[i];
                 // factored tiles: X~_j = 2^(cs_r - cs'_j) x_j; the others: x_j as it is
                 const f32x4 cp = cpk(k);
                 float cw[4];
@@ -330,7 +378,7 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                     // column 4 c4 + e, its 4 tokens 4 tq .. 4 tq + 3: half of 16-byte piece tq / 2
                     float xv[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) xv[i] = (e & 1) ? bf16_hi(xr[Sx][k][i][e >> 1]) : bf16_lo(xr[Sx][k][i][e >> 1]);
+                    for (int i = 0; i < 4; ++i) xv[i] = (e & 1) ? bf16_hi(xin[i][e >> 1]) : bf16_lo(xin[i][e >> 1]);
                     *reinterpret_cast<u32x2 *>(XWs + xw_off(4 * c4 + e, tq >> 1) + 4 * (tq & 1)) =
                         u32x2{pack_bf16x2(xv[0] * cw[0], xv[1] * cw[1]), pack_bf16x2(xv[2] * cw[2], xv[3] * cw[3])};
                 }
@@ -352,18 +400,38 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         const rsrc_t ry = make_rsrc(reinterpret_cast<char *>(a.Y) + x0, (uint32_t)xslab);
         constexpr int YP = PW / 8;             // 16-byte pieces per row
         constexpr int YRI = 64 / YP;           // rows per store instruction
+        // The gate y * SiLU(z) acts here, on the output rounded to bf16, with z
+        // read in the same whole-row pieces a tile ahead of its rows' store.
+        u32x4 zrow[kGate ? 16 / YRI : 1];
+        auto load_z = [&](int tau) __attribute__((always_inline)) {
+            if constexpr (kGate) {
+                const uint32_t sy = (uint32_t)(tau * TT) * x_tok + hp0;
+#pragma unroll
+                for (int k = 0; k < 16 / YRI; ++k) {
+                    const int row = 16 * wv + YRI * k + lane / YP, pc = lane % YP;
+                    zrow[k] = buf_ld128s(rz, (uint32_t)row * x_tok + (uint32_t)(16 * pc), sy);
+                }
+            }
+        };
         auto store_y = [&](int tau) __attribute__((always_inline)) {
             const bf16 *YSs = YSB + (tau & 1) * TT * Cfg::YLD;
             const uint32_t sy = (uint32_t)(tau * TT) * x_tok + hp0;
 #pragma unroll
             for (int k = 0; k < 16 / YRI; ++k) {
                 const int row = 16 * wv + YRI * k + lane / YP, pc = lane % YP;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(YSs + row * Cfg::YLD + 8 * pc);
+                u32x4 v = *reinterpret_cast<const u32x4 *>(YSs + row * Cfg::YLD + 8 * pc);
+                if constexpr (kGate) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[e] = pack_bf16x2(rs_gate(bf16_lo(v[e]), bf16_lo(zrow[k][e])),
+                                           rs_gate(bf16_hi(v[e]), bf16_hi(zrow[k][e])));
+                }
                 buf_st128s(v, ry, (uint32_t)row * x_tok + (uint32_t)(16 * pc), sy);
             }
         };
 
         const int tile_b = cb * NT;
+        load_z(tile_b);
         load_cs(tile_b * TT);
         issue_x(tile_b * TT, std::integral_constant<int, 0>{});
         store_cs(tile_b & 1);
@@ -371,7 +439,6 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         if constexpr (kDepth == 2) issue_x(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
         load_g(tile_b);
         __builtin_amdgcn_sched_barrier(0);
-        load_z(tile_b * TT);
         __syncthreads();
         for (int c = cb; c < ce; ++c) {
             const float *CSL = CSB + ((c - cb) & 1) * 2 * Q;
@@ -383,8 +450,12 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 const int slot = tau & 1;
                 load_cs(min(tau + 1, last_tile) * TT);
                 issue_x(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
-                // the previous tile's output (its rows were completed before the barrier)
-                if (tau > cb * NT) store_y(tau - 1);
+                // the previous tile's output (its rows were completed before the
+                // barrier), then the gate values of this tile's rows
+                if (tau > cb * NT) {
+                    store_y(tau - 1);
+                    load_z(tau);
+                }
                 // the state at the tile's start, rows p of half bh, both n halves
                 frag hs[2][NM][PBH];
 #pragma unroll
@@ -518,21 +589,11 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                             y[e] += Dh * bf16_lo(xv[e / 2]);
                             y[e + 1] += Dh * bf16_hi(xv[e / 2]);
                         }
-                        if constexpr (kGate) {
-                            // the gate acts on the output rounded to the storage type
-                            const xvec zv = zq[ib][q];
-#pragma unroll
-                            for (int e = 0; e < NE; e += 2) {
-                                y[e] = silu_gate((float)(bf16)y[e], bf16_lo(zv[e / 2]));
-                                y[e + 1] = silu_gate((float)(bf16)y[e + 1], bf16_hi(zv[e / 2]));
-                            }
-                        }
                         xvec o;
 #pragma unroll
                         for (int e = 0; e < NE; e += 2) o[e / 2] = pack_bf16x2(y[e], y[e + 1]);
                         *reinterpret_cast<xvec *>(YSs + (32 * ah + 16 * ib + r) * Cfg::YLD + PH * bh + 32 * q + pbase) = o;
                     }
-                load_z(min(tau + 1, last_tile) * TT);
                 // the next tile's C rows into the other slot
                 store_cs((tau + 1) & 1);
                 __syncthreads();
@@ -750,11 +811,16 @@ static ssd_status run_walk_rs(const FwdArgs &f, hipStream_t s) {
         wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
         wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg; wa.SL = f.S;
         wa.cu = f.cu; wa.total = (int)f.total; wa.z = f.z;
-        wa.conv_w = nullptr; wa.conv_b = nullptr;
+        wa.conv_w = f.conv_w; wa.conv_b = f.conv_b;
         const int64_t heads = f.batch * f.H * f.ns;
         const dim3 grid((unsigned)(heads * f.S));
-        const hipError_t e = f.z ? launch(k_walk_rs<Q, PW, N, true>, grid, dim3(512), s, wa)
-                                 : launch(k_walk_rs<Q, PW, N, false>, grid, dim3(512), s, wa);
+        hipError_t e;
+        if (f.conv_w)
+            e = f.z ? launch(k_walk_rs<Q, PW, N, true, true>, grid, dim3(512), s, wa)
+                    : launch(k_walk_rs<Q, PW, N, false, true>, grid, dim3(512), s, wa);
+        else
+            e = f.z ? launch(k_walk_rs<Q, PW, N, true, false>, grid, dim3(512), s, wa)
+                    : launch(k_walk_rs<Q, PW, N, false, false>, grid, dim3(512), s, wa);
         return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
     }
 }
@@ -778,7 +844,7 @@ static ssd_status walk_rs_p(const FwdArgs &f, hipStream_t s) {
 }
 
 bool walk_rs_supported(const FwdArgs &f) {
-    if (f.dtype != SSD_BF16 || f.conv_w || f.tt != 64) return false;
+    if (f.dtype != SSD_BF16 || f.tt != 64) return false;
     const int64_t pw = f.P / f.ns;
     return (pw == 32 || pw == 64) && (f.N == 64 || f.N == 128) && (f.Q == 64 || f.Q == 128 || f.Q == 256);
 }
