@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
+import glob
 import hashlib
 import json
 import os
@@ -67,6 +68,16 @@ def fwd_accounting(cfg, chunk):
     total = x + tokens * H * es + 2 * bc + 2 * H * 4 + x + final
     walk = x + 2 * bc + x + final  # the walk kernel's share: X, B, C in; Y, final state out
     return {"flops": flops, "bytes": total, "walk_bytes": walk, "tokens": tokens}
+
+
+def bwd_accounting(cfg):
+    """Algorithmic bytes of one backward: X, dY, dt, B, C in; dX, ddt, dB, dC out
+    (A, D, dA, dD are a few hundred bytes)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    x = cfg.batch * cfg.seqlen * cfg.nheads * cfg.headdim * es
+    dt = cfg.batch * cfg.seqlen * cfg.nheads * es
+    bc = cfg.batch * cfg.seqlen * cfg.ngroups * cfg.dstate * es
+    return (2 * x + dt + 2 * bc) + (x + dt + 2 * bc)
 
 
 def decode_accounting(d):
@@ -147,8 +158,7 @@ def cpu_single_thread(workload: str):
 
 
 def device_info(torch):
-    """GPU model, ROCm / HIP versions and the clocks rocm-smi reports."""
-    import subprocess
+    """GPU model, ROCm / HIP versions and the current clock levels."""
     prop = torch.cuda.get_device_properties(0)
     info = {"name": prop.name, "arch": getattr(prop, "gcnArchName", None),
             "compute_units": prop.multi_processor_count, "hbm_bytes": prop.total_memory,
@@ -158,12 +168,19 @@ def device_info(torch):
             info["rocm"] = f.read().strip()
     except OSError:
         info["rocm"] = None
-    try:
-        p = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30)
-        info["clocks"] = [l.strip() for l in p.stdout.splitlines()
-                          if ("sclk" in l or "mclk" in l or "fclk" in l) and "GPU[" in l][:8]
-    except Exception:  # noqa: BLE001  (optional)
-        info["clocks"] = None
+    # current clock levels from the driver's sysfs tables (the line marked *);
+    # read as files, so no program is started from a process that uses the GPU
+    clocks = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(card, name)) as f:
+                    cur = [l.strip() for l in f if l.strip().endswith("*")]
+                if cur:
+                    clocks[f"{os.path.basename(os.path.dirname(card))}/{name[7:]}"] = cur[0]
+            except OSError:
+                pass
+    info["clocks"] = clocks or None
     return info
 
 
@@ -211,9 +228,11 @@ def main():
                     help="sub-blocks of the timed steps for the median per-step time")
     ap.add_argument("--backward-steps", type=int, default=20)
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="for counter runs: 5 walk launches, then 5 element-wise negations of a "
-                         "512 MiB bf16 buffer (a copy of known size, to calibrate the counters); "
-                         "prints one line and exits")
+                    help="for counter runs: 5 forwards (or, with --probe-backward, 5 backward passes), "
+                         "then 5 element-wise negations of a 512 MiB bf16 buffer (a copy of known size, "
+                         "to calibrate the counters); prints one line and exits")
+    ap.add_argument("--probe-backward", action="store_true",
+                    help="with --traffic-probe: run ssd_chunk_scan_bwd instead of the forward")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -322,10 +341,16 @@ def main():
     sets, first_inp = make_sets(cfg, chunk, args.sets)
 
     if args.traffic_probe:
-        for i in range(5):
-            t = sets[i % len(sets)]
-            if lib.ssd_chunk_scan_prepare(*t["prep"]) or lib.ssd_chunk_scan_walk(*t["walk"]):
-                raise RuntimeError("forward failed")
+        if args.probe_backward:
+            t = sets[0]
+            dY = torch.empty_like(t["X"]).normal_()
+            for _ in range(5):
+                ssd.ssd_chunk_scan_bwd(t["X"], t["dt"], t["A"], t["B"], t["C"], t["D"], chunk, dY, stream=stream)
+        else:
+            for i in range(5):
+                t = sets[i % len(sets)]
+                if lib.ssd_chunk_scan_prepare(*t["prep"]) or lib.ssd_chunk_scan_walk(*t["walk"]):
+                    raise RuntimeError("forward failed")
         torch.cuda.synchronize()
         n_copy = 512 * 2 ** 20
         src = torch.ones(n_copy // 2, dtype=torch.bfloat16, device=dev)
@@ -333,9 +358,12 @@ def main():
         for _ in range(5):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"traffic_probe": True, "walk_launches": 5, "copy_bytes_read": n_copy,
-                          "copy_bytes_written": n_copy,
-                          "walk_algorithmic_bytes": fwd_accounting(cfg, chunk)["walk_bytes"]}), flush=True)
+        es = 2 if cfg.dtype == "bf16" else 4
+        bwd_bytes = bwd_accounting(cfg)
+        print(json.dumps({"traffic_probe": True, "backward": args.probe_backward, "launches": 5,
+                          "copy_bytes_read": n_copy, "copy_bytes_written": n_copy,
+                          "walk_algorithmic_bytes": fwd_accounting(cfg, chunk)["walk_bytes"],
+                          "backward_algorithmic_bytes": bwd_bytes}), flush=True)
         return
 
     K = args.steps
@@ -507,8 +535,7 @@ def main():
         be.record(stream)
         torch.cuda.synchronize()
         ms_b = bs.elapsed_time(be) / args.backward_steps
-        es = 2
-        bbytes = 2 * (2 * Bz * T * H * P * es + Bz * T * H * es + 2 * Bz * T * G * N * es)
+        bbytes = bwd_accounting(cfg)
         out["backward"] = {"workload": out["config"]["workload"], "ms_per_call": ms_b,
                            "tokens_per_s": Bz * T / (ms_b / 1e3),
                            "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
