@@ -68,8 +68,10 @@ typedef enum {
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
-/* Human-readable name of a status code (static storage; never NULL). */
-const char *ssd_status_string(ssd_status s);
+/* Human-readable name of a status code (static storage; never NULL). Takes any
+ * int, so a value that is not an ssd_status (e.g. from a newer library) gets a
+ * name too. */
+const char *ssd_status_string(int status);
 
 /*
  * Workspace (device memory, caller-allocated) needed by ssd_chunk_scan_fwd

@@ -138,6 +138,71 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported storage dtype {t.dtype}; use torch.bfloat16 or torch.float32")
 
 
+def _chk(name: str, t, shape, dtype) -> None:
+    """Raises ValueError unless tensor t (when given) has this shape and dtype:
+    the C ABI takes raw pointers and trusts the sizes it is told."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(d) for d in shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(int(d) for d in shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+
+
+def _check_scan(X, dt, A, B, C, D, *, Y=None, final_state=None, initial_state=None, z=None, dY=None,
+                packed_seqs: Optional[int] = None):
+    """Shapes and dtypes of a forward's (or backward's) tensors against X and B:
+    X (b, T, H, P) and B (b, T, G, N), or for a packed batch X (total, H, P) and
+    B (total, G, N) with packed_seqs sequences. X, dt, B, C, Y, z, dY share one
+    storage dtype; A, D and the states are fp32."""
+    import torch
+    if packed_seqs is None:
+        if X.dim() != 4 or B.dim() != 4:
+            raise ValueError("X must be (batch, T, H, P) and B (batch, T, G, N)")
+        bsz, T, H, P = X.shape
+        G, N = B.shape[2], B.shape[3]
+        lead, nst = (bsz, T), bsz
+    else:
+        if X.dim() != 3 or B.dim() != 3:
+            raise ValueError("packed X must be (total, H, P) and B (total, G, N)")
+        total, H, P = X.shape
+        G, N = B.shape[1], B.shape[2]
+        lead, nst = (total,), packed_seqs
+    st = X.dtype
+    _dtype_code(X)
+    _chk("dt", dt, (*lead, H), st)
+    _chk("B", B, (*lead, G, N), st)
+    _chk("C", C, (*lead, G, N), st)
+    _chk("A", A, (H,), torch.float32)
+    _chk("D", D, (H,), torch.float32)
+    _chk("Y", Y, X.shape, st)
+    _chk("z", z, X.shape, st)
+    _chk("dY", dY, X.shape, st)
+    _chk("final_state", final_state, (nst, H, P, N), torch.float32)
+    _chk("initial_state", initial_state, (nst, H, P, N), torch.float32)
+
+
+def _check_step(state, x, dt, A, B, C, D, y=None, z=None):
+    """Shapes and dtypes of a decode step's tensors against state (b, H, P, N)
+    and B (b, G, N)."""
+    import torch
+    if state.dim() != 4 or B.dim() != 3:
+        raise ValueError("state must be (batch, H, P, N) and B (batch, G, N)")
+    bsz, H, P, N = state.shape
+    G = B.shape[1]
+    st = x.dtype
+    _dtype_code(x)
+    _chk("state", state, (bsz, H, P, N), torch.float32)
+    _chk("x", x, (bsz, H, P), st)
+    _chk("dt", dt, (bsz, H), st)
+    _chk("B", B, (bsz, G, N), st)
+    _chk("C", C, (bsz, G, N), st)
+    _chk("A", A, (H,), torch.float32)
+    _chk("D", D, (H,), torch.float32)
+    _chk("y", y, (bsz, H, P), st)
+    _chk("z", z, (bsz, H, P), st)
+
+
 def _ptr(t) -> Optional[int]:
     if t is None:
         return None
@@ -173,6 +238,7 @@ def ssd_chunk_scan_fwd(X, dt, A, B, C, D, chunk: int, Y=None, final_state=None, 
     none was passed in."""
     import torch
     lib = load()
+    _check_scan(X, dt, A, B, C, D, Y=Y, final_state=final_state)
     bsz, T, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(X)
@@ -198,6 +264,9 @@ def ssd_chunk_scan_fwd_noalloc(X, dt, A, B, C, D, chunk: int, Y, final_state=Non
     skip it) already allocated. Calls that may overlap on one GPU race on the
     shared workspace. Returns (Y, final_state)."""
     lib = load()
+    if Y is None:
+        raise ValueError("ssd_chunk_scan_fwd_noalloc allocates nothing: pass Y")
+    _check_scan(X, dt, A, B, C, D, Y=Y, final_state=final_state)
     bsz, T, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
     st = lib.ssd_chunk_scan_fwd_noalloc(_ptr(X), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), chunk,
@@ -218,10 +287,16 @@ def _workspace(workspace, need, device):
 
 def ssd_chunk_scan_prepare(dt, A, B, C, chunk: int, headdim: int, *, workspace=None, stream=None):
     """Phase 1 of the forward: fills and returns the workspace."""
+    import torch
     lib = load()
+    if dt.dim() != 3 or B.dim() != 4:
+        raise ValueError("dt must be (batch, T, H) and B (batch, T, G, N)")
     bsz, T, H = dt.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(dt)
+    _chk("B", B, (bsz, T, G, N), dt.dtype)
+    _chk("C", C, (bsz, T, G, N), dt.dtype)
+    _chk("A", A, (H,), torch.float32)
     need = ssd_chunk_scan_fwd_workspace_bytes(bsz, T, H, headdim, N, G, chunk, code)
     workspace, nbytes = _workspace(workspace, need, dt.device)
     st = lib.ssd_chunk_scan_prepare(_ptr(dt), _ptr(A), _ptr(B), _ptr(C), chunk, bsz, T, H, headdim,
@@ -236,9 +311,17 @@ def ssd_chunk_scan_walk(X, B, C, D, workspace, chunk: int, initial_state=None, Y
     """Phase 2 of the forward: the chunk walk over a prepared workspace."""
     import torch
     lib = load()
+    if X.dim() != 4 or B.dim() != 4:
+        raise ValueError("X must be (batch, T, H, P) and B (batch, T, G, N)")
     bsz, T, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(X)
+    _chk("B", B, (bsz, T, G, N), X.dtype)
+    _chk("C", C, (bsz, T, G, N), X.dtype)
+    _chk("D", D, (H,), torch.float32)
+    _chk("Y", Y, X.shape, X.dtype)
+    _chk("final_state", final_state, (bsz, H, P, N), torch.float32)
+    _chk("initial_state", initial_state, (bsz, H, P, N), torch.float32)
     if Y is None:
         Y = torch.empty_like(X)
     if final_state is None and want_final:
@@ -256,6 +339,7 @@ def ssd_step(state, x, dt, A, B, C, D, y=None, *, stream=None):
     """One decode step; `state` (b, H, P, N) fp32 is updated in place. Returns y."""
     import torch
     lib = load()
+    _check_step(state, x, dt, A, B, C, D, y=y)
     bsz, H, P, N = state.shape
     G = B.shape[1]
     code = _dtype_code(x)
@@ -287,11 +371,13 @@ def ssd_chunk_scan_fwd_varlen(X, dt, A, B, C, D, chunk: int, cu_seqlens, max_seq
     (num_seqs, H, P, N) fp32."""
     import torch
     lib = load()
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-d int32 tensor of num_seqs + 1 offsets")
+    nseq = cu_seqlens.numel() - 1
+    _check_scan(X, dt, A, B, C, D, Y=Y, final_state=final_state, initial_state=initial_state,
+                packed_seqs=nseq)
     total, H, P = X.shape
     G, N = B.shape[1], B.shape[2]
-    if cu_seqlens.dtype != torch.int32:
-        raise TypeError("cu_seqlens must be int32")
-    nseq = cu_seqlens.numel() - 1
     code = _dtype_code(X)
     if Y is None:
         Y = torch.empty_like(X)
@@ -314,6 +400,8 @@ def ssd_chunk_scan_fwd_gated(X, dt, A, B, C, D, chunk: int, *, dt_bias=None, dt_
     1 softplus(dt + bias), 2 softplus(dt) + bias) and output gate Y * silu(z)."""
     import torch
     lib = load()
+    _check_scan(X, dt, A, B, C, D, Y=Y, final_state=final_state, z=z)
+    _chk("dt_bias", dt_bias, (X.shape[2],), torch.float32)
     bsz, T, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(X)
@@ -338,6 +426,10 @@ def ssd_chunk_scan_fwd_fused(X, dt, A, B, C, D, chunk: int, *, conv_w=None, conv
     causal 4-tap depthwise convolution (conv_w (H*P, 4), conv_b (H*P) fp32) and SiLU."""
     import torch
     lib = load()
+    _check_scan(X, dt, A, B, C, D, Y=Y, final_state=final_state, z=z)
+    _chk("dt_bias", dt_bias, (X.shape[2],), torch.float32)
+    _chk("conv_w", conv_w, (X.shape[2] * X.shape[3], 4), torch.float32)
+    _chk("conv_b", conv_b, (X.shape[2] * X.shape[3],), torch.float32)
     bsz, T, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(X)
@@ -361,6 +453,8 @@ def ssd_step_gated(state, x, dt, A, B, C, D, *, dt_bias=None, dt_softplus: int =
     """ssd_step with the fused prologue and output gate (see ssd_chunk_scan_fwd_gated)."""
     import torch
     lib = load()
+    _check_step(state, x, dt, A, B, C, D, y=y, z=z)
+    _chk("dt_bias", dt_bias, (state.shape[1],), torch.float32)
     bsz, H, P, N = state.shape
     G = B.shape[1]
     code = _dtype_code(x)
@@ -390,6 +484,7 @@ def ssd_chunk_scan_bwd(X, dt, A, B, C, D, chunk: int, dY, *, initial_state=None,
     the last is None unless want_initial_grad."""
     import torch
     lib = load()
+    _check_scan(X, dt, A, B, C, D, dY=dY, final_state=d_final_state, initial_state=initial_state)
     bsz, T, H, P = X.shape
     G, N = B.shape[2], B.shape[3]
     code = _dtype_code(X)

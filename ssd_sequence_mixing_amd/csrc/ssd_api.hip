@@ -49,6 +49,9 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
         return SSD_ERR_UNSUPPORTED;
     if (seqlen > kTwoGiB || nheads > 65536) return SSD_ERR_UNSUPPORTED;
     if (total < 0 || total > kTwoGiB) return SSD_ERR_SHAPE;
+    // grid: batch x heads x column slices (<= 4) x segments (<= 4) work-groups.
+    // Checked before any size product, which this bound keeps inside int64.
+    if (batch > (int64_t)INT32_MAX / 16 || batch * nheads > (int64_t)INT32_MAX / 16) return SSD_ERR_UNSUPPORTED;
     if (ssd::fwd_plan((ssd_dtype)dtype, batch, nheads, headdim, dstate, chunk, (seqlen + chunk - 1) / chunk,
                       !varlen, &lay->plan) != 0)
         return SSD_ERR_UNSUPPORTED;
@@ -68,7 +71,6 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     lay->cs_bytes = align256(batch * nheads * Tpad * 4);
     lay->g_bytes = align256(batch * ngroups * Tpad * lay->plan.tt * es);  // one tt x tt tile per tt tokens
     if (lay->g_bytes >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    if (batch * nheads > (int64_t)INT32_MAX / 16) return SSD_ERR_UNSUPPORTED;  // grid: x ns x S <= 16
     lay->seg_bytes = align256(batch * nheads * (lay->plan.S - 1) * headdim * dstate * 4);
     lay->total = (batch == 0 || seqlen == 0) ? 0 : 2 * lay->cs_bytes + lay->g_bytes + lay->seg_bytes;
     return SSD_OK;
@@ -141,7 +143,8 @@ ssd_status check_bwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     const int64_t es = esize((ssd_dtype)dtype);
     const int64_t Tpad = lay->fl.Tpad;
     lay->ntiles = Tpad / 64;
-    if (batch * lay->ntiles * nheads > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    // (batch x heads is bounded by the forward check, so this product fits)
+    if (batch * nheads * lay->ntiles > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
     lay->nblk = bwd_blocks(batch, lay->ntiles, ngroups, nheads / ngroups);
     lay->st_bytes = align256(batch * nheads * lay->ntiles * headdim * dstate * es);
     lay->lamb_bytes = align256(batch * nheads * lay->ntiles * 4);
@@ -232,8 +235,8 @@ ssd_status fwd_impl(const void *X, const float *conv_w, const float *conv_b, con
 
 extern "C" {
 
-const char *ssd_status_string(ssd_status s) {
-    switch (s) {
+const char *ssd_status_string(int status) {
+    switch (status) {
         case SSD_OK: return "SSD_OK";
         case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
         case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: invalid dimensions";
@@ -404,8 +407,10 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
         !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(dt_bias) || !aligned16(z))
         return SSD_ERR_ALIGN;
     if (batch == 0) return SSD_OK;
+    // grid size bound (each factor first, so that the product stays inside int64)
+    if (batch > (int64_t)UINT32_MAX || nheads > 65536 || headdim > 4096) return SSD_ERR_UNSUPPORTED;
     const int64_t rows = batch * nheads * headdim;
-    if (rows > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;  // grid size bound
+    if (rows > (int64_t)UINT32_MAX) return SSD_ERR_UNSUPPORTED;
     ssd::StepArgs a;
     a.state = state; a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
     a.batch = batch; a.H = nheads; a.P = headdim; a.N = dstate; a.G = ngroups; a.dtype = dtype;

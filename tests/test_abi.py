@@ -339,3 +339,43 @@ def test_fused_argument_checks():
     assert fused(X=None) == ENULL
     assert fused(wsp=None) == EWS
     assert fused(batch=0, wsp=None, wsb=0) == OK
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python binding checks shapes and dtypes before any C call (the C ABI
+    trusts the sizes it is told). CPU tensors suffice: the check comes first."""
+    import torch
+    X = torch.zeros((2, 8, 4, 16), dtype=torch.bfloat16)
+    dt = torch.zeros((2, 8, 4), dtype=torch.bfloat16)
+    B = torch.zeros((2, 8, 1, 16), dtype=torch.bfloat16)
+    A = torch.zeros(4)
+    D = torch.zeros(4)
+    bad = [
+        ("dt", dict(dt=torch.zeros((2, 8, 3), dtype=torch.bfloat16))),
+        ("B", dict(B=torch.zeros((2, 8, 1, 16), dtype=torch.float32))),
+        ("A", dict(A=torch.zeros(4, dtype=torch.float64))),
+        ("D", dict(D=torch.zeros(5))),
+        ("Y", dict(Y=torch.zeros((2, 8, 4, 8), dtype=torch.bfloat16))),
+        ("final_state", dict(final_state=torch.zeros((2, 4, 16, 16), dtype=torch.bfloat16))),
+    ]
+    for name, kw in bad:
+        args = dict(X=X, dt=dt, A=A, B=B, C=B, D=D)
+        extra = {k: kw.pop(k) for k in list(kw) if k in ("Y", "final_state")}
+        args.update(kw)
+        with pytest.raises(ValueError, match=f"^{name}:"):
+            ssd.ssd_chunk_scan_fwd(args["X"], args["dt"], args["A"], args["B"], args["C"], args["D"], 64,
+                                   **extra)
+    # the same tensors with consistent shapes pass the check and stop at the device check
+    with pytest.raises(ValueError, match="on the GPU"):
+        ssd.ssd_chunk_scan_fwd(X, dt, A, B, B, D, 64)
+    state = torch.zeros((2, 4, 16, 16))
+    x = torch.zeros((2, 4, 16), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="^state:"):
+        ssd.ssd_step(state.to(torch.bfloat16), x, dt[:, 0], A, B[:, 0], B[:, 0], D)
+    with pytest.raises(ValueError, match="^y:"):
+        ssd.ssd_step(state, x, dt[:, 0], A, B[:, 0], B[:, 0], D, y=torch.zeros((2, 4, 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="^dY:"):
+        ssd.ssd_chunk_scan_bwd(X, dt, A, B, B, D, 64, torch.zeros((2, 8, 4, 16)))
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        ssd.ssd_chunk_scan_fwd_varlen(X[0], dt[0], A, B[0], B[0], D, 64,
+                                      torch.zeros(3, dtype=torch.int64), 8)

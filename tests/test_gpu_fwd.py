@@ -255,3 +255,43 @@ def test_resume_across_calls(ssd):
     e = (rel(Ys, Yf.float().cpu().numpy()), rel(Fb.cpu().numpy(), Ff.cpu().numpy()))
     log(f"[fwd] resume across calls: rel Y={e[0]:.2e} final={e[1]:.2e}")
     assert max(e) <= TOL["bf16"], e
+
+
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 256), ("f32", 64)])
+def test_canaries_around_outputs_and_workspace(ssd, dtype, chunk):
+    """Y, the final state and the workspace sit inside larger buffers whose
+    guard bytes before and after must come back untouched; the results must
+    equal those of an ordinary call bit for bit. Ragged T, several heads."""
+    import torch
+    base = si.CONFIGS["l1p3b_bf16"] if dtype == "bf16" else si.CONFIGS["tiny_f32"]
+    cfg = dataclasses.replace(base, name=f"canary_{dtype}", batch=2, seqlen=1000, nheads=8,
+                              headdim=64 if dtype == "bf16" else 32, dstate=128 if dtype == "bf16" else 64,
+                              ngroups=2, seed=41)
+    log(f"[fwd canary] {cfg.name} chunk={chunk}")
+    inp = si.make_fwd_inputs(cfg)
+    X, dt, B, C = (to_dev(inp[k]) for k in ("X", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    code = ssd.SSD_BF16 if dtype == "bf16" else ssd.SSD_F32
+    Bz, T, H, P, N, G = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    need = ssd.ssd_chunk_scan_fwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
+    Yr, Fr = ssd.ssd_chunk_scan_fwd(X, dt, A, B, C, D, chunk)
+    GUARD, MARK = 4096, 0xA5
+
+    def guarded(nbytes):
+        return torch.full((GUARD + nbytes + GUARD,), MARK, dtype=torch.uint8, device="cuda")
+
+    y_bytes = X.numel() * X.element_size()
+    f_bytes = Bz * H * P * N * 4
+    Yb, Fb, Wb = guarded(y_bytes), guarded(f_bytes), guarded(need)
+    st = ssd.raw_call("ssd_chunk_scan_fwd", X.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(),
+                      D.data_ptr(), chunk, Yb.data_ptr() + GUARD, Fb.data_ptr() + GUARD, Bz, T, H, P, N, G, code,
+                      Wb.data_ptr() + GUARD, need, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    for buf, n in ((Yb, y_bytes), (Fb, f_bytes), (Wb, need)):
+        assert torch.all(buf[:GUARD] == MARK) and torch.all(buf[GUARD + n:] == MARK)
+    Y = Yb[GUARD:GUARD + y_bytes].view(X.dtype).view(X.shape)
+    F = Fb[GUARD:GUARD + f_bytes].view(torch.float32).view(Fr.shape)
+    ints = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(Y.view(ints), Yr.view(ints))
+    assert torch.equal(F.view(torch.int32), Fr.view(torch.int32))
