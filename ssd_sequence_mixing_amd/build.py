@@ -29,13 +29,20 @@ COMMON = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17", "-Wall",
           "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-file flags. The segment end-state kernel keeps its matrix-core
+# accumulators in ordinary VGPRs: left to its heuristics the compiler splits
+# them between the two register files and copies them back and forth every
+# step, and the copies wait on loads in flight.
+FILE_FLAGS = {"ssd_seg_states.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + DEVICE_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     p = subprocess.run(cmd, capture_output=True, text=True)

@@ -1122,9 +1122,15 @@ static ssd_status run_walk_c(const FwdArgs &f, hipStream_t s) {
         const int64_t heads = f.batch * f.H * f.ns;
         if (f.S > 1) {
             wa.SL = f.S - 1;
-            if (launch(k_chunk_walk<TI, Q, PW, N, TT, true, kConv>, dim3((unsigned)(heads * wa.SL)), dim3(256), s,
-                       wa) != hipSuccess)
-                return SSD_ERR_HIP;
+            if constexpr (kConv) {
+                // the segments' end states need the convolved X: the state-only walk
+                if (launch(k_chunk_walk<TI, Q, PW, N, TT, true, kConv>, dim3((unsigned)(heads * wa.SL)), dim3(256),
+                           s, wa) != hipSuccess)
+                    return SSD_ERR_HIP;
+            } else {
+                const ssd_status st = launch_seg_states(f, s);
+                if (st != SSD_OK) return st;
+            }
             const int64_t n4 = f.batch * f.H * f.P * f.N / 4;
             if (f.S > 2 && launch(k_seg_scan, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, f.seg,
                                   (const float *)f.cs2, f.batch * f.H, (int)(f.P * f.N), f.S, f.cps,

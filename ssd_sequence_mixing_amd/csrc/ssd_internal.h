@@ -152,6 +152,9 @@ ssd_status launch_walk_conv(const FwdArgs &f, hipStream_t s);
 // and N of 64 or 128, with or without the gate and the input convolution.
 bool walk_rs_supported(const FwdArgs &f);
 ssd_status launch_walk_rs(const FwdArgs &f, hipStream_t s);
+// The end states of a split sequence's segments 0 .. S - 2 (each entered with
+// zero, the first with f.init) into f.seg (ssd_seg_states.hip).
+ssd_status launch_seg_states(const FwdArgs &f, hipStream_t s);
 // One recurrent decode step.
 ssd_status launch_step(const StepArgs &a, hipStream_t s);
 
