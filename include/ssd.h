@@ -271,6 +271,32 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
                           void *stream);
 
 /*
+ * The gated decode step with the layer's input convolution fused in, the
+ * one-token form of ssd_chunk_scan_fwd_fused: x arrives before the causal
+ * conv1d(4) + SiLU, and the 3 raw inputs before it are carried in a rolling
+ * conv state (the SSD theory page's layer convolves the scan's input over a
+ * 4-token window, section 4.1; the recurrent form keeps what that window
+ * needs, as the SSM primer's decode keeps a fixed-size state). For channel
+ * c = h * headdim + p:
+ *
+ *   x'[b,c] = SiLU(conv_b[c] + sum_{k<3} conv_w[c][k] conv_state[b,c,k] + conv_w[c][3] x[b,c])
+ *
+ * in fp32, rounded to the storage type; x' is the step's input and the D
+ * skip's. Then conv_state[b,c,:] <- (conv_state[b,c,1], conv_state[b,c,2], x[b,c]).
+ *
+ *   conv_state (batch, nheads * headdim, 3)  dtype     in/out, oldest input first; zeros
+ *              at a sequence start (T steps from zero equal ssd_chunk_scan_fwd_fused
+ *              over those T tokens)
+ *   conv_w (nheads * headdim, 4) float32, conv_b (nheads * headdim) float32 or NULL
+ * Other arguments as ssd_step_gated; conv_state and conv_w 16-byte aligned.
+ */
+ssd_status ssd_step_fused(float *state, void *conv_state, const void *x, const float *conv_w,
+                          const float *conv_b, const void *dt, const float *dt_bias, int dt_softplus,
+                          const float *A, const void *B, const void *C, const float *D, const void *z,
+                          void *y, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+                          int64_t ngroups, ssd_dtype dtype, void *stream);
+
+/*
  * Backward pass: the gradients of the scalar  <dY, Y> + <dF, final_state>
  * for one ssd_chunk_scan_fwd (from initial_state, or zero), with respect to
  * every input. Training needs them; the pages' speed comparisons are of

@@ -18,7 +18,7 @@ __all__ = [
     "ssd_chunk_scan_walk", "ssd_step", "ssd_chunk_scan_varlen_workspace_bytes",
     "ssd_chunk_scan_fwd_varlen", "ssd_chunk_scan_fwd_gated", "ssd_step_gated",
     "ssd_chunk_scan_bwd_workspace_bytes", "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused",
-    "ssd_chunk_scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES", "EXPORTS",
+    "ssd_chunk_scan_fwd_noalloc", "ssd_step_fused", "NOALLOC_SCRATCH_BYTES", "EXPORTS",
 ]
 
 SSD_F32 = 0
@@ -32,7 +32,7 @@ EXPORTS = ("ssd_status_string", "ssd_chunk_scan_fwd_workspace_bytes", "ssd_chunk
            "ssd_chunk_scan_prepare", "ssd_chunk_scan_walk", "ssd_step",
            "ssd_chunk_scan_varlen_workspace_bytes", "ssd_chunk_scan_fwd_varlen",
            "ssd_chunk_scan_fwd_gated", "ssd_step_gated", "ssd_chunk_scan_bwd_workspace_bytes",
-           "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused", "ssd_chunk_scan_fwd_noalloc")
+           "ssd_chunk_scan_bwd", "ssd_chunk_scan_fwd_fused", "ssd_chunk_scan_fwd_noalloc", "ssd_step_fused")
 
 # SSD_NOALLOC_SCRATCH_BYTES: the static workspace of ssd_chunk_scan_fwd_noalloc.
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -114,6 +114,8 @@ def load():
     lib.ssd_chunk_scan_fwd_fused.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_fused.argtypes = ([_V] * 5 + [ctypes.c_int] + [_V] * 5 + [_I, _V, _V] + [_I] * 6 +
                                              [ctypes.c_int, _V, ctypes.c_size_t, _V])
+    lib.ssd_step_fused.restype = ctypes.c_int
+    lib.ssd_step_fused.argtypes = ([_V] * 7 + [ctypes.c_int] + [_V] * 6 + [_I] * 5 + [ctypes.c_int, _V])
     lib.ssd_chunk_scan_fwd_noalloc.restype = ctypes.c_int
     lib.ssd_chunk_scan_fwd_noalloc.argtypes = [_V] * 6 + [_I, _V, _V] + [_I] * 6 + [ctypes.c_int, _V]
     lib.ssd_chunk_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -275,6 +277,32 @@ def ssd_chunk_scan_fwd_noalloc(X, dt, A, B, C, D, chunk: int, Y, final_state=Non
     if st != 0:
         raise SSDError(st, "ssd_chunk_scan_fwd_noalloc")
     return Y, final_state
+
+
+def ssd_step_fused(state, conv_state, x, dt, A, B, C, D, *, conv_w, conv_b=None, dt_bias=None,
+                   dt_softplus: int = 0, z=None, y=None, stream=None):
+    """ssd_step_gated with the layer's causal conv1d(4) + SiLU on x: conv_state
+    (b, H*P, 3) in x's dtype holds the 3 earlier raw inputs (oldest first) and
+    is shifted in place, as is the fp32 state. conv_w (H*P, 4), conv_b (H*P)
+    fp32. Returns y."""
+    import torch
+    lib = load()
+    _check_step(state, x, dt, A, B, C, D, y=y, z=z)
+    bsz, H, P, N = state.shape
+    G = B.shape[1]
+    _chk("conv_state", conv_state, (bsz, H * P, 3), x.dtype)
+    _chk("conv_w", conv_w, (H * P, 4), torch.float32)
+    _chk("conv_b", conv_b, (H * P,), torch.float32)
+    _chk("dt_bias", dt_bias, (H,), torch.float32)
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.ssd_step_fused(_ptr(state), _ptr(conv_state), _ptr(x), _ptr(conv_w), _ptr(conv_b), _ptr(dt),
+                            _ptr(dt_bias), int(dt_softplus), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(y), bsz, H, P, N, G, code, _stream(stream))
+    if st != 0:
+        raise SSDError(st, "ssd_step_fused")
+    return y
 
 
 def _workspace(workspace, need, device):

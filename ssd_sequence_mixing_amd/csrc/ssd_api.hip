@@ -231,6 +231,12 @@ ssd_status fwd_impl(const void *X, const float *conv_w, const float *conv_b, con
     return ssd::launch_walk(f, s);
 }
 
+// The decode step with every option (defined after the entry points).
+ssd_status step_impl(float *state, void *conv_state, const void *x, const float *conv_w, const float *conv_b,
+                     const void *dt, const float *dt_bias, int dt_softplus, const float *A, const void *B,
+                     const void *C, const float *D, const void *z, void *y, int64_t batch, int64_t nheads,
+                     int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -397,6 +403,27 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
                           const float *A, const void *B, const void *C, const float *D, const void *z,
                           void *y, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
                           int64_t ngroups, ssd_dtype dtype, void *stream) {
+    return step_impl(state, nullptr, x, nullptr, nullptr, dt, dt_bias, dt_softplus, A, B, C, D, z, y, batch,
+                     nheads, headdim, dstate, ngroups, dtype, stream);
+}
+
+ssd_status ssd_step_fused(float *state, void *conv_state, const void *x, const float *conv_w, const float *conv_b,
+                          const void *dt, const float *dt_bias, int dt_softplus, const float *A, const void *B,
+                          const void *C, const float *D, const void *z, void *y, int64_t batch, int64_t nheads,
+                          int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *stream) {
+    if (batch != 0 && (!conv_state || !conv_w)) return SSD_ERR_NULL;
+    return step_impl(state, conv_state, x, conv_w, conv_b, dt, dt_bias, dt_softplus, A, B, C, D, z, y, batch,
+                     nheads, headdim, dstate, ngroups, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+ssd_status step_impl(float *state, void *conv_state, const void *x, const float *conv_w, const float *conv_b,
+                     const void *dt, const float *dt_bias, int dt_softplus, const float *A, const void *B,
+                     const void *C, const float *D, const void *z, void *y, int64_t batch, int64_t nheads,
+                     int64_t headdim, int64_t dstate, int64_t ngroups, ssd_dtype dtype, void *stream) {
     if (dt_softplus < 0 || dt_softplus > 2) return SSD_ERR_UNSUPPORTED;
     if (batch != 0 && (!state || !x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
     if (!valid_dtype((int)dtype)) return SSD_ERR_UNSUPPORTED;
@@ -404,7 +431,8 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
     if (nheads % ngroups != 0) return SSD_ERR_SHAPE;
     if (!in_set(dstate, {4, 8, 16, 32, 64, 128, 256})) return SSD_ERR_UNSUPPORTED;
     if (!aligned16(state) || !aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
-        !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(dt_bias) || !aligned16(z))
+        !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(dt_bias) || !aligned16(z) ||
+        !aligned16(conv_state) || !aligned16(conv_w) || ((uintptr_t)conv_b & 3u) != 0)
         return SSD_ERR_ALIGN;
     if (batch == 0) return SSD_OK;
     // grid size bound (each factor first, so that the product stays inside int64)
@@ -415,10 +443,11 @@ ssd_status ssd_step_gated(float *state, const void *x, const void *dt, const flo
     a.state = state; a.x = x; a.dt = dt; a.B = B; a.C = C; a.A = A; a.D = D; a.y = y;
     a.batch = batch; a.H = nheads; a.P = headdim; a.N = dstate; a.G = ngroups; a.dtype = dtype;
     a.dt_bias = dt_bias; a.softplus = dt_softplus; a.z = z;
+    a.conv_state = conv_state; a.conv_w = conv_w; a.conv_b = conv_b;
     return ssd::launch_step(a, reinterpret_cast<hipStream_t>(stream));
 }
 
-}  // extern "C"
+}  // namespace
 
 extern "C" {
 

@@ -204,29 +204,40 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
         cq[kk] = Tr::load_frag(rc, oob_if(ti >= T || n0 >= N, (uint32_t)(((ti * G + g) * N + n0) * ES)));
     }
     const size_t tile = (((size_t)b * G + g) * ntiles + tau) * (size_t)(TT * TT);
-    // the 64 B rows of a column group are staged in LDS once for the four
-    // waves (each reads all of them): 16-byte pieces, 8 consecutive n per read
+    // With N = 256 the 64 B rows of a column group (32 KB, which each of the
+    // four waves reads whole) are staged in LDS once per work-group as
+    // 16-byte pieces: it cuts the tile's L2 reads from 160 to 64 KB. For
+    // smaller N the waves load their fragments directly (shorter chain).
+    constexpr bool kBLds = N >= 256;
     constexpr int BLD = N + 16 / ES;                 // row length, padded by 16 bytes
     constexpr int PPR = N * ES / 16;                 // 16-byte pieces per row
-    __shared__ __attribute__((aligned(16))) TI bsh[64 * BLD];
+    __shared__ __attribute__((aligned(16))) TI bsh[kBLds ? 64 * BLD : 1];
     for (int cgp = 0; cgp <= band; ++cgp) {  // 64-column groups up to the band's diagonal
-        if (cgp > 0) __syncthreads();        // the previous group's rows are read
-        for (int c = threadIdx.x; c < 64 * PPR; c += 256) {
-            const int key = c / PPR, pc = c % PPR;
-            const int tj = t0 + 64 * cgp + key;
-            *reinterpret_cast<u32x4 *>(bsh + key * BLD + pc * (16 / ES)) =
-                buf_ld128(rb, oob_if(tj >= T, (uint32_t)((tj * G + g) * N * ES + pc * 16)));
-        }
-        __syncthreads();
         frag bk[4][NK];
+        if constexpr (kBLds) {
+            if (cgp > 0) __syncthreads();    // the previous group's rows are read
+            for (int c = threadIdx.x; c < 64 * PPR; c += 256) {
+                const int key = c / PPR, pc = c % PPR;
+                const int tj = t0 + 64 * cgp + key;
+                *reinterpret_cast<u32x4 *>(bsh + key * BLD + pc * (16 / ES)) =
+                    buf_ld128(rb, oob_if(tj >= T, (uint32_t)((tj * G + g) * N * ES + pc * 16)));
+            }
+            __syncthreads();
 #pragma unroll
-        for (int kk = 0; kk < NK; ++kk) {
-            const int n0 = kk * 32 + 8 * kg;
+            for (int kk = 0; kk < NK; ++kk)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                // (N = 16: lanes past the row's N entries take zeros, as C's do)
-                bk[cb][kk] = frag{};
-                if (n0 < N) bk[cb][kk] = Tr::lds_frag(bsh + (16 * cb + r) * BLD + n0);
+                for (int cb = 0; cb < 4; ++cb)
+                    bk[cb][kk] = Tr::lds_frag(bsh + (16 * cb + r) * BLD + kk * 32 + 8 * kg);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const int n0 = kk * 32 + 8 * kg;
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int tj = t0 + 64 * cgp + 16 * cb + r;
+                    bk[cb][kk] = Tr::load_frag(rb, oob_if(tj >= T || n0 >= N,
+                                                          (uint32_t)(((tj * G + g) * N + n0) * ES)));
+                }
             }
         }
         // acc[cb][i] = G[row][64 cgp + 16 cb + 4 kg + i]

@@ -84,6 +84,9 @@ struct StepArgs {
     const float *dt_bias;      // see FwdArgs
     int softplus;
     const void *z;             // (batch, H, P) like x, or null
+    void *conv_state;          // input convolution: (batch, H P, 3) raw inputs, oldest first, storage type
+    const float *conv_w;       // its taps (H P, 4), or null for no convolution
+    const float *conv_b;       // its bias (H P), or null (zero)
     int64_t batch, H, P, N, G;
     ssd_dtype dtype;
 };

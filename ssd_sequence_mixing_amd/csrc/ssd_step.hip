@@ -6,7 +6,9 @@
 //   y[p] = sum_n s[p,n] C[g,n] + D[h] x[p]
 //
 // optionally with the layer's prologue and epilogue fused in: dt =
-// softplus(dt + dt_bias[h]) and y <- y * silu(z[p]).
+// softplus(dt + dt_bias[h]), the input x <- SiLU(b + w . [x_{t-3}, x_{t-2},
+// x_{t-1}, x_t]) of the layer's causal convolution (the 3 earlier raw inputs
+// kept in a rolling conv state, shifted by this step) and y <- y * silu(z[p]).
 //
 // The state is the only large operand: the kernel streams it once in and
 // once out with 16-byte non-temporal accesses (it is not reused by this
@@ -70,7 +72,27 @@ __global__ __launch_bounds__(kStepThreads) void k_step(StepArgs a, int pblocks) 
 #pragma unroll
     for (int u = 0; u < kStepUnroll; ++u) {
         const bool ok = p[u] < P;
-        const float xv = ok ? Tr::to_f32(reinterpret_cast<const TI *>(a.x)[bh * P + p[u]]) : 0.f;
+        float xv = ok ? Tr::to_f32(reinterpret_cast<const TI *>(a.x)[bh * P + p[u]]) : 0.f;
+        if (a.conv_w && ok) {
+            // channel c = h P + p: x' = SiLU(b + w0 s0 + w1 s1 + w2 s2 + w3 x), in fp32 and
+            // rounded to the storage type (as the forward stages it); the conv
+            // state then holds (s1, s2, x). Every lane of the row reads it, one writes it,
+            // after the reads have been used.
+            const int64_t ch = (int64_t)h * P + p[u];
+            TI *cst = reinterpret_cast<TI *>(a.conv_state) + (bb * H * P + ch) * 3;
+            const TI s1 = cst[1], s2 = cst[2];
+            const float s0 = Tr::to_f32(cst[0]);
+            const f32x4 wv = *reinterpret_cast<const f32x4 *>(a.conv_w + 4 * ch);
+            const float v = (a.conv_b ? a.conv_b[ch] : 0.f) + wv[0] * s0 + wv[1] * Tr::to_f32(s1) +
+                            wv[2] * Tr::to_f32(s2) + wv[3] * xv;
+            const float xa = Tr::to_f32(Tr::from_f32(v / (1.f + expf(-v))));
+            if (c4 == 0) {
+                cst[0] = s1;
+                cst[1] = s2;
+                cst[2] = Tr::from_f32(xv);
+            }
+            xv = xa;
+        }
         const float uin = dtv * xv;
         f32x4 sn;
         float part = 0.f;

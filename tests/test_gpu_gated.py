@@ -228,3 +228,84 @@ def test_fused_without_conv_is_the_gated_forward(ssd):
     Y2, F2 = ssd.ssd_chunk_scan_fwd_fused(*args, 256, **kw)
     torch.cuda.synchronize()
     assert torch.equal(Y1, Y2) and torch.equal(F1, F2)
+
+
+def _step_seq_inputs(rng, Bz, T, H, P, N, G, dtype):
+    X = rng.standard_normal((Bz, T, H, P)).astype(np.float32)
+    raw = rng.standard_normal((Bz, T, H)).astype(np.float32)
+    Bm = (rng.standard_normal((Bz, T, G, N)) / np.sqrt(N)).astype(np.float32)
+    Cm = (rng.standard_normal((Bz, T, G, N)) / np.sqrt(N)).astype(np.float32)
+    z = rng.standard_normal((Bz, T, H, P)).astype(np.float32)
+    if dtype == "bf16":
+        X, raw, Bm, Cm, z = (si.bf16_round_bits(v) for v in (X, raw, Bm, Cm, z))
+    return X, raw, Bm, Cm, z
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fused_step_sequence(ssd, dtype):
+    """T fused decode steps from a given SSM state and conv state against the
+    oracle: the convolution over (conv state, then the step inputs), SiLU, the
+    step prologue, the recurrence and the gate. The conv state must end holding
+    the last 3 raw inputs exactly."""
+    import torch
+    rng = np.random.default_rng(91)
+    Bz, T, H, P, N, G = 2, 12, 4, 16, 32, 2
+    X, raw, Bm, Cm, z = _step_seq_inputs(rng, Bz, T, H, P, N, G, dtype)
+    f = si.bf16_bits_to_f32 if dtype == "bf16" else (lambda a: a)
+    A = -np.exp(rng.uniform(0, np.log(16), H)).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    bias = np.full(H, -2.0, dtype=np.float32)
+    cfg = dataclasses.replace(si.CONFIGS["tiny_f32"], nheads=H, headdim=P)
+    w, b = conv_inputs(cfg, 92)
+    state0 = rng.standard_normal((Bz, H, P, N)).astype(np.float32)
+    cs0 = rng.standard_normal((Bz, H * P, 3)).astype(np.float32)
+    if dtype == "bf16":
+        cs0 = si.bf16_round_bits(cs0)
+    # oracle: the window runs over the conv state's 3 inputs, then the steps'
+    ext = np.concatenate([f(cs0).transpose(0, 2, 1).reshape(Bz, 3, H, P), f(X)], axis=1)
+    xa = oracle_conv_x(ext, w, b)[:, 3:]
+    dt = oracle.dt_prologue(f(raw), bias, 1)
+    s_ref = state0.astype(np.float64)
+    y_ref = np.stack([oracle.gate(oracle.step(s_ref, xa[:, t], dt[:, t], A, f(Bm[:, t]), f(Cm[:, t]), D, G),
+                                  f(z[:, t])) for t in range(T)], axis=1)
+    st = torch.from_numpy(state0).cuda()
+    cst = to_dev(cs0)
+    ys = []
+    for t in range(T):
+        ys.append(to_np(ssd.ssd_step_fused(st, cst, to_dev(X[:, t]), to_dev(raw[:, t]), to_dev(A), to_dev(Bm[:, t]),
+                                           to_dev(Cm[:, t]), to_dev(D), conv_w=to_dev(w), conv_b=to_dev(b),
+                                           dt_bias=to_dev(bias), dt_softplus=1, z=to_dev(z[:, t]))))
+    torch.cuda.synchronize()
+    y = np.stack(ys, axis=1)
+    tol = TOL[dtype]
+    log(f"[fused step] {dtype}: y {rel(y, y_ref):.2e} state {rel(st.cpu().numpy(), s_ref):.2e}")
+    assert rel(y, y_ref) <= tol and rel(st.cpu().numpy(), s_ref) <= tol
+    last3 = X[:, T - 3:].reshape(Bz, 3, H * P).transpose(0, 2, 1)
+    got = cst.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else cst.cpu().numpy()
+    assert np.array_equal(got, last3)
+
+
+def test_fused_steps_equal_the_fused_forward(ssd):
+    """From zero states, T fused decode steps give what ssd_chunk_scan_fwd_fused
+    gives over the same T tokens (both on the GPU, bf16 storage)."""
+    import torch
+    rng = np.random.default_rng(93)
+    Bz, T, H, P, N, G = 2, 40, 4, 32, 64, 2
+    X, raw, Bm, Cm, z = _step_seq_inputs(rng, Bz, T, H, P, N, G, "bf16")
+    A = to_dev(-np.exp(rng.uniform(0, np.log(16), H)).astype(np.float32))
+    D = to_dev(rng.standard_normal(H).astype(np.float32))
+    bias = to_dev(np.full(H, -2.0, dtype=np.float32))
+    cfg = dataclasses.replace(si.CONFIGS["tiny_f32"], nheads=H, headdim=P)
+    w, b = (to_dev(v) for v in conv_inputs(cfg, 94))
+    Yf, Ff = ssd.ssd_chunk_scan_fwd_fused(to_dev(X), to_dev(raw), A, to_dev(Bm), to_dev(Cm), D, 64, conv_w=w,
+                                          conv_b=b, dt_bias=bias, dt_softplus=1, z=to_dev(z))
+    st = torch.zeros((Bz, H, P, N), device="cuda")
+    cst = torch.zeros((Bz, H * P, 3), dtype=torch.bfloat16, device="cuda")
+    ys = [ssd.ssd_step_fused(st, cst, to_dev(X[:, t]), to_dev(raw[:, t]), A, to_dev(Bm[:, t]), to_dev(Cm[:, t]), D,
+                             conv_w=w, conv_b=b, dt_bias=bias, dt_softplus=1, z=to_dev(z[:, t]))
+          for t in range(T)]
+    torch.cuda.synchronize()
+    y = np.stack([to_np(v) for v in ys], axis=1)
+    e_y, e_f = rel(y, to_np(Yf)), rel(st.cpu().numpy(), Ff.cpu().numpy())
+    log(f"[fused steps vs fused forward] y {e_y:.2e} final state {e_f:.2e}")
+    assert e_y <= TOL["bf16"] and e_f <= TOL["bf16"]
