@@ -540,7 +540,7 @@ def main():
                            "tokens_per_s": Bz * T / (ms_b / 1e3),
                            "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
                            "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
-                           "kernels": "k_state_pass x2, k_bwd_tile, k_bwd_fin, k_bwd_sum_bc (+ k_prepare)"}
+                           "kernels": "k_state_passes (both state passes, one launch), k_bwd_tile, k_bwd_fin, k_bwd_heads, k_bwd_sum_bc (+ k_prepare)"}
         del bws, dY, g
 
     if not args.no_cpu_baseline:

@@ -11,8 +11,11 @@
 //   Lambda_t = (dy_t . y_t' - dt_t x_t . v_t) + Lambda_{t+1},
 // a reverse running sum of per-token scalars. At a tile boundary Lambda is
 // also <E, s> of the adjoint arriving from the next tile and the state
-// leaving this one; the forward state pass forms that product from its fp32
-// state, and the running sum restarts from it at every tile. dA sums
+// leaving this one, s = 2^{cs_e - cs_r} h + sum_j 2^{cs_e - cs'_j} x_j B_j^T
+// with h the state entering the tile; k_bwd_tile forms it as
+// 2^{cs_e - cs_r} <E, h> + sum_j 2^{cs_e - cs'_j} x_j . (E B_j) from the
+// operands it already holds, and the running sum restarts from it at every
+// tile. dA sums
 // dt_t Lambda_t, which cancels heavily; a running sum over the whole
 // sequence would carry every rounding error of the per-token scalars (bf16
 // operands) into all earlier tokens.
@@ -20,18 +23,20 @@
 // The work follows the chunked form of the forward (the reading report's
 // section 3.1: quadratic diagonal blocks, rank-N blocks through states handed
 // across block boundaries), in 64-token tiles:
-//   k_state_pass<rev>  per (batch, head), tiles in reverse: the adjoint
+//   k_state_passes, reverse work-groups
+//                      per (batch, head), tiles in reverse: the adjoint
 //                      arriving at every tile from the tokens after it,
 //                      E = a ds of the next token (stored in the storage
 //                      type), and finally a_0 ds_0, the initial state's
 //                      gradient;
-//   k_state_pass<fwd>  per (batch, head): the state entering every tile
-//                      (stored in the storage type) and Lambda at every
-//                      tile's end;
+//   k_state_passes, forward work-groups (the same launch)
+//                      per (batch, head): the state entering every tile
+//                      (stored in the storage type);
 //   k_bwd_tile         per (batch, tile, group, block of heads): everything
 //                      inside the tile from h (entering state) and E (arriving
 //                      adjoint): y', v, dx, the per-token scalars of Lambda,
-//                      and dB, dC summed over the block's heads;
+//                      Lambda at the tile's end, and dB, dC summed over the
+//                      block's heads;
 //   k_bwd_fin          per (batch, head, tile): Lambda down the tile, ddt, and
 //                      the tile's shares of dA, dD (k_bwd_heads adds them up);
 //   k_bwd_sum_bc       dB and dC summed over head blocks, in the storage type.
@@ -46,6 +51,8 @@
 // overflows; masked positions are selected to zero before use.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "ssd_common.h"
 #include "ssd_internal.h"
@@ -220,33 +227,43 @@ struct TileRegs {
 };
 
 // ---------------------------------------------------------------------------
-// k_state_pass: one work-group (8 wavefronts) per (batch, head) walks the
-// tiles (backwards when kRev) with the P x N state in matrix-core
-// accumulators, wave w owning the state's columns n in blocks w, w + 8, ...
+// The state passes: one work-group of SP_NW wavefronts per (batch, head) walks
+// the tiles (backwards when kRev) with the P x N state in matrix-core
+// accumulators, wave w owning the state's columns n in blocks w, w + SP_NW, ...
 // Before each tile it stores the state it carries into Sst[tile] ([p][n],
 // storage type); after the last one it writes the state (fp32) to `out`.
 //   forward: S <- 2^{cs_e - cs_r} S + sum_t 2^{cs_e - cs'_t} x_t B_t^T
 //   reverse: S <- 2^{cs_e - cs_r} S + sum_t 2^{cs_t - cs_r} dy_t C_t^T
-// (U = X or dY, V = B or C).
+// (U = X or dY, V = B or C). The two passes share nothing, so k_state_passes
+// runs both in one launch (reverse work-groups first), two work-groups per CU.
 // ---------------------------------------------------------------------------
-template <typename TI, int P, int N, bool kRev>
-__global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
-    using Tr = Traits<TI>;
-    using frag = typename Tr::frag;
-    constexpr int ES = Tr::kBytes, PAD = 16 / ES, T_LD = kBT + PAD;
-    constexpr int NW = 8, NTH = 64 * NW;  // wavefronts; wave w owns n-blocks w, w + NW, ...
-    constexpr int PB = P / 16, NB = N / 16, NBW = (NB + NW - 1) / NW;
-    __shared__ __attribute__((aligned(16))) TI UT[P * T_LD];
-    __shared__ __attribute__((aligned(16))) TI VT[N * T_LD];
-    __shared__ float WT[kBT];
+constexpr int SP_NW = 4;  // wavefronts per state-pass work-group
+
+template <typename TI, int P, int N>
+struct SpLds {
+    static constexpr int ES = sizeof(TI), PAD = 16 / ES, T_LD = kBT + PAD, S_LD = N + PAD;
+    TI UT[P * T_LD];
+    TI VT[N * T_LD];
     // the state each tile stores goes through LDS ([p][n], padded rows) so that
     // it leaves as whole 16-byte row pieces: written straight from the
     // accumulators each store instruction would cover 16 rows x 32 bytes
-    constexpr int S_LD = N + PAD;
-    __shared__ __attribute__((aligned(16))) TI SS[P * S_LD];
+    TI SS[P * S_LD];
+    float WT[kBT];
+};
+
+template <typename TI, int P, int N, bool kRev>
+__device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, N> &sm, const int bh) {
+    using Tr = Traits<TI>;
+    using frag = typename Tr::frag;
+    using L = SpLds<TI, P, N>;
+    constexpr int ES = Tr::kBytes, T_LD = L::T_LD, S_LD = L::S_LD;
+    constexpr int NW = SP_NW, NTH = 64 * NW;  // wave w owns n-blocks w, w + NW, ...
+    constexpr int PB = P / 16, NB = N / 16, NBW = (NB + NW - 1) / NW;
+    TI *const UT = sm.UT, *const VT = sm.VT, *const SS = sm.SS;
+    float *const WT = sm.WT;
 
     const int H = a.H, G = a.G, T = a.T;
-    const int bh = blockIdx.x, b = bh / H, h = bh - b * H, g = (h * G) / H;
+    const int b = bh / H, h = bh - b * H, g = (h * G) / H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kg = lane >> 4;
     const rsrc_t ru = make_rsrc(reinterpret_cast<const char *>(a.U) + (size_t)b * T * H * P * ES,
                                 (uint32_t)((size_t)T * H * P * ES));
@@ -267,31 +284,24 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
             acc[pb][j] = v;
         }
     const int ntiles = a.ntiles;
-    // a tile's U, V, per-token exponent terms (and, forward, the adjoint
-    // arriving at it), loaded two tiles ahead into one of two register sets
+    // a tile's U, V and per-token exponent terms, loaded two tiles ahead into
+    // one of two register sets.
+    // Every slot is consumed before it is loaded again (a value still live
+    // across the next load into its slot becomes a register copy at the loop's
+    // back edge, and the copy waits for every load in flight).
     TileRegs<TI, kBT, P, NTH> ur[2];
     TileRegs<TI, kBT, N, NTH> vr[2];
-    float wcs[2] = {0.f, 0.f};                   // this thread's token term (tid < 64)
+    float wcs[2] = {0.f, 0.f};                   // this thread's token term
     float pcs_r[2] = {0.f, 0.f}, pcs_e[2] = {0.f, 0.f};
-    TI e4[2][PB][NBW][4];
     auto issue = [&](int tau, auto Sc) {
         constexpr int S = decltype(Sc)::value;
         const int t0 = tau * kBT;
         ur[S].load(ru, (uint32_t)(((size_t)t0 * H + h) * P * ES), (uint32_t)(H * P * ES), tid);
         vr[S].load(rv, (uint32_t)(((size_t)t0 * G + g) * N * ES), (uint32_t)(G * N * ES), tid);
-        pcs_r[S] = (tau % a.tpc == 0) ? 0.f : cs[t0 - 1];
+        // unconditional: a chunk's first tile takes 0 where the value is used
+        pcs_r[S] = cs[max(t0 - 1, 0)];
         pcs_e[S] = cs[t0 + kBT - 1];
         wcs[S] = kRev ? cs[t0 + (tid & 63)] : cp[t0 + (tid & 63)];
-        if constexpr (!kRev) {
-            const TI *E = reinterpret_cast<const TI *>(a.Est) + ((size_t)bh * ntiles + tau) * P * N;
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-                for (int j = 0; j < NBW; ++j) {
-                    const int nb = w + NW * j;
-                    if (nb < NB) lds_ld4<TI>(e4[S][pb][j], E + (16 * pb + r) * N + 16 * nb + 4 * kg);
-                }
-        }
     };
     auto tile_of = [&](int it) { return kRev ? max(ntiles - 1 - it, 0) : min(it, ntiles - 1); };
     issue(tile_of(0), std::integral_constant<int, 0>{});
@@ -307,8 +317,11 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
                 const int nb = w + NW * j;
                 if (nb < NB) store4<TI>(SS + (16 * pb + r) * S_LD + 16 * nb + 4 * kg, acc[pb][j]);
             }
-        const float cs_r = pcs_r[S], cs_e = pcs_e[S];
-        if (tid < kBT) WT[tid] = kRev ? fast_exp2(wcs[S] - cs_r) : fast_exp2(cs_e - wcs[S]);
+        const float cs_r = (tau % a.tpc == 0) ? 0.f : pcs_r[S], cs_e = pcs_e[S];
+        const float dec = fast_exp2(cs_e - cs_r);
+        // every wavefront writes the same 64 weights: no load result is consumed under a
+        // branch (that made the compiler wait for every load in flight, the prefetch included)
+        WT[tid & (kBT - 1)] = kRev ? fast_exp2(wcs[S] - cs_r) : fast_exp2(cs_e - wcs[S]);
         __syncthreads();  // SS and WT visible; the previous tile's reads of UT / VT are done
         {
             constexpr int VPRS = N * ES / 16;  // 16-byte pieces per state row
@@ -322,18 +335,8 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
         ur[S].template store_T<false>(UT, T_LD, tid, [](int) { return 1.f; });
         vr[S].template store_T<true>(VT, T_LD, tid, [&](int q) { return WT[q]; });
         __syncthreads();
-        TI ee[PB][NBW][4];
-        if constexpr (!kRev) {
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-                for (int j = 0; j < NBW; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) ee[pb][j][i] = e4[S][pb][j][i];
-        }
         // the tile after next is loaded while this one is computed (past the end: a reload)
         issue(tile_of(it + 2), Sc);
-        const float dec = fast_exp2(cs_e - cs_r);
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
@@ -353,30 +356,16 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
                 }
             }
         }
-        if constexpr (!kRev) {
-            // Lambda at the tile's end: <E of this tile, state after it>
-            float part = 0.f;
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb)
-#pragma unroll
-                for (int j = 0; j < NBW; ++j) {
-                    const int nb = w + NW * j;
-                    if (nb < NB) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) part += Tr::to_f32(ee[pb][j][i]) * acc[pb][j][i];
-                    }
-                }
-#pragma unroll
-            for (int m = 32; m > 0; m >>= 1) part += __shfl_xor(part, m);
-            // one share per wavefront, added up by k_bwd_fin in a fixed order
-            if (lane == 0) a.lamb[((size_t)bh * ntiles + tau) * NW + w] = part;
-        }
         __syncthreads();
     };
-    for (int it = 0; it < ntiles; it += 2) {
+    // pairs of steps with no condition inside the loop body (a conditional second step made
+    // the compiler drain every load in flight at the back edge), then an odd last tile
+    int it = 0;
+    for (; it + 1 < ntiles; it += 2) {
         step(it, std::integral_constant<int, 0>{});
-        if (it + 1 < ntiles) step(it + 1, std::integral_constant<int, 1>{});
+        step(it + 1, std::integral_constant<int, 1>{});
     }
+    if (it < ntiles) step(it, std::integral_constant<int, 0>{});
     if (a.out) {
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
@@ -388,6 +377,15 @@ __global__ __launch_bounds__(512) void k_state_pass(StatePassArgs a) {
                         acc[pb][j];
             }
     }
+}
+
+// work-groups [0, nbh): the reverse pass; [nbh, 2 nbh): the forward pass
+template <typename TI, int P, int N>
+__global__ __launch_bounds__(64 * SP_NW) void k_state_passes(StatePassArgs rev, StatePassArgs fwd, int nbh) {
+    __shared__ __attribute__((aligned(16))) SpLds<TI, P, N> sm;
+    const int x = blockIdx.x;
+    if (x < nbh) state_pass<TI, P, N, true>(rev, sm, x);
+    else state_pass<TI, P, N, false>(fwd, sm, x - nbh);
 }
 
 // ---------------------------------------------------------------------------
@@ -530,7 +528,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
         }
         // the next head's X, dY and per-token terms load while this head is computed
         TileRegs<TI, kBT, P, 256> xr, dyr;
-        float pcs = 0.f, pcp = 0.f, pdt = 0.f;  // token t0 + (tid & 63) of the prefetched head
+        // token t0 + (tid & 63) of the prefetched head; dt as its raw bits (0 past the end),
+        // converted where it is used, and every load unconditional, so that no wait for it
+        // sits under a branch or right after the load
+        float pcs = 0.f, pcp = 0.f;
+        uint32_t pdt = 0;
+        const rsrc_t rdt = make_rsrc(reinterpret_cast<const char *>(a.dt) + (size_t)b * T * H * ES,
+                                     (uint32_t)((size_t)T * H * ES));
         auto issue = [&](int k) {
             const int h = g * HG + blk * hpb + k;
             const size_t bh = (size_t)b * H + h;
@@ -540,7 +544,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             const int t = t0 + (tid & 63);
             pcs = a.cs2[bh * a.Tpad + t];
             pcp = a.dtf[bh * a.Tpad + t];
-            pdt = t < T ? Tr::to_f32(reinterpret_cast<const TI *>(a.dt)[((size_t)b * T + t) * H + h]) : 0.f;
+            const uint32_t od = (uint32_t)(((size_t)t * H + h) * ES);
+            if constexpr (ES == 2) pdt = buf_ld16(rdt, od);
+            else pdt = buf_ld32(rdt, od);
         };
         issue(0);
         for (int k = 0; k < hpb; ++k) {
@@ -552,10 +558,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             const float Dh = a.D[h];
             const uint32_t xo = (uint32_t)(((size_t)t0 * H + h) * P * ES);
             __syncthreads();  // the previous head's reads are done
-            if (tid < kBT) {
-                CS[tid] = pcs;
-                CP[tid] = pcp;
-                DT[tid] = pdt;
+            {
+                // the four role-A wavefronts write the same 64 values
+                const uint32_t u = pdt;
+                CS[tid & 63] = pcs;
+                CP[tid & 63] = pcp;
+                DT[tid & 63] = ES == 2 ? __uint_as_float(u << 16) : __uint_as_float(u);
             }
             xr.template store_T<false>(XT, T_LD, rt, [](int) { return 1.f; });
             xr.store_N(XN, P_LD, rt);
@@ -571,6 +579,14 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                 dt_o[i] = DT[16 * w + 4 * kg + i];
             }
             // ---- y' (scan output) and v = ds B, both [t][p] ----
+            // Lambda at the tile's end is <E, state after the tile>; the tokens' part of that
+            // state, sum_j 2^{cs_e - cs'_j} x_j B_j^T, contributes sum_j 2^{cs_e - cs'_j} x_j.(E B_j),
+            // formed here from E B_j before it is scaled into v (role B adds the entering
+            // state's part)
+            float wl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wl[i] = fast_exp2(cs_e - CP[16 * w + 4 * kg + i]);
+            float lam = 0.f;
             f32x4 ay[PB], av[PB];
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) {
@@ -581,6 +597,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     ay[pb] = Tr::mma(cw[kk], Tr::lds_frag(HN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), ay[pb]);
                     av[pb] = Tr::mma(bw[kk], Tr::lds_frag(EN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), av[pb]);
                 }
+                TI xl[4];
+                lds_ld4<TI>(xl, XT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lam += wl[i] * Tr::to_f32(xl[i]) * av[pb][i];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     ay[pb][i] *= fast_exp2(cs_o[i] - cs_r);
@@ -645,6 +665,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     a.xybuf[o] = sxy[i];
                 }
             }
+#pragma unroll
+            for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
+            // shares 0-3 of Lambda at the tile's end, one per wavefront (k_bwd_fin adds the 8
+            // shares in a fixed order)
+            if (lane == 0) a.lamb[(bh * a.ntiles + tau) * 8 + w] = lam;
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             constexpr int VPR = P * ES / 16;
             for (int v = lane; v < 16 * VPR; v += 64) {
@@ -683,8 +708,31 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             hr.template store_T<false>(HT, P_LD, rt, [](int) { return 1.f; });
             er.store_N(EN, N_LD, rt);
             er.template store_T<false>(ET, P_LD, rt, [](int) { return 1.f; });
+            // the entering state's part of Lambda at the tile's end: 2^{cs_e - cs_r} <E, h>, from
+            // the loaded pieces (h and E are loaded with the same offsets; spare units read 0)
+            float lam = 0.f;
+#pragma unroll
+            for (int kq = 0; kq < decltype(hr)::K; ++kq)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const frag hv = hr.v[kq][i], ev = er.v[kq][i];
+                    if constexpr (ES == 2) {
+                        // pairs straight from the packed registers (v_dot2c_f32_bf16)
+#define SSD_DOT2(e)                                                                                \
+    lam = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(hv, hv, e, e + 1),                   \
+                                          __builtin_shufflevector(ev, ev, e, e + 1), lam, false)
+                        SSD_DOT2(0); SSD_DOT2(2); SSD_DOT2(4); SSD_DOT2(6);
+#undef SSD_DOT2
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) lam += hv[e] * ev[e];
+                    }
+                }
             __syncthreads();
             issue(min(k + 1, hpb - 1));
+#pragma unroll
+            for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
+            if (lane == 0) a.lamb[(bh * a.ntiles + tau) * 8 + 4 + w] = fast_exp2(cs_e - cs_r) * lam;
             const float cs_t = CS[trow];
             float cs_o[4], dt_o[4];
 #pragma unroll
@@ -810,7 +858,7 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdFinArgs a) {
         if (lane + m < 64) run += v;
     }
     {
-        const float *lp = a.lamb + wid * 8;  // the state pass's 8 wavefront shares
+        const float *lp = a.lamb + wid * 8;  // k_bwd_tile's 8 wavefront shares
         run += ((lp[0] + lp[1]) + (lp[2] + lp[3])) + ((lp[4] + lp[5]) + (lp[6] + lp[7]));
     }
     float sdA = 0.f, sdD = 0.f;
@@ -919,18 +967,19 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
         StatePassArgs sp = {};
         sp.cs2 = f.cs2; sp.dtf = f.dtf; sp.H = (int)f.H; sp.G = (int)f.G; sp.T = (int)f.T;
         sp.Tpad = (int)f.Tpad; sp.ntiles = ntiles; sp.tpc = (int)(f.Q / kBT);
-        const dim3 grid_bh((unsigned)(f.batch * f.H));
-        sp.U = w.dY; sp.V = f.C; sp.init = w.dF; sp.Sst = w.Est; sp.out = w.dinit;
-        if (launch(k_state_pass<TI, P, N, true>, grid_bh, dim3(512), s, sp) != hipSuccess) return SSD_ERR_HIP;
-        sp.U = f.X; sp.V = f.B; sp.init = f.init; sp.Sst = w.Hst; sp.out = nullptr;
-        sp.Est = w.Est; sp.lamb = w.lamb;
-        if (launch(k_state_pass<TI, P, N, false>, grid_bh, dim3(512), s, sp) != hipSuccess) return SSD_ERR_HIP;
+        const int nbh = (int)(f.batch * f.H);
+        StatePassArgs rev = sp, fwd = sp;
+        rev.U = w.dY; rev.V = f.C; rev.init = w.dF; rev.Sst = w.Est; rev.out = w.dinit;
+        fwd.U = f.X; fwd.V = f.B; fwd.init = f.init; fwd.Sst = w.Hst; fwd.out = nullptr;
+        if (launch(k_state_passes<TI, P, N>, dim3((unsigned)(2 * nbh)), dim3(64 * SP_NW), s, rev, fwd, nbh) !=
+            hipSuccess)
+            return SSD_ERR_HIP;
         BwdTileArgs ta = {};
         ta.X = f.X; ta.dY = w.dY; ta.B = f.B; ta.C = f.C; ta.dt = f.dt; ta.D = f.D;
         ta.Hst = w.Hst; ta.Est = w.Est; ta.cs2 = f.cs2; ta.dtf = f.dtf;
         ta.dX = w.dX; ta.rbuf = w.rbuf; ta.qbuf = w.qbuf; ta.xybuf = w.xybuf; ta.dBp = w.dBp; ta.dCp = w.dCp;
         ta.H = (int)f.H; ta.G = (int)f.G; ta.T = (int)f.T; ta.Tpad = (int)f.Tpad; ta.ntiles = ntiles;
-        ta.tpc = (int)(f.Q / kBT); ta.nblk = w.nblk;
+        ta.tpc = (int)(f.Q / kBT); ta.nblk = w.nblk; ta.lamb = w.lamb;
         const int64_t tiles = f.batch * ntiles * f.G * w.nblk;
         if (launch(k_bwd_tile<TI, P, N>, dim3((unsigned)tiles), dim3(512), s, ta) != hipSuccess) return SSD_ERR_HIP;
         BwdFinArgs fa = {};

@@ -98,9 +98,6 @@ struct StatePassArgs {          // k_state_pass
     const float *init;          // state before the first tile walked (fp32), or null
     void *Sst;                  // (batch, H, ntiles, P, N) storage type: the state entering each tile
     float *out;                 // state after the last tile walked (fp32), or null
-    const void *Est;            // forward pass: the adjoints arriving at each tile (storage type)
-    float *lamb;                // forward pass: (batch, H, ntiles, 8) per-wavefront shares of
-                                // <E_tile, state after the tile>
     int H, G, T, Tpad, ntiles, tpc;  // tpc: 64-token tiles per chunk
 };
 
@@ -112,6 +109,8 @@ struct BwdTileArgs {            // k_bwd_tile
     void *dX;
     float *rbuf, *qbuf, *xybuf; // per (batch, head, token): x.v, dy.y' - dt x.v, dy.x
     float *dBp, *dCp;           // (batch, Tpad, nblk, G, N) partial sums over head blocks
+    float *lamb;                // (batch, H, ntiles, 8) per-wavefront shares of
+                                // <E_tile, state after the tile>
     int H, G, T, Tpad, ntiles, tpc, nblk;
 };
 
