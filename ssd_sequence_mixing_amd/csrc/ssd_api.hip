@@ -128,10 +128,12 @@ struct BwdLayout {
 };
 
 // Head blocks per group: the fewest (a divisor of the group's head count)
-// that give at least two work-groups per CU.
+// that give one work-group per CU (256 on this part; k_bwd_tile takes a CU's
+// LDS). Fewer blocks mean fewer dB / dC partials and less per-block staging
+// (at the 1.3B shape two blocks of 32 heads beat four of 16 by ~10 us).
 int bwd_blocks(int64_t batch, int64_t ntiles, int64_t G, int64_t HG) {
     for (int64_t k = 1; k <= HG; ++k)
-        if (HG % k == 0 && batch * ntiles * G * k >= 512) return (int)k;
+        if (HG % k == 0 && batch * ntiles * G * k >= 256) return (int)k;
     return (int)HG;
 }
 

@@ -225,6 +225,131 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         return reinterpret_cast<u32x4 *>(XCH + slot * Cfg::XCH_BYTES + ((w * XF + f) * 64 + lane) * 16);
     };
 
+    // X staging (units of 4 tokens x 4 columns, loaded two tiles ahead, each
+    // role lane st taking the same units): the output waves' job, or the state
+    // waves' when the input convolution is fused in (it would otherwise sit on
+    // the output waves, the role every tile waits for)
+    constexpr bool kXS = kConv;
+    uint32_t vx[RX];
+#pragma unroll
+    for (int k = 0; k < RX; ++k) {
+        const int u = st + 256 * k;
+        vx[k] = oob_if(u >= Cfg::UX, (uint32_t)(4 * rs_unit_tq(u)) * x_tok + (uint32_t)(8 * rs_unit_col(u)));
+    }
+    u32x2 xr[kDepth][RX][4];
+    // input convolution: the 3 tokens before each unit, and the unit's
+    // columns' taps and bias (a lane's units keep their columns on every tile)
+    u32x2 xhalo[kDepth][RX][kConv ? 3 : 1];
+    f32x4 ctap[RX][kConv ? 4 : 1];
+    float cbias[RX][kConv ? 4 : 1];
+    auto init_conv = [&]() __attribute__((always_inline)) {
+        if constexpr (kConv) {
+#pragma unroll
+            for (int k = 0; k < RX; ++k) {
+                const int u = st + 256 * k;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int col = h * P + p0 + (u < Cfg::UX ? 4 * rs_unit_col(u) + e : 0);
+                    ctap[k][e] = *reinterpret_cast<const f32x4 *>(a.conv_w + 4 * (size_t)col);
+                    cbias[k][e] = a.conv_b ? a.conv_b[col] : 0.f;
+                }
+            }
+        }
+    };
+    auto issue_x = [&](int tt, auto Sc) __attribute__((always_inline)) {
+        constexpr int Sx = decltype(Sc)::value;
+        const uint32_t sx = (uint32_t)tt * x_tok + hp0;
+#pragma unroll
+        for (int k = 0; k < RX; ++k) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xr[Sx][k][i] = __builtin_amdgcn_raw_buffer_load_b64(rx, vx[k] + i * x_tok, sx, 0);
+            if constexpr (kConv) {
+                const int u = st + 256 * k;
+                const int row0 = tt + 4 * rs_unit_tq(u) - 3;  // token of halo row 0 (before the sequence: 0)
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+                    xhalo[Sx][k][i] = __builtin_amdgcn_raw_buffer_load_b64(
+                        rx, oob_if(u >= Cfg::UX || row0 + i < 0,
+                                   (uint32_t)(row0 + i) * x_tok + hp0 + (uint32_t)(8 * rs_unit_col(u))),
+                        0, 0);
+            }
+        }
+    };
+    // writes the weighted X of a tile (and the plain X in per-element
+    // tiles) into X slot `slot`; cr / ce: cs2 before the tile and at its
+    // last token, cpk(k): cs' of unit k's 4 tokens
+    auto stage_x = [&](auto Sc, int slot, float cr, float ce, auto &&cpk) __attribute__((always_inline)) {
+        constexpr int Sx = decltype(Sc)::value;
+        const bool fd = (cr - ce <= kRsFDMax);
+        bf16 *XWs = XW + slot * PW * LD;
+        bf16 *XRs = reinterpret_cast<bf16 *>(smem + Cfg::XR_OFF + slot * Cfg::XR_BYTES);
+#pragma unroll
+        for (int k = 0; k < RX; ++k) {
+            const int u = st + 256 * k;
+            if (u >= Cfg::UX) continue;  // wave-uniform (UX is a multiple of 64)
+            const int tq = rs_unit_tq(u), c4 = rs_unit_col(u);
+            // the unit's 4 tokens x 4 columns (after the input convolution
+            // when there is one, rounded to bf16: the scan's input and the
+            // skip term's)
+            u32x2 xin[4];
+            if constexpr (kConv) {
+                // x' = SiLU(b + w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t)
+                float xo[4][4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float xv[7];  // tokens 4 tq - 3 .. 4 tq + 3 of column 4 c4 + e
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+                        xv[i] = (e & 1) ? bf16_hi(xhalo[Sx][k][i][e >> 1]) : bf16_lo(xhalo[Sx][k][i][e >> 1]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        xv[3 + i] = (e & 1) ? bf16_hi(xr[Sx][k][i][e >> 1]) : bf16_lo(xr[Sx][k][i][e >> 1]);
+                    const f32x4 w = ctap[k][e];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = cbias[k][e] + w[0] * xv[i] + w[1] * xv[i + 1] + w[2] * xv[i + 2] +
+                                        w[3] * xv[i + 3];
+                        xo[i][e] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xin[i] = u32x2{pack_bf16x2(xo[i][0], xo[i][1]), pack_bf16x2(xo[i][2], xo[i][3])};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xin[i] = xr[Sx][k][i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<u32x2 *>(XRs + (4 * tq + i) * Cfg::XRLD + 4 * c4) = xin[i];
+            // factored tiles: X~_j = 2^(cs_r - cs'_j) x_j; the others: x_j as it is
+            const f32x4 cp = cpk(k);
+            float cw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cw[i] = fd ? fast_exp2(cr - cp[i]) : 1.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // column 4 c4 + e, its 4 tokens 4 tq .. 4 tq + 3: half of 16-byte piece tq / 2
+                float xv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[i] = (e & 1) ? bf16_hi(xin[i][e >> 1]) : bf16_lo(xin[i][e >> 1]);
+                *reinterpret_cast<u32x2 *>(XWs + xw_off(4 * c4 + e, tq >> 1) + 4 * (tq & 1)) =
+                    u32x2{pack_bf16x2(xv[0] * cw[0], xv[1] * cw[1]), pack_bf16x2(xv[2] * cw[2], xv[3] * cw[3])};
+            }
+        }
+    };
+    // stages a tile whose log-decays are read from global memory
+    auto stage_x_global = [&](auto Sc, int tau) __attribute__((always_inline)) {
+        const int tt = tau * TT;
+        const float cr = (tt % Q == 0) ? 0.f : cs_row[tt - 1];
+        const float ce = cs_row[tt + TT - 1];
+        stage_x(Sc, tau & 1, cr, ce, [&](int k) __attribute__((always_inline)) {
+            return *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * rs_unit_tq(st + 256 * k));
+        });
+    };
+
+
     if (wv < 4) {
         // ============================ output waves ============================
         const float Dh = a.D[h];
@@ -276,124 +401,6 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 *reinterpret_cast<u32x4 *>(CLw + (32 * ah + 16 * bh + u / BCW) * Cfg::CLD + 8 * (u % BCW)) = crg[k];
             }
         };
-        // X staging: units of 4 tokens x 4 columns, loaded two tiles ahead
-        uint32_t vx[RX];
-#pragma unroll
-        for (int k = 0; k < RX; ++k) {
-            const int u = st + 256 * k;
-            vx[k] = oob_if(u >= Cfg::UX, (uint32_t)(4 * rs_unit_tq(u)) * x_tok + (uint32_t)(8 * rs_unit_col(u)));
-        }
-        u32x2 xr[kDepth][RX][4];
-        // input convolution: the 3 tokens before each unit, and the unit's
-        // columns' taps and bias (a lane's units keep their columns on every tile)
-        u32x2 xhalo[kDepth][RX][kConv ? 3 : 1];
-        f32x4 ctap[RX][kConv ? 4 : 1];
-        float cbias[RX][kConv ? 4 : 1];
-        if constexpr (kConv) {
-#pragma unroll
-            for (int k = 0; k < RX; ++k) {
-                const int u = st + 256 * k;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int col = h * P + p0 + (u < Cfg::UX ? 4 * rs_unit_col(u) + e : 0);
-                    ctap[k][e] = *reinterpret_cast<const f32x4 *>(a.conv_w + 4 * (size_t)col);
-                    cbias[k][e] = a.conv_b ? a.conv_b[col] : 0.f;
-                }
-            }
-        }
-        auto issue_x = [&](int tt, auto Sc) __attribute__((always_inline)) {
-            constexpr int Sx = decltype(Sc)::value;
-            const uint32_t sx = (uint32_t)tt * x_tok + hp0;
-#pragma unroll
-            for (int k = 0; k < RX; ++k) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    xr[Sx][k][i] = __builtin_amdgcn_raw_buffer_load_b64(rx, vx[k] + i * x_tok, sx, 0);
-                if constexpr (kConv) {
-                    const int u = st + 256 * k;
-                    const int row0 = tt + 4 * rs_unit_tq(u) - 3;  // token of halo row 0 (before the sequence: 0)
-#pragma unroll
-                    for (int i = 0; i < 3; ++i)
-                        xhalo[Sx][k][i] = __builtin_amdgcn_raw_buffer_load_b64(
-                            rx, oob_if(u >= Cfg::UX || row0 + i < 0,
-                                       (uint32_t)(row0 + i) * x_tok + hp0 + (uint32_t)(8 * rs_unit_col(u))),
-                            0, 0);
-                }
-            }
-        };
-        // writes the weighted X of a tile (and the plain X in per-element
-        // tiles) into X slot `slot`; cr / ce: cs2 before the tile and at its
-        // last token, cpk(k): cs' of unit k's 4 tokens
-        auto stage_x = [&](auto Sc, int slot, float cr, float ce, auto &&cpk) __attribute__((always_inline)) {
-            constexpr int Sx = decltype(Sc)::value;
-            const bool fd = (cr - ce <= kRsFDMax);
-            bf16 *XWs = XW + slot * PW * LD;
-            bf16 *XRs = reinterpret_cast<bf16 *>(smem + Cfg::XR_OFF + slot * Cfg::XR_BYTES);
-#pragma unroll
-            for (int k = 0; k < RX; ++k) {
-                const int u = st + 256 * k;
-                if (u >= Cfg::UX) continue;  // wave-uniform (UX is a multiple of 64)
-                const int tq = rs_unit_tq(u), c4 = rs_unit_col(u);
-                // the unit's 4 tokens x 4 columns (after the input convolution
-                // when there is one, rounded to bf16: the scan's input and the
-                // skip term's)
-                u32x2 xin[4];
-                if constexpr (kConv) {
-                    // x' = SiLU(b + w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t)
-                    float xo[4][4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float xv[7];  // tokens 4 tq - 3 .. 4 tq + 3 of column 4 c4 + e
-#pragma unroll
-                        for (int i = 0; i < 3; ++i)
-                            xv[i] = (e & 1) ? bf16_hi(xhalo[Sx][k][i][e >> 1]) : bf16_lo(xhalo[Sx][k][i][e >> 1]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            xv[3 + i] = (e & 1) ? bf16_hi(xr[Sx][k][i][e >> 1]) : bf16_lo(xr[Sx][k][i][e >> 1]);
-                        const f32x4 w = ctap[k][e];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const float v = cbias[k][e] + w[0] * xv[i] + w[1] * xv[i + 1] + w[2] * xv[i + 2] +
-                                            w[3] * xv[i + 3];
-                            xo[i][e] = v * __builtin_amdgcn_rcpf(1.f + fast_exp2(-kLog2e * v));
-                        }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        xin[i] = u32x2{pack_bf16x2(xo[i][0], xo[i][1]), pack_bf16x2(xo[i][2], xo[i][3])};
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) xin[i] = xr[Sx][k][i];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    *reinterpret_cast<u32x2 *>(XRs + (4 * tq + i) * Cfg::XRLD + 4 * c4) = xin[i];
-                // factored tiles: X~_j = 2^(cs_r - cs'_j) x_j; the others: x_j as it is
-                const f32x4 cp = cpk(k);
-                float cw[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) cw[i] = fd ? fast_exp2(cr - cp[i]) : 1.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // column 4 c4 + e, its 4 tokens 4 tq .. 4 tq + 3: half of 16-byte piece tq / 2
-                    float xv[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) xv[i] = (e & 1) ? bf16_hi(xin[i][e >> 1]) : bf16_lo(xin[i][e >> 1]);
-                    *reinterpret_cast<u32x2 *>(XWs + xw_off(4 * c4 + e, tq >> 1) + 4 * (tq & 1)) =
-                        u32x2{pack_bf16x2(xv[0] * cw[0], xv[1] * cw[1]), pack_bf16x2(xv[2] * cw[2], xv[3] * cw[3])};
-                }
-            }
-        };
-        // stages a tile whose log-decays are read from global memory
-        auto stage_x_global = [&](auto Sc, int tau) __attribute__((always_inline)) {
-            const int tt = tau * TT;
-            const float cr = (tt % Q == 0) ? 0.f : cs_row[tt - 1];
-            const float ce = cs_row[tt + TT - 1];
-            stage_x(Sc, tau & 1, cr, ce, [&](int k) __attribute__((always_inline)) {
-                return *reinterpret_cast<const f32x4 *>(cp_row + tt + 4 * rs_unit_tq(st + 256 * k));
-            });
-        };
-
         // The output rows of tile tau, staged in LDS slot tau % 2 by all four
         // output waves, leave as whole rows at the start of tile tau + 1: 16
         // rows per wave, PW / 8 lanes per row.
@@ -433,10 +440,12 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
         const int tile_b = cb * NT;
         load_z(tile_b);
         load_cs(tile_b * TT);
-        issue_x(tile_b * TT, std::integral_constant<int, 0>{});
+        if constexpr (!kXS) issue_x(tile_b * TT, std::integral_constant<int, 0>{});
         store_cs(tile_b & 1);
-        stage_x_global(std::integral_constant<int, 0>{}, tile_b);
-        if constexpr (kDepth == 2) issue_x(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
+        if constexpr (!kXS) {
+            stage_x_global(std::integral_constant<int, 0>{}, tile_b);
+            if constexpr (kDepth == 2) issue_x(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
+        }
         load_g(tile_b);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -449,7 +458,8 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 const int tau = c * NT + I;
                 const int slot = tau & 1;
                 load_cs(min(tau + 1, last_tile) * TT);
-                issue_x(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
+                if constexpr (!kXS)
+                    issue_x(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
                 // the previous tile's output (its rows were completed before the
                 // barrier), then the gate values of this tile's rows
                 if (tau > cb * NT) {
@@ -480,7 +490,7 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                 for (int ib = 0; ib < IB; ++ib) cs_i[ib] = CSL[tile0 + 32 * ah + 16 * ib + r];
                 // the next tile's weighted X into the other slots, while this
                 // tile's operands arrive (its X slot was last read a tile ago)
-                {
+                if constexpr (!kXS) {
                     constexpr int SxN = kDepth == 2 ? ((I + 1) & 1) : 0;
                     if constexpr (kCsLds) {
                         // (after the last tile this stages data nobody reads)
@@ -700,10 +710,16 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
             });
         };
         const int tile_b = cb * NT;
+        if constexpr (kXS) init_conv();
         publish(tile_b & 1);
         issue_b(tile_b * TT, std::integral_constant<int, 0>{});
+        if constexpr (kXS) issue_x(tile_b * TT, std::integral_constant<int, 0>{});
         stage_b_global(std::integral_constant<int, 0>{}, tile_b);
-        if constexpr (kDepth == 2) issue_b(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
+        if constexpr (kXS) stage_x_global(std::integral_constant<int, 0>{}, tile_b);
+        if constexpr (kDepth == 2) {
+            issue_b(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
+            if constexpr (kXS) issue_x(min(tile_b + 1, last_tile) * TT, std::integral_constant<int, 1>{});
+        }
         __syncthreads();
         float csn = 0.f, cpn = 0.f;
         for (int c = cb; c < ce; ++c) {
@@ -723,7 +739,9 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                     cpn = cp_row[kn];
                 }
                 issue_b(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
-                // the next tile's B^T into the other slot first (it was last read a
+                if constexpr (kXS)
+                    issue_x(min(tau + kDepth, last_tile) * TT, std::integral_constant<int, kDepth == 2 ? (I & 1) : 0>{});
+                // the next tile's B^T (and X) into the other slots first (last read a
                 // tile ago), while the output waves read their operands
                 {
                     constexpr int SxN = kDepth == 2 ? ((I + 1) & 1) : 0;
@@ -732,12 +750,14 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
                         const float *CSn = (I + 1 < NT) ? CSL : CSB + ((c + 1 - cb) & 1) * 2 * Q;
                         const int tn = ((I + 1) % NT) * TT;
                         const float cr = (I + 1 < NT) ? CSn[tn - 1] : 0.f;
-                        stage_b(std::integral_constant<int, SxN>{}, (tau + 1) & 1, cr, CSn[tn + TT - 1],
-                                [&](int k) __attribute__((always_inline)) {
-                                    return *reinterpret_cast<const f32x4 *>(CSn + Q + tn + 4 * rs_unit_tq(st + 256 * k));
-                                });
+                        auto cpk = [&](int k) __attribute__((always_inline)) {
+                            return *reinterpret_cast<const f32x4 *>(CSn + Q + tn + 4 * rs_unit_tq(st + 256 * k));
+                        };
+                        stage_b(std::integral_constant<int, SxN>{}, (tau + 1) & 1, cr, CSn[tn + TT - 1], cpk);
+                        if constexpr (kXS) stage_x(std::integral_constant<int, SxN>{}, (tau + 1) & 1, cr, CSn[tn + TT - 1], cpk);
                     } else {
                         stage_b_global(std::integral_constant<int, SxN>{}, min(tau + 1, last_tile));
+                        if constexpr (kXS) stage_x_global(std::integral_constant<int, SxN>{}, min(tau + 1, last_tile));
                     }
                 }
                 // state update: factored tiles h <- dec (h + B^T X~), the others

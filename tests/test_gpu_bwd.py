@@ -160,15 +160,16 @@ def test_bwd_deterministic(ssd):
 @pytest.mark.parametrize("G,P,N", [(1, 32, 32), (2, 64, 64)])
 def test_bwd_several_heads_per_block(ssd, G, P, N):
     """Batch 4, T 2048, 16 heads: the backward sums dB and dC over blocks of
-    4 heads of a group in registers (4 blocks of 4 heads with one group, 2 of 4
-    with two); every gradient is compared element by element."""
+    heads of a group in registers (2 blocks of 8 heads with one group, whose
+    partials are then added; 1 block of 8 per group with two); every gradient
+    is compared element by element."""
     check(ssd, shape("l1p3b_bf16", batch=4, seqlen=2048, nheads=16, headdim=P, dstate=N, ngroups=G,
                      seed=92), 256, False, True)
 
 
 @pytest.mark.timeout(600)
 def test_bwd_full_size_1p3b_layer(ssd):
-    """Batch 4, T 2048, 64 heads, P 64, N 128 (16 heads per block): every
+    """Batch 4, T 2048, 64 heads, P 64, N 128 (32 heads per block): every
     gradient element by element. The oracle runs one head at a time (dX, ddt,
     dA, the initial-state gradient of a head depend on that head alone) and
     dB, dC are the sums of the per-head contributions over the group."""
