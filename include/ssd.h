@@ -318,10 +318,13 @@ ssd_status ssd_step_fused(float *state, void *conv_state, const void *x, const f
  *   d_initial_state (batch, nheads, headdim, dstate) float32, or NULL (not written)
  *
  * Arithmetic in fp32 from the stored inputs; the per-tile states handed
- * between the passes are kept in the storage type. Supported: bf16 with
- * headdim in {32, 64} and dstate in {32, 64, 128}; float32 with (headdim,
- * dstate) in {(32, 32), (32, 64), (64, 32)}; other shapes return
- * SSD_ERR_UNSUPPORTED. Workspace
+ * between the passes are kept in the storage type. Supported: headdim in
+ * {32, 64} with dstate in {32, 64, 128, 256} for bf16 and {32, 64, 128} for
+ * float32; other shapes return SSD_ERR_UNSUPPORTED. Where the tile kernel's
+ * operands for the whole state do not fit one CU's LDS (bf16 dstate 256,
+ * float32 headdim 64 with dstate 64 or 128, float32 headdim 32 with dstate
+ * 128), it takes the state's columns in 2 or 4 slices and adds their parts
+ * (dX through an fp32 copy in the workspace) in a fixed order. Workspace
  * from ssd_chunk_scan_bwd_workspace_bytes ((size_t)-1 for an unsupported
  * shape), 256-byte aligned; at the 1.3B-layer shape it holds two bf16 copies
  * of the state per 64 tokens (134 MB each). Alignment, stream semantics and

@@ -123,8 +123,8 @@ ssd_status empty_final_state(float *final_state, const float *init, int64_t n, h
 // dB / dC.
 struct BwdLayout {
     FwdLayout fl;
-    int nblk;
-    int64_t ntiles, st_bytes, lamb_bytes, share_bytes, tok_bytes, part_bytes, total;
+    int nblk, ns;  // head blocks per group, n slices of k_bwd_tile
+    int64_t ntiles, st_bytes, lamb_bytes, share_bytes, tok_bytes, rq_bytes, part_bytes, dxp_bytes, total;
 };
 
 // Head blocks per group: the fewest (a divisor of the group's head count)
@@ -146,18 +146,23 @@ ssd_status check_bwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     const int64_t Tpad = lay->fl.Tpad;
     lay->ntiles = Tpad / 64;
     // (batch x heads is bounded by the forward check, so this product fits)
-    if (batch * nheads * lay->ntiles > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    lay->ns = ssd::bwd_nslices((ssd_dtype)dtype, headdim, dstate);
+    // k_bwd_tile's grid (batch x tiles x groups x head blocks x n slices) is at most this
+    if (batch * nheads * lay->ntiles * lay->ns > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
     lay->nblk = bwd_blocks(batch, lay->ntiles, ngroups, nheads / ngroups);
+    const int64_t ns = lay->ns;
     lay->st_bytes = align256(batch * nheads * lay->ntiles * headdim * dstate * es);
     lay->lamb_bytes = align256(batch * nheads * lay->ntiles * 4);
-    lay->share_bytes = align256(batch * nheads * lay->ntiles * 8 * 4);  // Lambda shares, 8 per tile
+    lay->share_bytes = align256(batch * nheads * lay->ntiles * ns * 8 * 4);  // Lambda shares, 8 per tile and slice
     lay->tok_bytes = align256(batch * nheads * Tpad * 4);
+    lay->rq_bytes = align256(ns * batch * nheads * Tpad * 4);  // x.v and the dy.y' scalar, one part per slice
     lay->part_bytes = align256(batch * Tpad * lay->nblk * ngroups * dstate * 4);
+    lay->dxp_bytes = ns > 1 ? align256(ns * batch * seqlen * nheads * headdim * 4) : 0;
     const int64_t fwd = 2 * lay->fl.cs_bytes + lay->fl.g_bytes + lay->fl.seg_bytes;
     lay->total = (batch == 0 || seqlen == 0)
                      ? 0
-                     : fwd + 2 * lay->st_bytes + lay->share_bytes + 2 * lay->lamb_bytes + 3 * lay->tok_bytes +
-                           2 * lay->part_bytes;
+                     : fwd + 2 * lay->st_bytes + lay->share_bytes + 2 * lay->lamb_bytes + 2 * lay->rq_bytes +
+                           lay->tok_bytes + 2 * lay->part_bytes + lay->dxp_bytes;
     return SSD_OK;
 }
 
@@ -501,11 +506,12 @@ ssd_status ssd_chunk_scan_bwd(const void *X, const void *dt, const float *A, con
     w.lamb = reinterpret_cast<float *>(ws); ws += lay.share_bytes;
     w.dApart = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
     w.dDpart = reinterpret_cast<float *>(ws); ws += lay.lamb_bytes;
-    w.rbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
-    w.qbuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
+    w.rbuf = reinterpret_cast<float *>(ws); ws += lay.rq_bytes;
+    w.qbuf = reinterpret_cast<float *>(ws); ws += lay.rq_bytes;
     w.xybuf = reinterpret_cast<float *>(ws); ws += lay.tok_bytes;
     w.dBp = reinterpret_cast<float *>(ws); ws += lay.part_bytes;
-    w.dCp = reinterpret_cast<float *>(ws);
+    w.dCp = reinterpret_cast<float *>(ws); ws += lay.part_bytes;
+    w.dXp = lay.dxp_bytes ? reinterpret_cast<float *>(ws) : nullptr;
     w.nblk = lay.nblk;
     w.dY = dY; w.dF = d_final_state; w.dX = dX; w.ddt = ddt; w.dB = dB; w.dC = dC;
     w.dA = dA; w.dD = dD; w.dinit = d_initial_state;

@@ -418,11 +418,18 @@ struct BwdCfg {
 // (16 token rows each) form y', v, dX and the per-token scalars; waves 4-7
 // (same rows) form x.dy products, dC and dB. The roles share no results, so
 // the two waves on each SIMD overlap.
-template <typename TI, int P, int N>
+// Where the LDS of one work-group cannot hold the whole n axis, NS = N / NL
+// work-groups take a slice of NL state columns each. Every sum over n (y', v,
+// C B^T, and through them dX, the per-token scalars and Lambda's parts) is
+// then a sum of the slices' partial results, which they write separately
+// (dX in fp32) for k_bwd_fin and k_bwd_dx to add in a fixed order; dB and dC
+// are per n and come out whole.
+template <typename TI, int P, int N, int NL>
 __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
-    using Cfg = BwdCfg<TI, P, N>;
+    using Cfg = BwdCfg<TI, P, NL>;
+    constexpr int NS = N / NL;
     constexpr int ES = Cfg::ES, PB = Cfg::PB, NB = Cfg::NB, NK = Cfg::NK, KP = Cfg::KP;
     constexpr int T_LD = Cfg::T_LD, P_LD = Cfg::P_LD, N_LD = Cfg::N_LD;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
@@ -434,6 +441,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 
     const int H = a.H, G = a.G, T = a.T, HG = H / G, nblk = a.nblk, hpb = HG / nblk;
     int x = blockIdx.x;
+    const int sl = x % NS;
+    x /= NS;
     const int blk = x % nblk;
     x /= nblk;
     const int g = x % G;
@@ -441,6 +450,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
     const int tau = x % a.ntiles;
     const int b = x / a.ntiles;
     const int t0 = tau * kBT;
+    const int n0 = sl * NL;  // this work-group's state columns n0 .. n0 + NL - 1
+    const size_t tsl = (size_t)sl * a.tok_stride;  // its per-token partials
+    const size_t tsl_x = (size_t)sl * a.dx_stride;  // and its part of dx (NS > 1)
     constexpr int NTH = 512;
     const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, kg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -457,9 +469,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
     const uint32_t b_tok = (uint32_t)(G * N * ES), x_tok = (uint32_t)(H * P * ES);
 
     // ---- per tile, shared by the block's heads ----
-    stage_T<TI, kBT, N, NTH, false>(rb, (uint32_t)(((size_t)t0 * G + g) * N * ES), b_tok, BT, T_LD, tid,
-                                    [](int) { return 1.f; });
-    stage_T<TI, kBT, N, NTH, false>(rc, (uint32_t)(((size_t)t0 * G + g) * N * ES), b_tok, CT, T_LD, tid,
+    stage_T<TI, kBT, NL, NTH, false>(rb, (uint32_t)((((size_t)t0 * G + g) * N + n0) * ES), b_tok, BT, T_LD, tid,
+                                     [](int) { return 1.f; });
+    stage_T<TI, kBT, NL, NTH, false>(rc, (uint32_t)((((size_t)t0 * G + g) * N + n0) * ES), b_tok, CT, T_LD, tid,
                                     [](int) { return 1.f; });
     const int trow = 16 * w + r;  // this lane's row token for A operands (tile-local)
     const int kc = w / 2;         // the k step holding the diagonal
@@ -500,7 +512,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
         //   g2[ub][i] = C_u . B_t with u = 16 ub + 4 kg + i   (ub >= w)
         frag cw[NK], bw[NK];
         f32x4 g1[4], g2[4];
-        const uint32_t grow = (uint32_t)((t0 * G + g) * N * ES);
+        const uint32_t grow = (uint32_t)(((t0 * G + g) * N + n0) * ES);
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             const uint32_t o = grow + (uint32_t)(16 * w + r) * b_tok + (uint32_t)((32 * kk + 8 * kg) * ES);
@@ -645,7 +657,15 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     sxv[i] += xv * av[pb][i];
                     sdy[i] += dv * ay[pb][i];
                     sxy[i] += dv * xv;
-                    OS[(4 * kg + i) * P_LD + 16 * pb + r] = Tr::from_f32(dt_o[i] * av[pb][i] + Dh * dv);
+                    if constexpr (NS == 1) {
+                        OS[(4 * kg + i) * P_LD + 16 * pb + r] = Tr::from_f32(dt_o[i] * av[pb][i] + Dh * dv);
+                    } else {
+                        // this slice's part of dx in fp32 (the skip term with slice 0's)
+                        const int t = t0 + 16 * w + 4 * kg + i;
+                        if (t < T)
+                            a.dXp[tsl_x + (((size_t)b * T + t) * H + h) * P + 16 * pb + r] =
+                                dt_o[i] * av[pb][i] + (sl == 0 ? Dh * dv : 0.f);
+                    }
                 }
             }
 #pragma unroll
@@ -660,23 +680,25 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const size_t o = bh * a.Tpad + t0 + 16 * w + 4 * kg + i;
-                    a.rbuf[o] = sxv[i];
-                    a.qbuf[o] = sdy[i] - dt_o[i] * sxv[i];
-                    a.xybuf[o] = sxy[i];
+                    a.rbuf[tsl + o] = sxv[i];
+                    a.qbuf[tsl + o] = sdy[i] - dt_o[i] * sxv[i];
+                    if (sl == 0) a.xybuf[o] = sxy[i];
                 }
             }
 #pragma unroll
             for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
             // shares 0-3 of Lambda at the tile's end, one per wavefront (k_bwd_fin adds the 8
             // shares in a fixed order)
-            if (lane == 0) a.lamb[(bh * a.ntiles + tau) * 8 + w] = lam;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            constexpr int VPR = P * ES / 16;
-            for (int v = lane; v < 16 * VPR; v += 64) {
-                const int rl = v / VPR, cv = v % VPR;
-                const u32x4 d =
-                    *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(OS + rl * P_LD) + cv * 16);
-                buf_st128(d, rdx, xo + (uint32_t)(16 * w + rl) * x_tok + (uint32_t)(cv * 16));
+            if (lane == 0) a.lamb[((bh * a.ntiles + tau) * NS + sl) * 8 + w] = lam;
+            if constexpr (NS == 1) {
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                constexpr int VPR = P * ES / 16;
+                for (int v = lane; v < 16 * VPR; v += 64) {
+                    const int rl = v / VPR, cv = v % VPR;
+                    const u32x4 d =
+                        *reinterpret_cast<const u32x4 *>(reinterpret_cast<const char *>(OS + rl * P_LD) + cv * 16);
+                    buf_st128(d, rdx, xo + (uint32_t)(16 * w + rl) * x_tok + (uint32_t)(cv * 16));
+                }
             }
         }
     } else {
@@ -687,14 +709,14 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             accb[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
             accc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        TileRegs<TI, P, N, 256> hr, er;
+        TileRegs<TI, P, NL, 256> hr, er;
         auto issue = [&](int k) {
             const int h = g * HG + blk * hpb + k;
             const size_t so = (((size_t)b * H + h) * a.ntiles + tau) * (size_t)(P * N);
-            hr.load(make_rsrc(reinterpret_cast<const TI *>(a.Hst) + so, (uint32_t)(P * N * ES)), 0u,
-                    (uint32_t)(N * ES), rt);
-            er.load(make_rsrc(reinterpret_cast<const TI *>(a.Est) + so, (uint32_t)(P * N * ES)), 0u,
-                    (uint32_t)(N * ES), rt);
+            hr.load(make_rsrc(reinterpret_cast<const TI *>(a.Hst) + so, (uint32_t)(P * N * ES)),
+                    (uint32_t)(n0 * ES), (uint32_t)(N * ES), rt);
+            er.load(make_rsrc(reinterpret_cast<const TI *>(a.Est) + so, (uint32_t)(P * N * ES)),
+                    (uint32_t)(n0 * ES), (uint32_t)(N * ES), rt);
         };
         issue(0);
         for (int k = 0; k < hpb; ++k) {
@@ -732,7 +754,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             issue(min(k + 1, hpb - 1));
 #pragma unroll
             for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
-            if (lane == 0) a.lamb[(bh * a.ntiles + tau) * 8 + 4 + w] = fast_exp2(cs_e - cs_r) * lam;
+            if (lane == 0) a.lamb[((bh * a.ntiles + tau) * NS + sl) * 8 + 4 + w] = fast_exp2(cs_e - cs_r) * lam;
             const float cs_t = CS[trow];
             float cs_o[4], dt_o[4];
 #pragma unroll
@@ -823,7 +845,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const size_t o =
-                    ((((size_t)b * a.Tpad + t0 + 16 * w + 4 * kg + i) * nblk + blk) * G + g) * N + 16 * nb + r;
+                    ((((size_t)b * a.Tpad + t0 + 16 * w + 4 * kg + i) * nblk + blk) * G + g) * N + n0 + 16 * nb + r;
                 a.dBp[o] = accb[nb][i];
                 a.dCp[o] = accc[nb][i];
             }
@@ -850,20 +872,26 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdFinArgs a) {
     const bool real = t < a.T;
     const size_t o = (size_t)bh * a.Tpad + t;
     const size_t od = ((size_t)b * a.T + t) * a.H + h;
-    const float q = real ? a.qbuf[o] : 0.f;
+    // the n slices' parts of the per-token scalars, added in slice order
+    float q = 0.f, rv = 0.f;
+    if (real)
+        for (int sl = 0; sl < a.ns; ++sl) {
+            q += a.qbuf[sl * a.tok_stride + o];
+            rv += a.rbuf[sl * a.tok_stride + o];
+        }
     float run = q;  // suffix sum over the lanes at and after this one
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
         const float v = __shfl_down(run, m);
         if (lane + m < 64) run += v;
     }
-    {
-        const float *lp = a.lamb + wid * 8;  // k_bwd_tile's 8 wavefront shares
+    for (int sl = 0; sl < a.ns; ++sl) {
+        const float *lp = a.lamb + (wid * a.ns + sl) * 8;  // k_bwd_tile's 8 wavefront shares of slice sl
         run += ((lp[0] + lp[1]) + (lp[2] + lp[3])) + ((lp[4] + lp[5]) + (lp[6] + lp[7]));
     }
     float sdA = 0.f, sdD = 0.f;
     if (real) {
-        reinterpret_cast<TI *>(a.ddt)[od] = Traits<TI>::from_f32(a.rbuf[o] + a.A[h] * run);
+        reinterpret_cast<TI *>(a.ddt)[od] = Traits<TI>::from_f32(rv + a.A[h] * run);
         sdA = Traits<TI>::to_f32(reinterpret_cast<const TI *>(a.dt)[od]) * run;
         sdD = a.xybuf[o];
     }
@@ -876,6 +904,17 @@ __global__ __launch_bounds__(256) void k_bwd_fin(BwdFinArgs a) {
         a.dApart[wid] = sdA;
         a.dDpart[wid] = sdD;
     }
+}
+
+// dX from the n slices' fp32 parts, added in slice order, in the storage type.
+template <typename TI>
+__global__ __launch_bounds__(256) void k_bwd_dx(const float *__restrict__ dXp, TI *__restrict__ dX, int64_t n,
+                                                int ns) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;  // n is a multiple of 4 (P is)
+    f32x4 v = *reinterpret_cast<const f32x4 *>(dXp + i);
+    for (int sl = 1; sl < ns; ++sl) v += *reinterpret_cast<const f32x4 *>(dXp + (size_t)sl * n + i);
+    store4<TI>(dX + i, v);
 }
 
 __global__ __launch_bounds__(256) void k_bwd_heads(const float *__restrict__ dApart, const float *__restrict__ dDpart,
@@ -933,28 +972,65 @@ __global__ __launch_bounds__(256) void k_bwd_sum_bc(const float *__restrict__ dB
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+// The n slice of k_bwd_tile: the widest of N, N / 2, N / 4 (at least 32
+// columns) whose work-group fits a CU's LDS; 0 when none does.
+template <typename TI, int P, int N>
+static constexpr int bwd_nl() {
+    if constexpr (BwdCfg<TI, P, N>::kFits) return N;
+    else if constexpr (N >= 64 && BwdCfg<TI, P, N / 2>::kFits) return N / 2;
+    else if constexpr (N >= 128 && BwdCfg<TI, P, N / 4>::kFits) return N / 4;
+    else return 0;
+}
+
+// Shapes the backward covers: k_bwd_tile fits with at most 4 n slices, and the
+// state passes (the whole n axis per work-group) fit LDS and registers (fp32
+// up to N 128).
 template <typename TI, int P, int N>
 static constexpr bool bwd_fits() {
-    return BwdCfg<TI, P, N>::kFits;
+    return bwd_nl<TI, P, N>() > 0 && sizeof(SpLds<TI, P, N>) <= 160 * 1024 && (sizeof(TI) == 2 || N <= 128);
+}
+
+template <typename TI, typename F>
+static auto bwd_shape(int64_t P, int64_t N, F f) {
+    using I32 = std::integral_constant<int, 32>;
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using I256 = std::integral_constant<int, 256>;
+    auto pick = [&](auto Pc) {
+        switch (N) {
+            case 32: return f(Pc, I32{});
+            case 64: return f(Pc, I64{});
+            case 128: return f(Pc, I128{});
+            case 256: return f(Pc, I256{});
+            default: return decltype(f(Pc, I32{})){};
+        }
+    };
+    if (P == 32) return pick(I32{});
+    if (P == 64) return pick(I64{});
+    return decltype(f(I32{}, I32{})){};
 }
 
 template <typename TI>
 static bool bwd_shape_ok(int64_t P, int64_t N) {
-    auto f = [](auto Pc, auto Nc) { return bwd_fits<TI, decltype(Pc)::value, decltype(Nc)::value>(); };
-    using I32 = std::integral_constant<int, 32>;
-    using I64 = std::integral_constant<int, 64>;
-    using I128 = std::integral_constant<int, 128>;
-    if (P == 32 && N == 32) return f(I32{}, I32{});
-    if (P == 32 && N == 64) return f(I32{}, I64{});
-    if (P == 32 && N == 128) return f(I32{}, I128{});
-    if (P == 64 && N == 32) return f(I64{}, I32{});
-    if (P == 64 && N == 64) return f(I64{}, I64{});
-    if (P == 64 && N == 128) return f(I64{}, I128{});
-    return false;
+    return bwd_shape<TI>(P, N, [](auto Pc, auto Nc) {
+        return bwd_fits<TI, decltype(Pc)::value, decltype(Nc)::value>();
+    });
 }
 
 bool bwd_supported(ssd_dtype dt, int64_t P, int64_t N) {
     return dt == SSD_BF16 ? bwd_shape_ok<bf16>(P, N) : bwd_shape_ok<float>(P, N);
+}
+
+template <typename TI>
+static int bwd_ns(int64_t P, int64_t N) {
+    return bwd_shape<TI>(P, N, [](auto Pc, auto Nc) {
+        constexpr int Pv = decltype(Pc)::value, Nv = decltype(Nc)::value, nl = bwd_nl<TI, Pv, Nv>();
+        return nl > 0 ? Nv / nl : 0;
+    });
+}
+
+int bwd_nslices(ssd_dtype dt, int64_t P, int64_t N) {
+    return dt == SSD_BF16 ? bwd_ns<bf16>(P, N) : bwd_ns<float>(P, N);
 }
 
 template <typename TI, int P, int N>
@@ -962,6 +1038,7 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
     if constexpr (!bwd_fits<TI, P, N>()) {
         return SSD_ERR_UNSUPPORTED;
     } else {
+        constexpr int NL = bwd_nl<TI, P, N>(), NS = N / NL;
         const FwdArgs &f = w.f;
         const int ntiles = (int)(f.Tpad / kBT);
         StatePassArgs sp = {};
@@ -980,11 +1057,21 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
         ta.dX = w.dX; ta.rbuf = w.rbuf; ta.qbuf = w.qbuf; ta.xybuf = w.xybuf; ta.dBp = w.dBp; ta.dCp = w.dCp;
         ta.H = (int)f.H; ta.G = (int)f.G; ta.T = (int)f.T; ta.Tpad = (int)f.Tpad; ta.ntiles = ntiles;
         ta.tpc = (int)(f.Q / kBT); ta.nblk = w.nblk; ta.lamb = w.lamb;
-        const int64_t tiles = f.batch * ntiles * f.G * w.nblk;
-        if (launch(k_bwd_tile<TI, P, N>, dim3((unsigned)tiles), dim3(512), s, ta) != hipSuccess) return SSD_ERR_HIP;
+        ta.dXp = w.dXp;
+        ta.tok_stride = (size_t)(f.batch * f.H * f.Tpad);
+        ta.dx_stride = (size_t)(f.batch * f.T * f.H * f.P);
+        const int64_t tiles = f.batch * ntiles * f.G * w.nblk * NS;
+        if (launch(k_bwd_tile<TI, P, N, NL>, dim3((unsigned)tiles), dim3(512), s, ta) != hipSuccess)
+            return SSD_ERR_HIP;
+        if constexpr (NS > 1) {
+            const int64_t n = f.batch * f.T * f.H * f.P;
+            if (launch(k_bwd_dx<TI>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), s, (const float *)w.dXp,
+                       (TI *)w.dX, n, NS) != hipSuccess)
+                return SSD_ERR_HIP;
+        }
         BwdFinArgs fa = {};
         fa.qbuf = w.qbuf; fa.rbuf = w.rbuf; fa.xybuf = w.xybuf; fa.lamb = w.lamb; fa.dt = f.dt; fa.A = f.A;
-        fa.ddt = w.ddt;
+        fa.ddt = w.ddt; fa.tok_stride = ta.tok_stride; fa.ns = NS;
         fa.batch = (int)f.batch; fa.T = (int)f.T; fa.Tpad = (int)f.Tpad; fa.H = (int)f.H; fa.ntiles = ntiles;
         fa.dApart = w.dApart; fa.dDpart = w.dDpart;
         const int64_t waves = f.batch * f.H * ntiles;
@@ -1007,6 +1094,7 @@ static ssd_status bwd_n(const BwdArgs &w, hipStream_t s) {
         case 32: return run_bwd<TI, P, 32>(w, s);
         case 64: return run_bwd<TI, P, 64>(w, s);
         case 128: return run_bwd<TI, P, 128>(w, s);
+        case 256: return run_bwd<TI, P, 256>(w, s);
         default: return SSD_ERR_UNSUPPORTED;
     }
 }

@@ -109,13 +109,18 @@ struct BwdTileArgs {            // k_bwd_tile
     void *dX;
     float *rbuf, *qbuf, *xybuf; // per (batch, head, token): x.v, dy.y' - dt x.v, dy.x
     float *dBp, *dCp;           // (batch, Tpad, nblk, G, N) partial sums over head blocks
-    float *lamb;                // (batch, H, ntiles, 8) per-wavefront shares of
+    float *lamb;                // (batch, H, ntiles, NS, 8) per-wavefront shares of
                                 // <E_tile, state after the tile>
+    float *dXp;                 // NS > 1: (NS, batch, T, H, P) fp32 parts of dX
+    size_t tok_stride;          // elements between the n slices' rbuf / qbuf parts
+    size_t dx_stride;           // elements between the n slices' dXp parts
     int H, G, T, Tpad, ntiles, tpc, nblk;
 };
 
 struct BwdFinArgs {             // k_bwd_fin
     const float *qbuf, *rbuf, *xybuf, *lamb;
+    size_t tok_stride;          // elements between the n slices' rbuf / qbuf parts
+    int ns;                     // n slices of k_bwd_tile
     const void *dt;
     const float *A;
     void *ddt;
@@ -131,12 +136,15 @@ struct BwdArgs {
     float *dA, *dD, *dinit;     // dinit may be null
     void *Hst, *Est;            // workspace, storage type
     float *lamb, *dApart, *dDpart;                  // workspace, fp32, (batch, H, ntiles) each
-    float *rbuf, *qbuf, *xybuf, *dBp, *dCp;          // workspace, fp32
+    float *rbuf, *qbuf, *xybuf, *dBp, *dCp;          // workspace, fp32 (rbuf, qbuf: one part per n slice)
+    float *dXp;                 // workspace, fp32, n slices > 1 only
     int nblk;                   // head blocks per group
 };
 
 // Whether a backward kernel covers (dtype, P, N).
 bool bwd_supported(ssd_dtype dt, int64_t P, int64_t N);
+// Work-groups k_bwd_tile splits the n axis over (1 where it fits one CU's LDS).
+int bwd_nslices(ssd_dtype dt, int64_t P, int64_t N);
 // The backward launches (after launch_prepare on the same FwdArgs).
 ssd_status launch_bwd(const BwdArgs &w, hipStream_t s);
 

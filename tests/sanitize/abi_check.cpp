@@ -77,7 +77,7 @@ int main() {
     EXPECT(ssd_step(F, P, P, F, P, P, F, P, INT64_MAX, 64, 64, 128, 1, SSD_BF16, nullptr), SSD_ERR_UNSUPPORTED);
     EXPECT(ssd_step_gated(F, P, P, F, 7, F, P, P, F, nullptr, P, 256, 64, 64, 128, 1, SSD_BF16, nullptr), SSD_ERR_UNSUPPORTED);
     // backward
-    EXPECT(ssd_chunk_scan_bwd(P, P, F, P, P, F, 256, nullptr, P, nullptr, P, P, F, P, P, F, nullptr, 4, 2048, 64, 64, 256, 1, SSD_BF16, WS, BIG, nullptr), SSD_ERR_UNSUPPORTED);
+    EXPECT(ssd_chunk_scan_bwd(P, P, F, P, P, F, 256, nullptr, P, nullptr, P, P, F, P, P, F, nullptr, 4, 2048, 64, 128, 128, 1, SSD_BF16, WS, BIG, nullptr), SSD_ERR_UNSUPPORTED);
     EXPECT(ssd_chunk_scan_bwd(P, P, F, P, P, F, 256, nullptr, P, nullptr, P, P, nullptr, P, P, F, nullptr, 4, 2048, 64, 64, 128, 1, SSD_BF16, WS, BIG, nullptr), SSD_ERR_NULL);
     EXPECT(ssd_chunk_scan_bwd(P, P, F, P, P, F, 256, nullptr, P, nullptr, P, P, F, P, P, F, nullptr, 4, 2048, 64, 64, 128, 1, SSD_BF16, WS, 16, nullptr), SSD_ERR_WORKSPACE);
     EXPECT(ssd_chunk_scan_bwd(P, P, F, P, P, F, 256, nullptr, P, nullptr, P, P, F, P, P, F, nullptr, INT64_MAX, 2048, 64, 64, 128, 1, SSD_BF16, WS, BIG, nullptr), SSD_ERR_UNSUPPORTED);

@@ -281,21 +281,31 @@ def bwd(X=P16, dt=P16, A=P16, B=P16, C=P16, D=P16, chunk=256, init=None, dY=P16,
                         dinit, batch, T, H, P, N, G, dtype, wsp, wsb, stream)
 
 
+def bwd_ws(N, dtype, ns):
+    """The backward's workspace at batch 4, T 2048, 64 heads, P 64, one group,
+    chunk 256, with k_bwd_tile's n axis in `ns` slices."""
+    es = 2 if dtype == BF16 else 4
+    fwd = ws(4, 2048, 64, 64, N, 1, 256, dtype)
+    st = 4 * 64 * 32 * 64 * N * es              # states per 64-token tile, storage type
+    lamb = 4 * 64 * 32 * 4
+    shares = 8 * ns * lamb                      # Lambda shares: 8 per tile and slice
+    tok = 4 * 64 * 2048 * 4
+    nblk = 1                                    # 4 x 32 tiles x 1 group x 2 blocks = 256 work-groups
+    while 4 * 32 * nblk < 256:
+        nblk *= 2
+    part = 4 * 2048 * nblk * N * 4
+    dxp = ns * 4 * 2048 * 64 * 64 * 4 if ns > 1 else 0
+    return fwd + 2 * st + shares + 2 * lamb + 2 * ns * tok + tok + 2 * part + dxp
+
+
 def test_bwd_workspace_query():
     q = ssd.load().ssd_chunk_scan_bwd_workspace_bytes
-    fwd = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
-    st = 4 * 64 * 32 * 64 * 128 * 2            # states per 64-token tile, bf16
-    lamb = 4 * 64 * 32 * 4
-    shares = 8 * lamb
-    tok = 4 * 64 * 2048 * 4
-    nblk = 1                                    # 4 x 32 tiles x 1 group x 4 blocks = 512 work-groups
-    while 4 * 32 * nblk < 512:
-        nblk *= 2
-    part = 4 * 2048 * nblk * 128 * 4
-    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == fwd + 2 * st + shares + 2 * lamb + 3 * tok + 2 * part
-    assert q(4, 2048, 64, 64, 256, 1, 256, BF16) == ctypes.c_size_t(-1).value   # N 256: not covered
+    assert q(4, 2048, 64, 64, 128, 1, 256, BF16) == bwd_ws(128, BF16, 1)
+    assert q(4, 2048, 64, 64, 256, 1, 256, BF16) == bwd_ws(256, BF16, 2)    # n in 2 slices of 128
+    assert q(4, 2048, 64, 64, 128, 1, 256, F32) == bwd_ws(128, F32, 4)      # n in 4 slices of 32
     assert q(4, 2048, 64, 128, 64, 1, 256, BF16) == ctypes.c_size_t(-1).value   # P 128: not covered
-    assert q(4, 2048, 64, 64, 128, 1, 256, F32) == ctypes.c_size_t(-1).value
+    assert q(4, 2048, 64, 64, 256, 1, 256, F32) == ctypes.c_size_t(-1).value    # fp32 N 256: not covered
+    assert q(4, 2048, 64, 64, 16, 1, 256, BF16) == ctypes.c_size_t(-1).value    # N 16: not covered
     assert q(2, 100, 4, 32, 64, 1, 64, F32) > 0
     assert q(0, 2048, 64, 64, 128, 1, 256, BF16) == 0
 
@@ -307,7 +317,7 @@ def test_bwd_null(field):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=-1), ESHAPE), (dict(H=64, G=3), ESHAPE), (dict(chunk=32), EUNSUP),
-    (dict(N=256), EUNSUP), (dict(P=128), EUNSUP), (dict(dtype=F32), EUNSUP), (dict(dtype=7), EUNSUP),
+    (dict(N=16), EUNSUP), (dict(P=128), EUNSUP), (dict(dtype=F32, N=256), EUNSUP), (dict(dtype=7), EUNSUP),
 ])
 def test_bwd_shape_checks(kw, code):
     assert bwd(**kw) == code

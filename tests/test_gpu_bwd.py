@@ -122,6 +122,57 @@ def test_bwd_f32(ssd, P, N):
     check(ssd, shape("tiny_f32", batch=2, seqlen=150, nheads=2, headdim=P, dstate=N, seed=84), 64, True, True)
 
 
+@pytest.mark.parametrize("P,N", [(64, 64), (64, 128), (32, 128)])
+def test_bwd_f32_n_slices(ssd, P, N):
+    """fp32 shapes whose tile kernel takes the n axis in 2 or 4 slices (the
+    1.3B layer's head shape among them), the slices' parts of dX, of the
+    per-token scalars and of Lambda added afterwards."""
+    check(ssd, shape("tiny_f32", batch=2, seqlen=150, nheads=2, headdim=P, dstate=N, seed=94), 64, True, True)
+
+
+@pytest.mark.parametrize("P", [32, 64])
+def test_bwd_bf16_state_size_256(ssd, P):
+    """N 256 (the 16K-token workload's state size), two groups, an initial
+    state and a final-state gradient, ragged length: the n axis in 2 slices."""
+    check(ssd, shape("long16k_bf16", batch=2, seqlen=300, nheads=4, headdim=P, dstate=256, ngroups=2, seed=93),
+          128, True, True)
+
+
+def test_bwd_bf16_state_size_256_head_blocks(ssd):
+    """Batch 4, T 2048, 16 heads, P 64, N 256, 2 groups: blocks of 8 heads of
+    a group summed in registers together with 2 n slices; every gradient
+    element by element."""
+    check(ssd, shape("long16k_bf16", batch=4, seqlen=2048, nheads=16, headdim=64, dstate=256, ngroups=2,
+                     seed=95), 256, False, True)
+
+
+@pytest.mark.timeout(600)
+def test_bwd_full_size_16k(ssd):
+    """The 16K-token workload (batch 1, T 16384, 64 heads, P 64, N 256, 8
+    groups, chunk 256): dX, ddt, dA and the initial-state gradient of two heads
+    of different groups element by element against the oracle run on those
+    heads alone (each depends on its own head only), and every gradient finite.
+    dB and dC need all heads of a group; their slices and head blocks are
+    checked element by element at N 256 above."""
+    cfg = si.CONFIGS["long16k_bf16"]
+    inp = grad_inputs(cfg, 96, False, True)
+    log("[bwd full size] 16K tokens")
+    g = gpu_bwd(ssd, inp, cfg.chunk)
+    for k in KEYS:
+        assert np.all(np.isfinite(g[k])), k
+    HG = cfg.nheads // cfg.ngroups
+    for h in (5, 42):
+        gr, sl = h // HG, slice(h, h + 1)
+        r = oracle.bwd(inp["X32"][:, :, sl], inp["dt32"][:, :, sl], inp["A"][sl], inp["B32"][:, :, gr:gr + 1],
+                       inp["C32"][:, :, gr:gr + 1], inp["D"][sl], 1, inp["dY32"][:, :, sl], None, inp["dF"][:, sl])
+        e = {"dX": rel(g["dX"][:, :, sl], r["dX"]), "ddt": rel(g["ddt"][:, :, sl], r["ddt"]),
+             "dinit": rel(g["dinit"][:, sl], r["dinit"]), "dD": rel(g["dD"][sl], r["dD"]),
+             "dA": float(np.abs(g["dA"][h] - r["dA"][0]) / np.sum(np.abs(inp["dt32"][:, :, sl] * r["lam"])))}
+        log(f"    head {h}: " + " ".join(f"{k}={v:.2e}" for k, v in e.items()))
+        for k, v in e.items():
+            assert v <= TOL["bf16"], (h, k, v)
+
+
 def test_bwd_long_memory(ssd):
     """Small |A|: the adjoint and the states carry across many tiles."""
     cfg = shape("l1p3b_bf16", batch=1, seqlen=700, nheads=2, headdim=32, dstate=32, seed=85)
