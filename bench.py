@@ -15,7 +15,8 @@ sub-blocks give the median per-step time beside the mean. The 125M-layer and
 "shapes". The decode step is timed after the forward: 1000 ssd_step calls on
 the 256 x 64 x 64 x 128 fp32 state, then 50 forwards with the fused layer
 prologue / epilogue (ssd_chunk_scan_fwd_fused) and 20 backward passes
-(ssd_chunk_scan_bwd) of the forward workload, reported beside the forward.
+(ssd_chunk_scan_bwd) of the forward workload (and 5 of the 16K-token one),
+reported beside the forward.
 Prints one JSON line.
 
 The oracle is timed beside the GPU on a bounded sample of the same workload
@@ -506,20 +507,21 @@ def main():
         except ssd.SSDError:
             bwd_ok = False  # no backward kernel for this shape (e.g. N 256)
             out["backward"] = None
-    if bwd_ok:
-        # one backward (ssd_chunk_scan_bwd) of the same workload; its states per
-        # 64-token tile (2 x 134 MB at the 1.3B shape) already exceed the cache
-        t = sets[0]
+    def time_backward(bcfg, t, bchunk, steps):
+        """ssd_chunk_scan_bwd on input set t of workload bcfg: `steps` calls
+        between two events, after 3 untimed ones (arguments marshalled once)."""
+        bcode = ssd.SSD_BF16 if bcfg.dtype == "bf16" else ssd.SSD_F32
+        b_, t_, h_, p_, n_, g_ = bcfg.batch, bcfg.seqlen, bcfg.nheads, bcfg.headdim, bcfg.dstate, bcfg.ngroups
         rng = np.random.default_rng(7)
-        dY = up(si.bf16_round_bits(rng.standard_normal((Bz, T, H, P)).astype(np.float32)))
-        nb = ssd.ssd_chunk_scan_bwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
+        dY = up(si.bf16_round_bits(rng.standard_normal((b_, t_, h_, p_)).astype(np.float32)))
+        nb = ssd.ssd_chunk_scan_bwd_workspace_bytes(b_, t_, h_, p_, n_, g_, bchunk, bcode)
         bws = torch.empty(nb, dtype=torch.uint8, device=dev)
         g = {"dX": torch.empty_like(t["X"]), "ddt": torch.empty_like(t["dt"]), "dB": torch.empty_like(t["B"]),
              "dC": torch.empty_like(t["C"]), "dA": torch.empty_like(t["A"]), "dD": torch.empty_like(t["D"])}
         bargs = (t["X"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
-                 t["D"].data_ptr(), chunk, None, dY.data_ptr(), None, g["dX"].data_ptr(), g["ddt"].data_ptr(),
+                 t["D"].data_ptr(), bchunk, None, dY.data_ptr(), None, g["dX"].data_ptr(), g["ddt"].data_ptr(),
                  g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(), g["dD"].data_ptr(), None,
-                 Bz, T, H, P, N, G, code, bws.data_ptr(), nb, sptr)
+                 b_, t_, h_, p_, n_, g_, bcode, bws.data_ptr(), nb, sptr)
 
         def bwd():
             st = lib.ssd_chunk_scan_bwd(*bargs)
@@ -530,18 +532,30 @@ def main():
         torch.cuda.synchronize()
         bs, be = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         bs.record(stream)
-        for _ in range(args.backward_steps):
+        for _ in range(steps):
             bwd()
         be.record(stream)
         torch.cuda.synchronize()
-        ms_b = bs.elapsed_time(be) / args.backward_steps
-        bbytes = bwd_accounting(cfg)
-        out["backward"] = {"workload": out["config"]["workload"], "ms_per_call": ms_b,
-                           "tokens_per_s": Bz * T / (ms_b / 1e3),
-                           "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
-                           "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS,
-                           "kernels": "k_state_passes (both state passes, one launch), k_bwd_tile, k_bwd_fin, k_bwd_heads, k_bwd_sum_bc (+ k_prepare)"}
+        ms_b = bs.elapsed_time(be) / steps
+        bbytes = bwd_accounting(bcfg)
         del bws, dY, g
+        return {"workload": WORKLOAD_NAMES.get(bcfg.name, bcfg.name), "ms_per_call": ms_b, "tokens_per_s": b_ * t_ / (ms_b / 1e3),
+                "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
+                "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+    if bwd_ok:
+        # one backward (ssd_chunk_scan_bwd) of the same workload; its states per
+        # 64-token tile (2 x 134 MB at the 1.3B shape) already exceed the cache
+        out["backward"] = time_backward(cfg, sets[0], chunk, args.backward_steps)
+        out["backward"]["kernels"] = ("k_state_passes (both state passes, one launch), k_bwd_tile, k_bwd_fin, "
+                                      "k_bwd_heads, k_bwd_sum_bc (+ k_prepare; k_bwd_dx where the n axis is split)")
+        if not args.no_shapes and args.workload != "long16k_bf16":
+            # the 16K-token workload's backward (N 256: the tile kernel takes the n axis in 2 slices)
+            c3 = si.CONFIGS["long16k_bf16"]
+            s3, _ = make_sets(c3, c3.chunk, 1)
+            out["backward"]["long16k_bf16"] = time_backward(c3, s3[0], c3.chunk, max(5, args.backward_steps // 4))
+            del s3
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(first_inp, cfg)
