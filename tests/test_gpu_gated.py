@@ -198,6 +198,30 @@ def test_fused_conv_forward(ssd, dtype, chunk, with_bias, gated):
     assert all(np.isfinite(e) and e <= tol for e in errs), errs
 
 
+def test_fused_conv_full_width_walks(ssd):
+    """Batch 4 x 64 heads, P 64, N 128, chunk 256, gated, with bias: one
+    work-group per (batch, head) over all 64 columns, the variant timed on the
+    1.3B-layer shape (its state waves stage the convolved X)."""
+    import torch
+    cfg = dataclasses.replace(si.CONFIGS["l1p3b_bf16"], name="conv_full", batch=4, seqlen=200, nheads=64,
+                              seed=97)
+    inp = raw_inputs(cfg, 98)
+    w, b = conv_inputs(cfg, 99)
+    Xc = oracle_conv_x(inp["X32"], w, b)
+    dt = oracle.dt_prologue(inp["dtraw32"], inp["bias"], 1)
+    Yr, Fr, _ = oracle.fwd(Xc, dt, inp["A"], inp["B32"], inp["C32"], inp["D"], cfg.ngroups)
+    Yr = oracle.gate(Yr, inp["z32"])
+    log("[conv] full-width walks")
+    Y, F = ssd.ssd_chunk_scan_fwd_fused(
+        to_dev(inp["X"]), to_dev(inp["dtraw"]), to_dev(inp["A"]), to_dev(inp["B"]), to_dev(inp["C"]),
+        to_dev(inp["D"]), 256, conv_w=to_dev(w), conv_b=to_dev(b), dt_bias=to_dev(inp["bias"]), dt_softplus=1,
+        z=to_dev(inp["z"]))
+    torch.cuda.synchronize()
+    e = (rel(to_np(Y), Yr), rel(F.cpu().numpy(), Fr))
+    log(f"    rel err Y={e[0]:.2e} final={e[1]:.2e}")
+    assert e[0] <= TOL["bf16"] and e[1] <= TOL["bf16"], e
+
+
 def test_fused_conv_split_sequence(ssd):
     """Few heads and a long sequence: the walk splits it into segments, whose
     state-only pass applies the convolution too (tokens before each segment
