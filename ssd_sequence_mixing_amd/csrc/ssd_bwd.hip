@@ -76,18 +76,6 @@ __device__ __forceinline__ void lds_st4(TI *p, float a, float b, float c, float 
     store4<TI>(p, f32x4{a, b, c, d});
 }
 
-// Four consecutive elements from LDS.
-template <typename TI>
-__device__ __forceinline__ void lds_ld4(TI *d, const TI *p) {
-    if constexpr (sizeof(TI) == 2) {
-        const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-    } else {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
-        d[0] = v[0]; d[1] = v[1]; d[2] = v[2]; d[3] = v[3];
-    }
-}
-
 // A fragment from two runs of 4 consecutive elements (k slots 0-3 and 4-7).
 template <typename TI>
 __device__ __forceinline__ typename Traits<TI>::frag lds_frag_split(const TI *p0, const TI *p1) {
@@ -396,23 +384,76 @@ struct BwdCfg {
     static constexpr int ES = sizeof(TI), PAD = 16 / ES;
     static constexpr int PB = P / 16, NB = N / 16, NK = N / 32, KP = P / 32;
     static constexpr int T_LD = kBT + PAD, P_LD = P + PAD, N_LD = N + PAD;
-    // element offsets (storage type)
-    static constexpr int BT_OFF = 0;                       // B^T [n][t]
-    static constexpr int CT_OFF = BT_OFF + N * T_LD;       // C^T [n][t]
-    static constexpr int XT_OFF = CT_OFF + N * T_LD;       // X^T [p][t]
-    static constexpr int DYT_OFF = XT_OFF + P * T_LD;      // dY^T [p][t]
-    static constexpr int XN_OFF = DYT_OFF + P * T_LD;      // X [t][p]
-    static constexpr int DYN_OFF = XN_OFF + kBT * P_LD;    // dY [t][p]
-    static constexpr int HN_OFF = DYN_OFF + kBT * P_LD;    // h [p][n]
-    static constexpr int EN_OFF = HN_OFF + P * N_LD;       // E [p][n]
-    static constexpr int HT_OFF = EN_OFF + P * N_LD;       // h^T [n][p]
-    static constexpr int ET_OFF = HT_OFF + N * P_LD;       // E^T [n][p]
-    static constexpr int OS_OFF = ET_OFF + N * P_LD;       // dX staging, 16 rows per wave
-    static constexpr int ELEMS = OS_OFF + 4 * 16 * P_LD;
-    static constexpr int F_OFF = (ELEMS * ES + 15) / 16 * 16;  // bytes: cs, cs', dt of the tile
-    static constexpr int LDS = F_OFF + 3 * kBT * 4;
+    // element offsets (storage type); N is the work-group's slice of the state columns
+    static constexpr int BT_OFF = 0;                       // B^T [n][t], per tile
+    static constexpr int CT_OFF = BT_OFF + N * T_LD;       // C^T [n][t], per tile
+    static constexpr int OS_OFF = CT_OFF + N * T_LD;       // dX staging, 16 rows per wave
+    static constexpr int HEAD_OFF = OS_OFF + 4 * 16 * P_LD;
+    // two per-head buffers (head k in buffer k % 2), each row-major only: the
+    // transposed operands are read from them with the LDS transpose read
+    static constexpr int XN = 0;                           // X [t][p]
+    static constexpr int DYN = XN + kBT * P_LD;            // dY [t][p]
+    static constexpr int HN = DYN + kBT * P_LD;            // h [p][n]
+    static constexpr int EN = HN + P * N_LD;               // E [p][n]
+    static constexpr int BUF = EN + P * N_LD;
+    static constexpr int ELEMS = HEAD_OFF + 2 * BUF;
+    // bytes: per buffer the head's cs, cs', dt of the tile's tokens, then cs before the tile
+    // (0 at a chunk's start), cs at its end and D
+    static constexpr int F_OFF = (ELEMS * ES + 15) / 16 * 16;
+    static constexpr int FBUF = 3 * kBT + 4;
+    static constexpr int LDS = F_OFF + 2 * FBUF * 4;
     static constexpr bool kFits = LDS <= 160 * 1024 && P % 32 == 0 && N % 32 == 0;
 };
+
+// Four consecutive rows kb .. kb + 3 of column c0 + (lane & 15) of a
+// row-major matrix M in LDS (row pitch ld elements); kb may differ between the
+// wavefront's four 16-lane groups. bf16: one LDS transpose read, in which lane
+// j of a group supplies the address of row kb + j / 4, columns c0 + 4 (j % 4)
+// .. + 3, and receives the column of its own lane index; fp32: four reads.
+__device__ __forceinline__ u32x2 tr4_bits(const bf16 *M, int ld, int kb, int c0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int j = lane & 15;
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(M + (kb + (j >> 2)) * ld + c0 + 4 * (j & 3)));
+    return __builtin_bit_cast(u32x2, v);
+}
+template <typename TI>
+__device__ __forceinline__ void tr4(const TI *M, int ld, int kb, int c0, int lane, TI (&o)[4]) {
+    if constexpr (sizeof(TI) == 2) {
+        const u32x2 w = tr4_bits(M, ld, kb, c0, lane);
+        const uint32_t w0 = w[0], w1 = w[1];
+        o[0] = __builtin_bit_cast(bf16, (uint16_t)(w0 & 0xffffu));
+        o[1] = __builtin_bit_cast(bf16, (uint16_t)(w0 >> 16));
+        o[2] = __builtin_bit_cast(bf16, (uint16_t)(w1 & 0xffffu));
+        o[3] = __builtin_bit_cast(bf16, (uint16_t)(w1 >> 16));
+    } else {
+        const int c = c0 + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = M[(kb + e) * ld + c];
+    }
+}
+// A matrix-core operand from a row-major matrix read down its columns: slots
+// 0-3 rows kb0 .. kb0 + 3, slots 4-7 rows kb1 .. kb1 + 3, column c0 + (lane & 15).
+template <typename TI>
+__device__ __forceinline__ typename Traits<TI>::frag tr_frag(const TI *M, int ld, int kb0, int kb1, int c0,
+                                                               int lane) {
+    typename Traits<TI>::frag f;
+    if constexpr (sizeof(TI) == 2) {
+        const u32x2 a = tr4_bits(M, ld, kb0, c0, lane), b = tr4_bits(M, ld, kb1, c0, lane);
+        const uint32_t a0 = a[0], a1 = a[1], b0 = b[0], b1 = b[1];
+        f = __builtin_bit_cast(bf16x8, u32x4{a0, a1, b0, b1});
+    } else {
+        TI x[4], y[4];
+        tr4<TI>(M, ld, kb0, c0, lane, x);
+        tr4<TI>(M, ld, kb1, c0, lane, y);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = x[e];
+            f[4 + e] = y[e];
+        }
+    }
+    return f;
+}
 
 // 8 wavefronts in two roles over the same staged tile and head: waves 0-3
 // (16 token rows each) form y', v, dX and the per-token scalars; waves 4-7
@@ -434,10 +475,17 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
     constexpr int T_LD = Cfg::T_LD, P_LD = Cfg::P_LD, N_LD = Cfg::N_LD;
     __shared__ __attribute__((aligned(16))) char smem[Cfg::LDS];
     TI *const L = reinterpret_cast<TI *>(smem);
-    TI *BT = L + Cfg::BT_OFF, *CT = L + Cfg::CT_OFF, *XT = L + Cfg::XT_OFF, *DYT = L + Cfg::DYT_OFF;
-    TI *XN = L + Cfg::XN_OFF, *DYN = L + Cfg::DYN_OFF, *HN = L + Cfg::HN_OFF, *EN = L + Cfg::EN_OFF;
-    TI *HT = L + Cfg::HT_OFF, *ET = L + Cfg::ET_OFF;
-    float *CS = reinterpret_cast<float *>(smem + Cfg::F_OFF), *CP = CS + kBT, *DT = CP + kBT;
+    TI *const BT = L + Cfg::BT_OFF, *const CT = L + Cfg::CT_OFF;
+    TI *const HB = L + Cfg::HEAD_OFF;                                  // the two per-head buffers
+    float *const FB = reinterpret_cast<float *>(smem + Cfg::F_OFF);    // their cs, cs', dt
+    // the current head's buffer (set at the top of each head)
+    const TI *XN = nullptr, *DYN = nullptr, *HN = nullptr, *EN = nullptr;
+    const float *CS = nullptr, *CP = nullptr, *DT = nullptr, *SC = nullptr;
+    auto use_buffer = [&](int sb) __attribute__((always_inline)) {
+        const TI *B0 = HB + sb * Cfg::BUF;
+        XN = B0 + Cfg::XN; DYN = B0 + Cfg::DYN; HN = B0 + Cfg::HN; EN = B0 + Cfg::EN;
+        CS = FB + sb * Cfg::FBUF; CP = CS + kBT; DT = CP + kBT; SC = DT + kBT;
+    };
 
     const int H = a.H, G = a.G, T = a.T, HG = H / G, nblk = a.nblk, hpb = HG / nblk;
     int x = blockIdx.x;
@@ -543,7 +591,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
         // token t0 + (tid & 63) of the prefetched head; dt as its raw bits (0 past the end),
         // converted where it is used, and every load unconditional, so that no wait for it
         // sits under a branch or right after the load
-        float pcs = 0.f, pcp = 0.f;
+        float pcs = 0.f, pcp = 0.f, pcr = 0.f, pce = 0.f, pd = 0.f;  // pcr, pce, pd: the head's cs_r, cs_e, D
         uint32_t pdt = 0;
         const rsrc_t rdt = make_rsrc(reinterpret_cast<const char *>(a.dt) + (size_t)b * T * H * ES,
                                      (uint32_t)((size_t)T * H * ES));
@@ -556,33 +604,36 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             const int t = t0 + (tid & 63);
             pcs = a.cs2[bh * a.Tpad + t];
             pcp = a.dtf[bh * a.Tpad + t];
+            pcr = a.cs2[bh * a.Tpad + max(t0 - 1, 0)];
+            pce = a.cs2[bh * a.Tpad + t0 + kBT - 1];
+            pd = a.D[h];
             const uint32_t od = (uint32_t)(((size_t)t * H + h) * ES);
             if constexpr (ES == 2) pdt = buf_ld16(rdt, od);
             else pdt = buf_ld32(rdt, od);
         };
+        // writes the loaded head's X, dY (row-major) and per-token terms into buffer sb
+        auto stage = [&](int sb) {
+            TI *B0 = HB + sb * Cfg::BUF;
+            float *F = FB + sb * Cfg::FBUF;
+            // the four role-A wavefronts write the same values
+            const uint32_t u = pdt;
+            F[tid & 63] = pcs;
+            F[kBT + (tid & 63)] = pcp;
+            F[2 * kBT + (tid & 63)] = ES == 2 ? __uint_as_float(u << 16) : __uint_as_float(u);
+            F[3 * kBT + (tid & 3)] = (tid & 3) == 0 ? (tau % a.tpc == 0 ? 0.f : pcr) : (tid & 3) == 1 ? pce : pd;
+            xr.store_N(B0 + Cfg::XN, P_LD, rt);
+            dyr.store_N(B0 + Cfg::DYN, P_LD, rt);
+        };
         issue(0);
+        stage(0);
+        issue(min(1, hpb - 1));
+        __syncthreads();  // pairs with role B's: head 0 and the tile's B^T, C^T staged
         for (int k = 0; k < hpb; ++k) {
+            use_buffer(k & 1);
             const int h = g * HG + blk * hpb + k;
             const size_t bh = (size_t)b * H + h;
-            const float *cs = a.cs2 + bh * a.Tpad + t0;
-            const float cs_r = (tau % a.tpc == 0) ? 0.f : cs[-1];
-            const float cs_e = cs[kBT - 1];
-            const float Dh = a.D[h];
+            const float cs_r = SC[0], cs_e = SC[1], Dh = SC[2];
             const uint32_t xo = (uint32_t)(((size_t)t0 * H + h) * P * ES);
-            __syncthreads();  // the previous head's reads are done
-            {
-                // the four role-A wavefronts write the same 64 values
-                const uint32_t u = pdt;
-                CS[tid & 63] = pcs;
-                CP[tid & 63] = pcp;
-                DT[tid & 63] = ES == 2 ? __uint_as_float(u << 16) : __uint_as_float(u);
-            }
-            xr.template store_T<false>(XT, T_LD, rt, [](int) { return 1.f; });
-            xr.store_N(XN, P_LD, rt);
-            dyr.template store_T<false>(DYT, T_LD, rt, [](int) { return 1.f; });
-            dyr.store_N(DYN, P_LD, rt);
-            __syncthreads();
-            issue(min(k + 1, hpb - 1));  // past the last head: a harmless reload
             const float cs_t = CS[trow];
             float cs_o[4], dt_o[4];  // output rows t = 16 w + 4 kg + i
 #pragma unroll
@@ -609,8 +660,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     ay[pb] = Tr::mma(cw[kk], Tr::lds_frag(HN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), ay[pb]);
                     av[pb] = Tr::mma(bw[kk], Tr::lds_frag(EN + (16 * pb + r) * N_LD + 32 * kk + 8 * kg), av[pb]);
                 }
-                TI xl[4];
-                lds_ld4<TI>(xl, XT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
+                TI xl[4];  // x of this lane's 4 rows, column 16 pb + r
+                tr4<TI>(XN, P_LD, 16 * w + 4 * kg, 16 * pb, lane, xl);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lam += wl[i] * Tr::to_f32(xl[i]) * av[pb][i];
 #pragma unroll
@@ -626,8 +677,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     const frag m = make_a(g1, k2, true, cs_t, kSplit ? &lo : nullptr);
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb) {
-                        const TI *p = XT + (16 * pb + r) * T_LD + 32 * k2 + 4 * kg;
-                        const frag xb = lds_frag_split<TI>(p, p + 16);
+                        const frag xb = tr_frag<TI>(XN, P_LD, 32 * k2 + 4 * kg, 32 * k2 + 16 + 4 * kg, 16 * pb, lane);
                         ay[pb] = Tr::mma(m, xb, ay[pb]);
                         if constexpr (kSplit) ay[pb] = Tr::mma(lo, xb, ay[pb]);
                     }
@@ -637,8 +687,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     const frag m = make_a(g2, k2, false, cs_t, kSplit ? &lo : nullptr);
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb) {
-                        const TI *p = DYT + (16 * pb + r) * T_LD + 32 * k2 + 4 * kg;
-                        const frag db = lds_frag_split<TI>(p, p + 16);
+                        const frag db = tr_frag<TI>(DYN, P_LD, 32 * k2 + 4 * kg, 32 * k2 + 16 + 4 * kg, 16 * pb, lane);
                         av[pb] = Tr::mma(m, db, av[pb]);
                         if constexpr (kSplit) av[pb] = Tr::mma(lo, db, av[pb]);
                     }
@@ -649,8 +698,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) {
                 TI xs[4], ds[4];
-                lds_ld4<TI>(xs, XT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
-                lds_ld4<TI>(ds, DYT + (16 * pb + r) * T_LD + 16 * w + 4 * kg);
+                tr4<TI>(XN, P_LD, 16 * w + 4 * kg, 16 * pb, lane, xs);
+                tr4<TI>(DYN, P_LD, 16 * w + 4 * kg, 16 * pb, lane, ds);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float xv = Tr::to_f32(xs[i]), dv = Tr::to_f32(ds[i]);
@@ -700,6 +749,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     buf_st128(d, rdx, xo + (uint32_t)(16 * w + rl) * x_tok + (uint32_t)(cv * 16));
                 }
             }
+            // the next head into the other buffer (its last reads, head k - 1's, ended at the
+            // barrier before this head); past the last head a harmless repeat of it
+            stage((k + 1) & 1);
+            issue(min(k + 2, hpb - 1));
+            __syncthreads();
         }
     } else {
         // ================= role B: dC and dB, summed over the heads =================
@@ -710,28 +764,24 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             accc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         TileRegs<TI, P, NL, 256> hr, er;
+        float pcr = 0.f, pce = 0.f;  // the loaded head's cs before the tile and at its end
         auto issue = [&](int k) {
             const int h = g * HG + blk * hpb + k;
             const size_t so = (((size_t)b * H + h) * a.ntiles + tau) * (size_t)(P * N);
+            pcr = a.cs2[((size_t)b * H + h) * a.Tpad + max(t0 - 1, 0)];
+            pce = a.cs2[((size_t)b * H + h) * a.Tpad + t0 + kBT - 1];
             hr.load(make_rsrc(reinterpret_cast<const TI *>(a.Hst) + so, (uint32_t)(P * N * ES)),
                     (uint32_t)(n0 * ES), (uint32_t)(N * ES), rt);
             er.load(make_rsrc(reinterpret_cast<const TI *>(a.Est) + so, (uint32_t)(P * N * ES)),
                     (uint32_t)(n0 * ES), (uint32_t)(N * ES), rt);
         };
-        issue(0);
-        for (int k = 0; k < hpb; ++k) {
-            const int h = g * HG + blk * hpb + k;
-            const size_t bh = (size_t)b * H + h;
-            const float *cs = a.cs2 + bh * a.Tpad + t0;
-            const float cs_r = (tau % a.tpc == 0) ? 0.f : cs[-1];
-            const float cs_e = cs[kBT - 1];
-            __syncthreads();  // the previous head's reads are done
-            hr.store_N(HN, N_LD, rt);
-            hr.template store_T<false>(HT, P_LD, rt, [](int) { return 1.f; });
-            er.store_N(EN, N_LD, rt);
-            er.template store_T<false>(ET, P_LD, rt, [](int) { return 1.f; });
-            // the entering state's part of Lambda at the tile's end: 2^{cs_e - cs_r} <E, h>, from
-            // the loaded pieces (h and E are loaded with the same offsets; spare units read 0)
+        // writes the loaded head (head kh)'s h and E (row-major) into buffer sb, and its share of
+        // Lambda at the tile's end from the entering state: 2^{cs_e - cs_r} <E, h>, from the loaded
+        // pieces (h and E are loaded with the same offsets; spare units read 0)
+        auto stage = [&](int kh, int sb) {
+            TI *B0 = HB + sb * Cfg::BUF;
+            hr.store_N(B0 + Cfg::HN, N_LD, rt);
+            er.store_N(B0 + Cfg::EN, N_LD, rt);
             float lam = 0.f;
 #pragma unroll
             for (int kq = 0; kq < decltype(hr)::K; ++kq)
@@ -750,11 +800,19 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                         for (int e = 0; e < 8; ++e) lam += hv[e] * ev[e];
                     }
                 }
-            __syncthreads();
-            issue(min(k + 1, hpb - 1));
 #pragma unroll
             for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
-            if (lane == 0) a.lamb[((bh * a.ntiles + tau) * NS + sl) * 8 + 4 + w] = fast_exp2(cs_e - cs_r) * lam;
+            const size_t bh = (size_t)b * H + g * HG + blk * hpb + kh;
+            const float cs_r = (tau % a.tpc == 0) ? 0.f : pcr;
+            if (lane == 0) a.lamb[((bh * a.ntiles + tau) * NS + sl) * 8 + 4 + w] = fast_exp2(pce - cs_r) * lam;
+        };
+        issue(0);
+        stage(0, 0);
+        issue(min(1, hpb - 1));
+        __syncthreads();  // pairs with role A's
+        for (int k = 0; k < hpb; ++k) {
+            use_buffer(k & 1);
+            const float cs_r = SC[0], cs_e = SC[1];
             const float cs_t = CS[trow];
             float cs_o[4], dt_o[4];
 #pragma unroll
@@ -782,7 +840,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
                         tmp[nb] = Tr::mma(Tr::lds_frag(DYN + trow * P_LD + 32 * kp + 8 * kg),
-                                          Tr::lds_frag(HT + (16 * nb + r) * P_LD + 32 * kp + 8 * kg), tmp[nb]);
+                                          tr_frag<TI>(HN, N_LD, 32 * kp + 8 * kg, 32 * kp + 8 * kg + 4, 16 * nb, lane),
+                                          tmp[nb]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) tmp[nb][i] *= fast_exp2(cs_o[i] - cs_r);
                 }
@@ -819,7 +878,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 #pragma unroll
                     for (int kp = 0; kp < KP; ++kp)
                         tmp[nb] = Tr::mma(Tr::lds_frag(XN + trow * P_LD + 32 * kp + 8 * kg),
-                                          Tr::lds_frag(ET + (16 * nb + r) * P_LD + 32 * kp + 8 * kg), tmp[nb]);
+                                          tr_frag<TI>(EN, N_LD, 32 * kp + 8 * kg, 32 * kp + 8 * kg + 4, 16 * nb, lane),
+                                          tmp[nb]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) tmp[nb][i] *= fast_exp2(cs_e - cs_o[i]);
                 }
@@ -838,6 +898,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) accb[nb][i] += dt_o[i] * tmp[nb][i];
             }
+            // the next head into the other buffer, as in role A
+            stage(min(k + 1, hpb - 1), (k + 1) & 1);
+            issue(min(k + 2, hpb - 1));
+            __syncthreads();
         }
         // dB, dC of this head block: part[b][t][blk][g][n] (fp32)
 #pragma unroll
