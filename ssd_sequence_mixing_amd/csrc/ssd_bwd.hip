@@ -455,6 +455,32 @@ __device__ __forceinline__ typename Traits<TI>::frag tr_frag(const TI *M, int ld
     return f;
 }
 
+// Sum over each row of 16 lanes, left in every lane of the row, with DPP moves on the vector
+// ALU (no LDS traffic): neighbours, then pairs (quad permutes), then the two quads of each
+// half-row (half-row mirror), then the two half-rows (row mirror).
+__device__ __forceinline__ float row16_sum(float v) {
+    auto mv = [](float x, int ctrl) -> float {
+        switch (ctrl) {  // the control word must be a constant
+            case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+            case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+            case 0x141: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+            default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+        }
+    };
+    v += mv(v, 0xB1);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+    v += mv(v, 0x4E);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+    v += mv(v, 0x141);  // row_half_mirror: lane i <- 7 - i within each 8
+    v += mv(v, 0x140);  // row_mirror: lane i <- 15 - i
+    return v;
+}
+// Sum over all 64 lanes: the rows' sums, then across rows with two lane shuffles.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
 // 8 wavefronts in two roles over the same staged tile and head: waves 0-3
 // (16 token rows each) form y', v, dX and the per-token scalars; waves 4-7
 // (same rows) form x.dy products, dC and dB. The roles share no results, so
@@ -718,13 +744,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                 }
             }
 #pragma unroll
-            for (int m = 1; m < 16; m <<= 1)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    sxv[i] += __shfl_xor(sxv[i], m);
-                    sdy[i] += __shfl_xor(sdy[i], m);
-                    sxy[i] += __shfl_xor(sxy[i], m);
-                }
+            for (int i = 0; i < 4; ++i) {
+                sxv[i] = row16_sum(sxv[i]);
+                sdy[i] = row16_sum(sdy[i]);
+                sxy[i] = row16_sum(sxy[i]);
+            }
             if (r == 0) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -734,8 +758,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                     if (sl == 0) a.xybuf[o] = sxy[i];
                 }
             }
-#pragma unroll
-            for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
+            lam = wave_sum(lam);
             // shares 0-3 of Lambda at the tile's end, one per wavefront (k_bwd_fin adds the 8
             // shares in a fixed order)
             if (lane == 0) a.lamb[((bh * a.ntiles + tau) * NS + sl) * 8 + w] = lam;
@@ -800,8 +823,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
                         for (int e = 0; e < 8; ++e) lam += hv[e] * ev[e];
                     }
                 }
-#pragma unroll
-            for (int m = 32; m > 0; m >>= 1) lam += __shfl_xor(lam, m);
+            lam = wave_sum(lam);
             const size_t bh = (size_t)b * H + g * HG + blk * hpb + kh;
             const float cs_r = (tau % a.tpc == 0) ? 0.f : pcr;
             if (lane == 0) a.lamb[((bh * a.ntiles + tau) * NS + sl) * 8 + 4 + w] = fast_exp2(pce - cs_r) * lam;
