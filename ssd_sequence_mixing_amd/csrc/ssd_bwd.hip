@@ -15,10 +15,9 @@
 // with h the state entering the tile; k_bwd_tile forms it as
 // 2^{cs_e - cs_r} <E, h> + sum_j 2^{cs_e - cs'_j} x_j . (E B_j) from the
 // operands it already holds, and the running sum restarts from it at every
-// tile. dA sums
-// dt_t Lambda_t, which cancels heavily; a running sum over the whole
-// sequence would carry every rounding error of the per-token scalars (bf16
-// operands) into all earlier tokens.
+// tile. dA sums dt_t Lambda_t, which cancels heavily; a running sum over the
+// whole sequence would carry every rounding error of the per-token scalars
+// (bf16 operands) into all earlier tokens.
 //
 // The work follows the chunked form of the forward (the reading report's
 // section 3.1: quadratic diagonal blocks, rank-N blocks through states handed
@@ -32,11 +31,12 @@
 //   k_state_passes, forward work-groups (the same launch)
 //                      per (batch, head): the state entering every tile
 //                      (stored in the storage type);
-//   k_bwd_tile         per (batch, tile, group, block of heads): everything
-//                      inside the tile from h (entering state) and E (arriving
-//                      adjoint): y', v, dx, the per-token scalars of Lambda,
-//                      Lambda at the tile's end, and dB, dC summed over the
-//                      block's heads;
+//   k_bwd_tile         per (batch, tile, group, block of heads, slice of the
+//                      state's columns): everything inside the tile from h
+//                      (entering state) and E (arriving adjoint): y', v, dx,
+//                      the per-token scalars of Lambda, Lambda at the tile's
+//                      end, and dB, dC summed over the block's heads;
+//   k_bwd_dx           (more than one slice) dx from the slices' fp32 parts;
 //   k_bwd_fin          per (batch, head, tile): Lambda down the tile, ddt, and
 //                      the tile's shares of dA, dD (k_bwd_heads adds them up);
 //   k_bwd_sum_bc       dB and dC summed over head blocks, in the storage type.
