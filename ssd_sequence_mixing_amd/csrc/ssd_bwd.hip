@@ -39,7 +39,8 @@
 //   k_bwd_dx           (more than one slice) dx from the slices' fp32 parts;
 //   k_bwd_fin          per (batch, head, tile): Lambda down the tile, ddt, and
 //                      the tile's shares of dA, dD (k_bwd_heads adds them up);
-//   k_bwd_sum_bc       dB and dC summed over head blocks, in the storage type.
+//   k_bwd_sum_bc       dB and dC summed over head blocks, in the storage type
+//                      (with one block per group k_bwd_tile writes them).
 // Within a tile (t the row token, j <= t and u >= t other tokens of the
 // tile, cs the chunk-local base-2 log-decays, cs' = cs - log2 dt, r / e the
 // tile's reference (token before it) and end):
@@ -925,16 +926,32 @@ __global__ __launch_bounds__(512, 1) void k_bwd_tile(BwdTileArgs a) {
             issue(min(k + 2, hpb - 1));
             __syncthreads();
         }
-        // dB, dC of this head block: part[b][t][blk][g][n] (fp32)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        if (nblk == 1) {
+            // the group's heads are all in this block: dB, dC in the storage type, real tokens only
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const size_t o =
-                    ((((size_t)b * a.Tpad + t0 + 16 * w + 4 * kg + i) * nblk + blk) * G + g) * N + n0 + 16 * nb + r;
-                a.dBp[o] = accb[nb][i];
-                a.dCp[o] = accc[nb][i];
+                const int t = t0 + 16 * w + 4 * kg + i;
+                if (t < T) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const size_t o = (((size_t)b * T + t) * G + g) * N + n0 + 16 * nb + r;
+                        reinterpret_cast<TI *>(a.dB)[o] = Tr::from_f32(accb[nb][i]);
+                        reinterpret_cast<TI *>(a.dC)[o] = Tr::from_f32(accc[nb][i]);
+                    }
+                }
             }
+        } else {
+            // dB, dC of this head block: part[b][t][blk][g][n] (fp32), added up by k_bwd_sum_bc
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const size_t o =
+                        ((((size_t)b * a.Tpad + t0 + 16 * w + 4 * kg + i) * nblk + blk) * G + g) * N + n0 + 16 * nb + r;
+                    a.dBp[o] = accb[nb][i];
+                    a.dCp[o] = accc[nb][i];
+                }
+        }
     }
 }
 
@@ -1143,7 +1160,7 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
         ta.dX = w.dX; ta.rbuf = w.rbuf; ta.qbuf = w.qbuf; ta.xybuf = w.xybuf; ta.dBp = w.dBp; ta.dCp = w.dCp;
         ta.H = (int)f.H; ta.G = (int)f.G; ta.T = (int)f.T; ta.Tpad = (int)f.Tpad; ta.ntiles = ntiles;
         ta.tpc = (int)(f.Q / kBT); ta.nblk = w.nblk; ta.lamb = w.lamb;
-        ta.dXp = w.dXp;
+        ta.dXp = w.dXp; ta.dB = w.dB; ta.dC = w.dC;
         ta.tok_stride = (size_t)(f.batch * f.H * f.Tpad);
         ta.dx_stride = (size_t)(f.batch * f.T * f.H * f.P);
         const int64_t tiles = f.batch * ntiles * f.G * w.nblk * NS;
@@ -1165,6 +1182,7 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
             launch(k_bwd_heads, dim3((unsigned)f.H), dim3(256), s, (const float *)w.dApart, (const float *)w.dDpart,
                    w.dA, w.dD, (int)f.batch, (int)f.H, ntiles) != hipSuccess)
             return SSD_ERR_HIP;
+        if (w.nblk == 1) return SSD_OK;  // k_bwd_tile wrote dB and dC
         const int64_t n = f.batch * f.T * f.G * N;
         return launch(k_bwd_sum_bc<TI>, dim3((unsigned)((n + 255) / 256)), dim3(256), s, (const float *)w.dBp,
                       (const float *)w.dCp, (TI *)w.dB, (TI *)w.dC, f.batch, (int)f.T, (int)f.Tpad, w.nblk,

@@ -109,6 +109,7 @@ struct BwdTileArgs {            // k_bwd_tile
     void *dX;
     float *rbuf, *qbuf, *xybuf; // per (batch, head, token): x.v, dy.y' - dt x.v, dy.x
     float *dBp, *dCp;           // (batch, Tpad, nblk, G, N) partial sums over head blocks
+    void *dB, *dC;              // one head block per group: dB, dC (storage type) written directly
     float *lamb;                // (batch, H, ntiles, NS, 8) per-wavefront shares of
                                 // <E_tile, state after the tile>
     float *dXp;                 // NS > 1: (NS, batch, T, H, P) fp32 parts of dX
