@@ -23,13 +23,15 @@
 // section 3.1: quadratic diagonal blocks, rank-N blocks through states handed
 // across block boundaries), in 64-token tiles:
 //   k_state_passes, reverse work-groups
-//                      per (batch, head), tiles in reverse: the adjoint
+//                      per (batch, head, slice of the state's columns;
+//                      one slice unless the pairs are too few to fill the
+//                      CUs), tiles in reverse: the adjoint
 //                      arriving at every tile from the tokens after it,
 //                      E = a ds of the next token (stored in the storage
 //                      type), and finally a_0 ds_0, the initial state's
 //                      gradient;
 //   k_state_passes, forward work-groups (the same launch)
-//                      per (batch, head): the state entering every tile
+//                      per (batch, head, column slice): the state entering every tile
 //                      (stored in the storage type);
 //   k_bwd_tile         per (batch, tile, group, block of heads, slice of the
 //                      state's columns): everything inside the tile from h
@@ -225,10 +227,14 @@ struct TileRegs {
 //   reverse: S <- 2^{cs_e - cs_r} S + sum_t 2^{cs_t - cs_r} dy_t C_t^T
 // (U = X or dY, V = B or C). The two passes share nothing, so k_state_passes
 // runs both in one launch (reverse work-groups first), two work-groups per CU.
+// Columns n of the state evolve independently (V's column n feeds only the
+// state's column n), so where (batch, head) pairs are too few to fill the
+// CUs, each pass splits the state's N columns into slices of NL, one
+// work-group per slice, each staging the whole U tile and its slice of V.
 // ---------------------------------------------------------------------------
 constexpr int SP_NW = 4;  // wavefronts per state-pass work-group
 
-template <typename TI, int P, int N>
+template <typename TI, int P, int N>  // N: the work-group's slice of the state's columns
 struct SpLds {
     static constexpr int ES = sizeof(TI), PAD = 16 / ES, T_LD = kBT + PAD, S_LD = N + PAD;
     TI UT[P * T_LD];
@@ -240,14 +246,16 @@ struct SpLds {
     float WT[kBT];
 };
 
-template <typename TI, int P, int N, bool kRev>
-__device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, N> &sm, const int bh) {
+// One pass over the state columns n0 .. n0 + NL - 1 (of N) of (batch, head) bh.
+template <typename TI, int P, int N, int NL, bool kRev>
+__device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, NL> &sm, const int bh,
+                                           const int n0) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
-    using L = SpLds<TI, P, N>;
+    using L = SpLds<TI, P, NL>;
     constexpr int ES = Tr::kBytes, T_LD = L::T_LD, S_LD = L::S_LD;
-    constexpr int NW = SP_NW, NTH = 64 * NW;  // wave w owns n-blocks w, w + NW, ...
-    constexpr int PB = P / 16, NB = N / 16, NBW = (NB + NW - 1) / NW;
+    constexpr int NW = SP_NW, NTH = 64 * NW;  // wave w owns n-blocks w, w + NW, ... of the slice
+    constexpr int PB = P / 16, NB = NL / 16, NBW = (NB + NW - 1) / NW;
     TI *const UT = sm.UT, *const VT = sm.VT, *const SS = sm.SS;
     float *const WT = sm.WT;
 
@@ -269,7 +277,8 @@ __device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, 
             const int nb = w + NW * j;
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (a.init && nb < NB)
-                v = *reinterpret_cast<const f32x4 *>(a.init + ((size_t)bh * P + 16 * pb + r) * N + 16 * nb + 4 * kg);
+                v = *reinterpret_cast<const f32x4 *>(a.init + ((size_t)bh * P + 16 * pb + r) * N + n0 + 16 * nb +
+                                                     4 * kg);
             acc[pb][j] = v;
         }
     const int ntiles = a.ntiles;
@@ -279,14 +288,14 @@ __device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, 
     // across the next load into its slot becomes a register copy at the loop's
     // back edge, and the copy waits for every load in flight).
     TileRegs<TI, kBT, P, NTH> ur[2];
-    TileRegs<TI, kBT, N, NTH> vr[2];
+    TileRegs<TI, kBT, NL, NTH> vr[2];
     float wcs[2] = {0.f, 0.f};                   // this thread's token term
     float pcs_r[2] = {0.f, 0.f}, pcs_e[2] = {0.f, 0.f};
     auto issue = [&](int tau, auto Sc) {
         constexpr int S = decltype(Sc)::value;
         const int t0 = tau * kBT;
         ur[S].load(ru, (uint32_t)(((size_t)t0 * H + h) * P * ES), (uint32_t)(H * P * ES), tid);
-        vr[S].load(rv, (uint32_t)(((size_t)t0 * G + g) * N * ES), (uint32_t)(G * N * ES), tid);
+        vr[S].load(rv, (uint32_t)((((size_t)t0 * G + g) * N + n0) * ES), (uint32_t)(G * N * ES), tid);
         // unconditional: a chunk's first tile takes 0 where the value is used
         pcs_r[S] = cs[max(t0 - 1, 0)];
         pcs_e[S] = cs[t0 + kBT - 1];
@@ -298,7 +307,7 @@ __device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, 
     auto step = [&](int it, auto Sc) {
         constexpr int S = decltype(Sc)::value;
         const int tau = tile_of(it);
-        TI *dst = reinterpret_cast<TI *>(a.Sst) + ((size_t)bh * ntiles + tau) * P * N;
+        TI *dst = reinterpret_cast<TI *>(a.Sst) + ((size_t)bh * ntiles + tau) * P * N + n0;
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb)
 #pragma unroll
@@ -313,7 +322,7 @@ __device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, 
         WT[tid & (kBT - 1)] = kRev ? fast_exp2(wcs[S] - cs_r) : fast_exp2(cs_e - wcs[S]);
         __syncthreads();  // SS and WT visible; the previous tile's reads of UT / VT are done
         {
-            constexpr int VPRS = N * ES / 16;  // 16-byte pieces per state row
+            constexpr int VPRS = NL * ES / 16;  // 16-byte pieces per row of the slice
 #pragma unroll
             for (int v = tid; v < P * VPRS; v += NTH) {
                 const int p = v / VPRS, c = v % VPRS;
@@ -362,19 +371,31 @@ __device__ __forceinline__ void state_pass(const StatePassArgs &a, SpLds<TI, P, 
             for (int j = 0; j < NBW; ++j) {
                 const int nb = w + NW * j;
                 if (nb < NB)
-                    *reinterpret_cast<f32x4 *>(a.out + ((size_t)bh * P + 16 * pb + r) * N + 16 * nb + 4 * kg) =
+                    *reinterpret_cast<f32x4 *>(a.out + ((size_t)bh * P + 16 * pb + r) * N + n0 + 16 * nb + 4 * kg) =
                         acc[pb][j];
             }
     }
 }
 
-// work-groups [0, nbh): the reverse pass; [nbh, 2 nbh): the forward pass
-template <typename TI, int P, int N>
+// work-groups [0, nbh N / NL): the reverse pass; the rest: the forward pass;
+// each (batch, head) pair's N / NL column slices are consecutive
+template <typename TI, int P, int N, int NL>
 __global__ __launch_bounds__(64 * SP_NW) void k_state_passes(StatePassArgs rev, StatePassArgs fwd, int nbh) {
-    __shared__ __attribute__((aligned(16))) SpLds<TI, P, N> sm;
-    const int x = blockIdx.x;
-    if (x < nbh) state_pass<TI, P, N, true>(rev, sm, x);
-    else state_pass<TI, P, N, false>(fwd, sm, x - nbh);
+    constexpr int NSL = N / NL;
+    __shared__ __attribute__((aligned(16))) SpLds<TI, P, NL> sm;
+    const int per = nbh * NSL;
+    const int x = (int)blockIdx.x < per ? (int)blockIdx.x : (int)blockIdx.x - per;
+    const int bh = x / NSL, n0 = (x % NSL) * NL;
+    if ((int)blockIdx.x < per) state_pass<TI, P, N, NL, true>(rev, sm, bh, n0);
+    else state_pass<TI, P, N, NL, false>(fwd, sm, bh, n0);
+}
+
+// Column slices of the state passes: halve the slice (down to 64 columns)
+// while the two passes together have fewer than two work-groups per CU.
+static int state_pass_slices(int64_t nbh, int N) {
+    int nsl = 1;
+    while (2 * nbh * nsl < 2 * 256 && N / (2 * nsl) >= 64) nsl *= 2;
+    return nsl;
 }
 
 // ---------------------------------------------------------------------------
@@ -1151,9 +1172,15 @@ static ssd_status run_bwd(const BwdArgs &w, hipStream_t s) {
         StatePassArgs rev = sp, fwd = sp;
         rev.U = w.dY; rev.V = f.C; rev.init = w.dF; rev.Sst = w.Est; rev.out = w.dinit;
         fwd.U = f.X; fwd.V = f.B; fwd.init = f.init; fwd.Sst = w.Hst; fwd.out = nullptr;
-        if (launch(k_state_passes<TI, P, N>, dim3((unsigned)(2 * nbh)), dim3(64 * SP_NW), s, rev, fwd, nbh) !=
-            hipSuccess)
-            return SSD_ERR_HIP;
+        const int nsl = state_pass_slices(nbh, N);
+        hipError_t e = hipErrorInvalidValue;
+        const dim3 grid((unsigned)(2 * nbh * nsl));
+        if (nsl == 1) e = launch(k_state_passes<TI, P, N, N>, grid, dim3(64 * SP_NW), s, rev, fwd, nbh);
+        if constexpr (N >= 128)
+            if (nsl == 2) e = launch(k_state_passes<TI, P, N, N / 2>, grid, dim3(64 * SP_NW), s, rev, fwd, nbh);
+        if constexpr (N >= 256)
+            if (nsl == 4) e = launch(k_state_passes<TI, P, N, N / 4>, grid, dim3(64 * SP_NW), s, rev, fwd, nbh);
+        if (e != hipSuccess) return SSD_ERR_HIP;
         BwdTileArgs ta = {};
         ta.X = f.X; ta.dY = w.dY; ta.B = f.B; ta.C = f.C; ta.dt = f.dt; ta.D = f.D;
         ta.Hst = w.Hst; ta.Est = w.Est; ta.cs2 = f.cs2; ta.dtf = f.dtf;
