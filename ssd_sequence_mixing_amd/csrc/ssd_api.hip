@@ -71,7 +71,7 @@ ssd_status check_fwd_shape(int64_t batch, int64_t seqlen, int64_t nheads, int64_
     lay->cs_bytes = align256(batch * nheads * Tpad * 4);
     lay->g_bytes = align256(batch * ngroups * Tpad * lay->plan.tt * es);  // one tt x tt tile per tt tokens
     if (lay->g_bytes >= kTwoGiB) return SSD_ERR_UNSUPPORTED;
-    lay->seg_bytes = align256(batch * nheads * (lay->plan.S - 1) * headdim * dstate * 4);
+    lay->seg_bytes = align256(batch * nheads * (lay->plan.S - 1) * lay->plan.segk * headdim * dstate * 4);
     lay->total = (batch == 0 || seqlen == 0) ? 0 : 2 * lay->cs_bytes + lay->g_bytes + lay->seg_bytes;
     return SSD_OK;
 }
@@ -99,6 +99,7 @@ FwdArgs make_args(const FwdLayout &lay, int64_t batch, int64_t seqlen, int64_t n
     f.tt = lay.plan.tt;
     f.S = lay.plan.S;
     f.cps = lay.plan.cps;
+    f.segk = lay.plan.segk;
     f.seg = reinterpret_cast<float *>(ws + 2 * lay.cs_bytes + lay.g_bytes);
     return f;
 }

@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
     // full walk enters segment s with the scanned state in slot s - 1
     const float *init_mat = (seg == 0) ? (a.init ? a.init + bhs * P * N : nullptr)
                             : kStateOnly ? nullptr
-                                         : a.seg + (bhs * (S - 1) + seg - 1) * P * N;
+                                         : a.seg + (bhs * (S - 1) * a.segk + seg * a.segk - 1) * P * N;
     float *out_mat = kStateOnly ? a.seg + (bhs * (S - 1) + seg) * P * N
                                 : ((seg == S - 1 && a.final_state) ? a.final_state + bhs * P * N : nullptr);
 
@@ -999,7 +999,8 @@ __global__ __launch_bounds__(kStateOnly ? 256 : 512, 1) void k_chunk_walk(WalkAr
 // D_s the segment's total log-decay (the sum of its chunks' last cs2), i.e.
 // the state passing of the chunked method at segment granularity. Rewritten in
 // place: slot s ends up holding the state entering segment s + 1. One thread
-// per 4 state elements.
+// per 4 state elements. (Where the pre-pass halves the walk's segments, the
+// segments here are those halves.)
 // ---------------------------------------------------------------------------
 static __global__ __launch_bounds__(256) void k_seg_scan(float *__restrict__ seg, const float *__restrict__ cs2,
                                                   int64_t bh_count, int PN, int S, int cps, int nC, int Q,
@@ -1104,6 +1105,10 @@ int fwd_plan(ssd_dtype dt, int64_t batch, int64_t H, int64_t P, int64_t N, int64
     plan->tt = tt;
     plan->S = S;
     plan->cps = (int)((nC + S - 1) / S);
+    // The end-state pre-pass takes each segment but the last as two halves
+    // where its chunks split evenly: twice the work-groups, each with half the
+    // tiles, for a pre-pass whose time is the length of its walks.
+    plan->segk = (S > 1 && plan->cps % 2 == 0) ? 2 : 1;
     return 0;
 }
 
@@ -1141,10 +1146,14 @@ static ssd_status run_walk_c(const FwdArgs &f, hipStream_t s) {
         wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
         wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
         wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg;
+        wa.segk = kConv ? 1 : f.segk;
         wa.cu = f.cu; wa.total = (int)f.total; wa.z = f.z;
         wa.conv_w = f.conv_w; wa.conv_b = f.conv_b;
         const int64_t heads = f.batch * f.H * f.ns;
         if (f.S > 1) {
+            // the pre-pass and the scan run over wa.segk sub-segments per
+            // segment (all segments but the last): SP - 1 of them, cpp chunks each
+            const int SP = (f.S - 1) * wa.segk + 1, cpp = f.cps / wa.segk;
             wa.SL = f.S - 1;
             if constexpr (kConv) {
                 // the segments' end states need the convolved X: the state-only walk
@@ -1152,13 +1161,16 @@ static ssd_status run_walk_c(const FwdArgs &f, hipStream_t s) {
                            s, wa) != hipSuccess)
                     return SSD_ERR_HIP;
             } else {
-                const ssd_status st = launch_seg_states(f, s);
+                FwdArgs fs = f;
+                fs.S = SP;
+                fs.cps = cpp;
+                const ssd_status st = launch_seg_states(fs, s);
                 if (st != SSD_OK) return st;
             }
             const int64_t n4 = f.batch * f.H * f.P * f.N / 4;
-            if (f.S > 2 && launch(k_seg_scan, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, f.seg,
-                                  (const float *)f.cs2, f.batch * f.H, (int)(f.P * f.N), f.S, f.cps,
-                                  (int)f.nC, (int)f.Q, (int)f.Tpad) != hipSuccess)
+            if (SP > 2 && launch(k_seg_scan, dim3((unsigned)((n4 + 255) / 256)), dim3(256), s, f.seg,
+                                 (const float *)f.cs2, f.batch * f.H, (int)(f.P * f.N), SP, cpp, (int)f.nC,
+                                 (int)f.Q, (int)f.Tpad) != hipSuccess)
                 return SSD_ERR_HIP;
         }
         if (walk_rs_supported(f)) return launch_walk_rs(f, s);

@@ -29,7 +29,8 @@ struct FwdArgs {
     int64_t g_bytes;
     int ns, tt;                // walk plan: work-groups per head, tile tokens
     int S, cps;                // walk plan: sequence segments, chunks per segment
-    float *seg;                // workspace: (batch, H, S - 1, P, N) fp32 segment states
+    int segk;                  // walk plan: pre-pass sub-segments per segment (1 or 2)
+    float *seg;                // workspace: (batch, H, (S - 1) segk, P, N) fp32 (sub-)segment states
     bool no_g;                 // the caller reads no C B^T tiles (the backward): prepare skips them
 };
 
@@ -38,6 +39,7 @@ struct FwdArgs {
 struct WalkPlan {
     int ns, tt;   // work-groups per head (P / ns columns each), tile tokens
     int S, cps;   // sequence segments walked in parallel, chunks per segment
+    int segk;     // sub-segments per segment in the end-state pre-pass (1 or 2)
 };
 // Fills the plan; -1 if no kernel covers the shape.
 // segments: whether the sequence may be split (not for packed batches).
@@ -68,7 +70,9 @@ struct WalkArgs {
     int batch, T, H, G, nC, Tpad;
     int P, NS;                 // head dimension, and the work-groups sharing each head's P columns
     int S, SL, cps;            // sequence segments, segments in this launch, chunks per segment
-    float *seg;                // (batch, H, S - 1, P, N) segment states (S > 1)
+    int segk;                  // seg holds (S - 1) segk sub-segment states per (batch, head); segment
+                               // s > 0 enters with the one in slot s segk - 1
+    float *seg;                // (batch, H, (S - 1) segk, P, N) segment states (S > 1)
     const int *cu;             // see FwdArgs
     int total;
     const void *z;             // see FwdArgs

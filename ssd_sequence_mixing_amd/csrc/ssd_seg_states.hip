@@ -41,7 +41,10 @@ struct SegCfg {
     static constexpr int ES = Traits<TI>::kBytes;
     static constexpr int TT = 64;                    // tile tokens
     static constexpr int VE = 16 / ES;               // elements per 16-byte piece
-    static constexpr int LD = TT + 16 / ES;          // token-major row length (padded by 16 bytes)
+    // token-major row length: bf16 rows are not padded (their 16-byte pieces
+    // are permuted instead, see tok_off), so that three work-groups fit a CU;
+    // fp32 rows are padded by 16 bytes
+    static constexpr int LD = ES == 2 ? TT : TT + 16 / ES;
     static constexpr int NBLK = NSL / 16, PBLK = PW / 16;
     // wavefront w keeps p-block w % PBLK and every (4 / PBLK)-th n-block from w / PBLK
     static constexpr int NSTEP = 4 / PBLK;
@@ -51,6 +54,16 @@ struct SegCfg {
     static constexpr int RB = (UB + 255) / 256, RX = (UX + 255) / 256;
     static constexpr int BT_ELEMS = NSL * LD, XT_ELEMS = PW * LD;
 };
+
+// Element offset of token column c (a multiple of 4) of row rho in a
+// token-major LDS tile. bf16: piece c / 8 of the row sits at position
+// (c / 8) ^ (rho % 8), so the 8 rows a matrix-core read covers per bank cycle
+// (16 bytes each at one piece index) fall in 8 different pieces.
+template <typename TI, int LD>
+__device__ __forceinline__ int tok_off(int rho, int c) {
+    if constexpr (sizeof(TI) == 2) return rho * LD + 8 * ((c >> 3) ^ (rho & 7)) + (c & 7);
+    else return rho * LD + c;
+}
 
 // element e of a 16-byte piece, as fp32
 template <typename TI> __device__ __forceinline__ float piece_elem(const u32x4 &v, int e);
@@ -85,7 +98,7 @@ __device__ __forceinline__ void put4(float *dst, float a, float b, float c, floa
 }  // namespace
 
 template <typename TI, int NSL, int PW>
-__global__ __launch_bounds__(256) void k_seg_states(SegArgs a) {
+__global__ __launch_bounds__(256, sizeof(TI) == 2 ? 3 : 1) void k_seg_states(SegArgs a) {
     using Tr = Traits<TI>;
     using Cfg = SegCfg<TI, NSL, PW>;
     constexpr int TT = Cfg::TT, VE = Cfg::VE, LD = Cfg::LD, ES = Cfg::ES;
@@ -180,7 +193,7 @@ __global__ __launch_bounds__(256) void k_seg_states(SegArgs a) {
             if (u >= Cfg::UB) continue;
             const int tq = u % (TT / 4), pc = u / (TT / 4);
 #pragma unroll
-            for (int e = 0; e < VE; ++e) put_col(BT + (pc * VE + e) * LD + 4 * tq, br[R][k], e);
+            for (int e = 0; e < VE; ++e) put_col(BT + tok_off<TI, LD>(pc * VE + e, 4 * tq), br[R][k], e);
         }
 #pragma unroll
         for (int k = 0; k < RX; ++k) {
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(256) void k_seg_states(SegArgs a) {
             for (int i = 0; i < 4; ++i) w[i] = fast_exp2(sc - cpr[R][k][i]);
 #pragma unroll
             for (int e = 0; e < VE; ++e)
-                put4(XT + (pc * VE + e) * LD + 4 * tq, piece_elem<TI>(xr[R][k][0], e) * w[0],
+                put4(XT + tok_off<TI, LD>(pc * VE + e, 4 * tq), piece_elem<TI>(xr[R][k][0], e) * w[0],
                      piece_elem<TI>(xr[R][k][1], e) * w[1], piece_elem<TI>(xr[R][k][2], e) * w[2],
                      piece_elem<TI>(xr[R][k][3], e) * w[3]);
         }
@@ -227,12 +240,12 @@ __global__ __launch_bounds__(256) void k_seg_states(SegArgs a) {
         const TI *XT = XTB + R * Cfg::XT_ELEMS;
 #pragma unroll
         for (int ks = 0; ks < TT / 32; ++ks) {
-            const auto fx = Tr::lds_frag(XT + (16 * pbw + r) * LD + 32 * ks + 8 * kg);
+            const auto fx = Tr::lds_frag(XT + tok_off<TI, LD>(16 * pbw + r, 32 * ks + 8 * kg));
 #pragma unroll
             for (int j = 0; j < BPW; ++j) {
                 const int nb = nbw + NSTEP * j;
                 if (NBLK % NSTEP != 0 && nb >= NBLK) continue;  // wave-uniform
-                acc[j] = Tr::mma(Tr::lds_frag(BT + (16 * nb + r) * LD + 32 * ks + 8 * kg), fx, acc[j]);
+                acc[j] = Tr::mma(Tr::lds_frag(BT + tok_off<TI, LD>(16 * nb + r, 32 * ks + 8 * kg)), fx, acc[j]);
             }
         }
         // the tile before this one into the other slot (last read a step ago)

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(512, 1) void k_walk_rs(WalkArgs a) {
     const int last_tile = max(ce * NT - 1, cb * NT);
     const size_t bhs = (size_t)bhi;
     const float *init_mat = (seg == 0) ? (a.init ? a.init + bhs * P * N : nullptr)
-                                       : a.seg + (bhs * (S - 1) + seg - 1) * P * N;
+                                       : a.seg + (bhs * (S - 1) * a.segk + seg * a.segk - 1) * P * N;
     float *out_mat = (seg == S - 1 && a.final_state) ? a.final_state + bhs * P * N : nullptr;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -830,6 +830,7 @@ static ssd_status run_walk_rs(const FwdArgs &f, hipStream_t s) {
         wa.batch = (int)f.batch; wa.T = (int)f.T; wa.H = (int)f.H; wa.G = (int)f.G; wa.nC = (int)f.nC;
         wa.Tpad = (int)f.Tpad; wa.P = (int)f.P; wa.NS = f.ns; wa.g_bytes = (uint32_t)f.g_bytes;
         wa.S = f.S; wa.cps = f.cps; wa.seg = f.seg; wa.SL = f.S;
+        wa.segk = f.conv_w ? 1 : f.segk;  // the convolution walks' pre-pass takes whole segments
         wa.cu = f.cu; wa.total = (int)f.total; wa.z = f.z;
         wa.conv_w = f.conv_w; wa.conv_b = f.conv_b;
         const int64_t heads = f.batch * f.H * f.ns;

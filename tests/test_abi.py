@@ -64,10 +64,11 @@ def test_workspace_query():
     n = ws(4, 2048, 64, 64, 128, 1, 256, BF16)
     # two fp32 (b, H, Tpad) arrays plus the bf16 C B^T of every 64-token tile
     assert n == 2 * 4 * 64 * 2048 * 4 + 4 * 1 * 32 * 64 * 64 * 2
-    # 16K tokens, 64 heads: the sequence is walked as 4 segments, whose end
-    # states (3 of them) take (b, H, 3, P, N) fp32 more
+    # 16K tokens, 64 heads: the sequence is walked as 4 segments; the end
+    # states of the first 3, each in two halves of 8 chunks, take
+    # (b, H, 6, P, N) fp32 more
     n = ws(1, 16384, 64, 64, 256, 8, 256, BF16)
-    assert n == 2 * 64 * 16384 * 4 + 8 * 16384 * 64 * 2 + 64 * 3 * 64 * 256 * 4
+    assert n == 2 * 64 * 16384 * 4 + 8 * 16384 * 64 * 2 + 64 * 6 * 64 * 256 * 4
     assert ws(0, 2048, 64, 64, 128, 1, 256, BF16) == 0
     assert ws(4, 0, 64, 64, 128, 1, 256, BF16) == 0
     assert ws(4, 2048, 64, 64, 128, 3, 256, BF16) == big      # H % G

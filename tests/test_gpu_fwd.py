@@ -234,6 +234,36 @@ def test_walk_from_initial_state(ssd, dtype, chunk):
     assert max(e) <= tol, e
 
 
+@pytest.mark.parametrize("dtype,T,chunk,init", [("bf16", 1000, 64, False), ("bf16", 950, 64, True),
+                                                 ("f32", 1000, 64, True), ("bf16", 2048, 128, False)])
+def test_split_sequence_halved_prepass(ssd, dtype, T, chunk, init):
+    """Few heads and a long sequence: the walk cuts the sequence into segments
+    (8 of 2 chunks at 16 chunks, 4 of 4 at 15 chunks, the last one partial),
+    and the end-state pre-pass takes each segment but the last as two halves,
+    whose states the scan chains into the segments' entering states; with and
+    without an initial state (which enters the first half only)."""
+    import torch
+    import oracle
+    base = si.CONFIGS["l1p3b_bf16"] if dtype == "bf16" else si.CONFIGS["tiny_f32"]
+    over = dict(headdim=64, dstate=128) if dtype == "bf16" else dict(headdim=32, dstate=64)
+    cfg = dataclasses.replace(base, name=f"split_{dtype}_{T}", batch=1, seqlen=T, nheads=2, ngroups=2,
+                              seed=73 + T % 7, **over)
+    inp = si.make_fwd_inputs(cfg)
+    h0 = np.random.default_rng(74).standard_normal((1, 2, cfg.headdim, cfg.dstate)).astype(np.float32) \
+        if init else None
+    log(f"[fwd] split sequence {dtype} T {T} chunk {chunk} init {init}")
+    X, dt, B, C = (to_dev(inp[k]) for k in ("X", "dt", "B", "C"))
+    A, D = to_dev(inp["A"]), to_dev(inp["D"])
+    ws = ssd.ssd_chunk_scan_prepare(dt, A, B, C, chunk, cfg.headdim)
+    Y, F = ssd.ssd_chunk_scan_walk(X, B, C, D, ws, chunk, initial_state=None if h0 is None else to_dev(h0))
+    torch.cuda.synchronize()
+    Yr, Fr, _ = oracle.fwd(inp["X32"], inp["dt32"], inp["A"], inp["B32"], inp["C32"], inp["D"], cfg.ngroups,
+                           init_state=h0)
+    e = (rel(Y.float().cpu().numpy(), Yr), rel(F.cpu().numpy(), Fr))
+    log(f"    rel err Y={e[0]:.2e} final={e[1]:.2e}")
+    assert max(e) <= TOL[cfg.dtype], e
+
+
 def test_resume_across_calls(ssd):
     """Forward over [0, T1), then a walk over [T1, T) from the carried final
     state, reproduces one forward over [0, T) to the bf16 tolerance."""
