@@ -78,10 +78,9 @@ template <typename TI, int Q>
 __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, const float *__restrict__ A,
                                           float *__restrict__ cs2, float *__restrict__ dtf, int Tmax, int H,
                                           int nC, int Tpad, const int *cu, int total,
-                                          const float *__restrict__ dt_bias, int softplus) {
+                                          const float *__restrict__ dt_bias, int softplus, float *tile) {
     constexpr int ES = Traits<TI>::kBytes;
-    constexpr int LD = Q + 1;
-    __shared__ float tile[kCumsumHeads * LD];
+    constexpr int LD = Q + 1;  // the caller's tile holds kCumsumHeads * LD floats
     const int hblocks = (H + kCumsumHeads - 1) / kCumsumHeads;
     int x = blk;
     const int c = x % nC;
@@ -172,7 +171,7 @@ __device__ __forceinline__ void dt_cumsum(int blk, const TI *__restrict__ dt, co
 template <typename TI, int N, int TT>
 __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, const TI *__restrict__ Cm,
                                         TI *__restrict__ Gout, int Tmax, int G, int ntiles, uint32_t g_bytes,
-                                        const int *cu, int total) {
+                                        const int *cu, int total, TI *bsh) {
     using Tr = Traits<TI>;
     using frag = typename Tr::frag;
     constexpr int ES = Tr::kBytes;
@@ -211,7 +210,7 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
     constexpr bool kBLds = N >= 256;
     constexpr int BLD = N + 16 / ES;                 // row length, padded by 16 bytes
     constexpr int PPR = N * ES / 16;                 // 16-byte pieces per row
-    __shared__ __attribute__((aligned(16))) TI bsh[kBLds ? 64 * BLD : 1];
+    // bsh: the caller's LDS, 64 * BLD elements
     for (int cgp = 0; cgp <= band; ++cgp) {  // 64-column groups up to the band's diagonal
         frag bk[4][NK];
         if constexpr (kBLds) {
@@ -272,13 +271,18 @@ __device__ __forceinline__ void tile_cb(int blk, const TI *__restrict__ Bm, cons
 // ---------------------------------------------------------------------------
 template <typename TI, int Q, int N, int TT>
 __global__ __launch_bounds__(256) void k_prepare(PrepArgs a) {
+    // one LDS buffer for whichever job the work-group runs (the C B^T job
+    // stages B rows only for N >= 256), so that more work-groups fit a CU
+    constexpr int kCbBytes = N >= 256 ? 64 * (N + 16 / (int)sizeof(TI)) * (int)sizeof(TI) : 0;
+    constexpr int kCsBytes = kCumsumHeads * (Q + 1) * 4;
+    __shared__ __attribute__((aligned(16))) char lds[kCbBytes > kCsBytes ? kCbBytes : kCsBytes];
     const int blk = blockIdx.x;
     if (blk < a.cb_blocks) {
         tile_cb<TI, N, TT>(blk, (const TI *)a.B, (const TI *)a.C, (TI *)a.Gbuf, a.T, a.G, a.ntiles, a.g_bytes,
-                           a.cu, a.total);
+                           a.cu, a.total, reinterpret_cast<TI *>(lds));
     } else {
         dt_cumsum<TI, Q>(blk - a.cb_blocks, (const TI *)a.dt, a.A, a.cs2, a.dtf, a.T, a.H, a.nC, a.Tpad, a.cu,
-                         a.total, a.dt_bias, a.softplus);
+                         a.total, a.dt_bias, a.softplus, reinterpret_cast<float *>(lds));
     }
 }
 
