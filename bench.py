@@ -8,15 +8,20 @@ i.e. ssd_chunk_scan_fwd) over one batch of the 1.3B-layer workload
 (batch 4, T 2048, 64 heads, P 64, N 128, one group, chunk 256, bf16
 storage), with inputs resident in HBM. Three independent input / output /
 workspace sets rotate (444 MB together, more than the 256 MB Infinity Cache),
-so no step reads the previous step's data from the cache. The K timed steps
-run back to back between two events; events at the boundaries of R equal
-sub-blocks give the median per-step time beside the mean. The 125M-layer and
-16K-token shapes are timed the same way (fewer steps) and reported under
-"shapes". The decode step is timed after the forward: 1000 ssd_step calls on
-the 256 x 64 x 64 x 128 fp32 state, then 50 forwards with the fused layer
-prologue / epilogue (ssd_chunk_scan_fwd_fused) and 20 backward passes
-(ssd_chunk_scan_bwd) of the forward workload (and 5 of the 16K-token one),
-reported beside the forward.
+so no step reads the previous step's data from the cache. After W untimed
+steps, the K timed steps run back to back between two events; events at the
+boundaries of R equal sub-blocks give the median per-step time beside the
+mean.
+
+The other measurements run before the forward's: the 125M-layer and 16K-token
+forwards (timed like the main one, fewer steps, under "shapes"), 50 forwards
+with the fused layer prologue / epilogue (ssd_chunk_scan_fwd_fused), 20
+backward passes (ssd_chunk_scan_bwd) of the forward workload (and 5 of the
+16K-token one) and 1000 ssd_step calls on the 256 x 64 x 64 x 128 fp32 state
+(decode). The forward is timed last, straight after the decode steps, so that
+it runs on a GPU whose clocks have left their idle state: from idle the same
+forward takes ~10% longer for the first few tens of milliseconds, longer than a
+short timed run lasts.
 Prints one JSON line.
 
 The oracle is timed beside the GPU on a bounded sample of the same workload
@@ -368,6 +373,158 @@ def main():
         return
 
     K = args.steps
+    # The other GPU workloads first: the forward is timed last, on a GPU whose
+    # clocks have left their idle state (see the module docstring). Every input
+    # is made before any of them runs, so that the GPU work runs back to back
+    # with no long host-side pause between the sections.
+    sections = {}
+    shape_names = [] if args.no_shapes else [n for n in ("l125m_bf16", "long16k_bf16") if n != args.workload]
+    shape_sets = {n: make_sets(si.CONFIGS[n], si.CONFIGS[n].chunk, 3 if n == "l125m_bf16" else 2)[0]
+                  for n in shape_names}
+    if not args.no_decode:
+        dc = si.DECODE
+        d = si.make_decode_inputs(dc)
+        state = up(d["state0"])
+        A_d, D_d = up(d["A"]), up(d["D"])
+        dsets = [{k: up(v) for k, v in s.items() if not k.endswith("32")} for s in d["sets"]]
+        y = torch.empty_like(dsets[0]["x"])
+        del d
+    torch.cuda.synchronize()
+
+    if shape_names:
+        # the other two forward workloads, timed the same way with fewer steps
+        sections["shapes"] = {}
+        for name in shape_names:
+            c2 = si.CONFIGS[name]
+            s2 = shape_sets[name]
+            tm2 = time_forward(s2, max(10, K // 4), 5, args.repeats)
+            _, summ = shape_summary(c2, c2.chunk, tm2)
+            summ["workload"] = WORKLOAD_NAMES[name]
+            summ["config"] = {"batch": c2.batch, "seqlen": c2.seqlen, "nheads": c2.nheads, "headdim": c2.headdim,
+                              "dstate": c2.dstate, "ngroups": c2.ngroups, "chunk": c2.chunk}
+            sections["shapes"][name] = summ
+
+    if not args.no_fused:
+        # the forward with the layer's fused prologue and epilogue (causal conv1d +
+        # SiLU on X, softplus(dt + bias), Y * SiLU(z)) on the same workload. The
+        # step sizes arrive before their activation: raw N(0, 1) with bias -4,
+        # so softplus(raw + bias) has the plain workload's distribution.
+        t = sets[0]
+        rng = np.random.default_rng(8)
+        cw = up((0.5 * rng.standard_normal((H * P, 4))).astype(np.float32))
+        cb = up((0.1 * rng.standard_normal(H * P)).astype(np.float32))
+        dtb = up(np.full(H, -4.0, dtype=np.float32))
+        dt_raw = up(si.bf16_round_bits(rng.standard_normal((Bz, T, H)).astype(np.float32)))
+        zz = torch.empty_like(t["X"]).normal_()
+        Yf = torch.empty_like(t["X"])
+        Ff = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dev)
+        # arguments marshalled once, as for the forward: the timed loop is C calls only
+        fargs = (t["X"].data_ptr(), cw.data_ptr(), cb.data_ptr(), dt_raw.data_ptr(), dtb.data_ptr(), 1,
+                 t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(), zz.data_ptr(), chunk,
+                 Yf.data_ptr(), Ff.data_ptr(), Bz, T, H, P, N, G, code, t["W"].data_ptr(), t["W"].numel(), sptr)
+
+        def fused():
+            st = lib.ssd_chunk_scan_fwd_fused(*fargs)
+            if st:
+                raise ssd.SSDError(st, "ssd_chunk_scan_fwd_fused")
+        for _ in range(5):
+            fused()
+        torch.cuda.synchronize()
+        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fs.record(stream)
+        for _ in range(50):
+            fused()
+        fe.record(stream)
+        torch.cuda.synchronize()
+        ms_f = fs.elapsed_time(fe) / 50
+        es = 2 if cfg.dtype == "bf16" else 4
+        fbytes = fwd_accounting(cfg, chunk)["bytes"] + Bz * T * H * P * es  # plus z
+        sections["fused"] = {"workload": WORKLOAD_NAMES[args.workload] + ", conv1d(4)+SiLU on X, softplus(dt+bias) "
+                                         "with raw dt ~ N(0,1) and bias -4, Y*SiLU(z)", "ms_per_call": ms_f,
+                             "tokens_per_s": Bz * T / (ms_f / 1e3),
+                        "algorithmic_bytes": fbytes, "hbm_frac": fbytes / (ms_f / 1e3) / 1e9 / HBM_PEAK_GBS}
+        del zz, Yf, Ff, dt_raw
+
+    bwd_ok = not args.no_backward and cfg.dtype == "bf16"
+    if bwd_ok:
+        try:
+            ssd.ssd_chunk_scan_bwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
+        except ssd.SSDError:
+            bwd_ok = False  # no backward kernel for this shape (e.g. N 256)
+            sections["backward"] = None
+    def time_backward(bcfg, t, bchunk, steps):
+        """ssd_chunk_scan_bwd on input set t of workload bcfg: `steps` calls
+        between two events, after 3 untimed ones (arguments marshalled once)."""
+        bcode = ssd.SSD_BF16 if bcfg.dtype == "bf16" else ssd.SSD_F32
+        b_, t_, h_, p_, n_, g_ = bcfg.batch, bcfg.seqlen, bcfg.nheads, bcfg.headdim, bcfg.dstate, bcfg.ngroups
+        rng = np.random.default_rng(7)
+        dY = up(si.bf16_round_bits(rng.standard_normal((b_, t_, h_, p_)).astype(np.float32)))
+        nb = ssd.ssd_chunk_scan_bwd_workspace_bytes(b_, t_, h_, p_, n_, g_, bchunk, bcode)
+        bws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        g = {"dX": torch.empty_like(t["X"]), "ddt": torch.empty_like(t["dt"]), "dB": torch.empty_like(t["B"]),
+             "dC": torch.empty_like(t["C"]), "dA": torch.empty_like(t["A"]), "dD": torch.empty_like(t["D"])}
+        bargs = (t["X"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
+                 t["D"].data_ptr(), bchunk, None, dY.data_ptr(), None, g["dX"].data_ptr(), g["ddt"].data_ptr(),
+                 g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(), g["dD"].data_ptr(), None,
+                 b_, t_, h_, p_, n_, g_, bcode, bws.data_ptr(), nb, sptr)
+
+        def bwd():
+            st = lib.ssd_chunk_scan_bwd(*bargs)
+            if st:
+                raise ssd.SSDError(st, "ssd_chunk_scan_bwd")
+        for _ in range(3):
+            bwd()
+        torch.cuda.synchronize()
+        bs, be = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        bs.record(stream)
+        for _ in range(steps):
+            bwd()
+        be.record(stream)
+        torch.cuda.synchronize()
+        ms_b = bs.elapsed_time(be) / steps
+        bbytes = bwd_accounting(bcfg)
+        del bws, dY, g
+        return {"workload": WORKLOAD_NAMES.get(bcfg.name, bcfg.name), "ms_per_call": ms_b, "tokens_per_s": b_ * t_ / (ms_b / 1e3),
+                "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
+                "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS}
+
+    if bwd_ok:
+        # one backward (ssd_chunk_scan_bwd) of the same workload; its states per
+        # 64-token tile (2 x 134 MB at the 1.3B shape) already exceed the cache
+        sections["backward"] = time_backward(cfg, sets[0], chunk, args.backward_steps)
+        sections["backward"]["kernels"] = ("k_state_passes (both state passes, one launch), k_bwd_tile, k_bwd_fin, "
+                                      "k_bwd_heads, k_bwd_sum_bc (+ k_prepare; k_bwd_dx where the n axis is split)")
+        if not args.no_shapes and args.workload != "long16k_bf16":
+            # the 16K-token workload's backward (N 256: the tile kernel takes the n axis in 2 slices)
+            c3 = si.CONFIGS["long16k_bf16"]
+            s3 = shape_sets["long16k_bf16"]
+            sections["backward"]["long16k_bf16"] = time_backward(c3, s3[0], c3.chunk, max(5, args.backward_steps // 4))
+
+    # the decode step last before the forward: 180 ms of back-to-back GPU work
+    if not args.no_decode:
+        dcode = ssd.SSD_BF16
+        dargs = [(state.data_ptr(), s["x"].data_ptr(), s["dt"].data_ptr(), A_d.data_ptr(),
+                  s["B"].data_ptr(), s["C"].data_ptr(), D_d.data_ptr(), y.data_ptr(), dc.batch,
+                  dc.nheads, dc.headdim, dc.dstate, dc.ngroups, dcode, sptr) for s in dsets]
+        for i in range(10):
+            lib.ssd_step(*dargs[i % len(dargs)])
+        torch.cuda.synchronize()
+        ds, de = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ds.record(stream)
+        for i in range(args.decode_steps):
+            if lib.ssd_step(*dargs[i % len(dargs)]):
+                raise RuntimeError("ssd_step failed")
+        de.record(stream)
+        torch.cuda.synchronize()
+        us = ds.elapsed_time(de) * 1e3 / args.decode_steps
+        dacc = decode_accounting(dc)
+        gbs = dacc["bytes"] / (us / 1e6) / 1e9
+        sections["decode"] = {"workload": "ssd_step batch 256, 64 heads, P 64, N 128, fp32 state",
+                         "steps": args.decode_steps, "us_per_step": us, "GB/s": gbs,
+                         "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": dacc["bytes"],
+                         "kernel": "k_step"}
+        del state, dsets
+
     tm = time_forward(sets, K, args.warmup, args.repeats)
     ms_step, prep_ms, walk_ms, wall_s = tm["ms_step"], tm["ms_prepare"], tm["ms_walk"], tm["wall_s"]
 
@@ -411,151 +568,9 @@ def main():
                     "algorithmic_bytes": acc["bytes"]},
         "device": device_info(torch),
     }
-
-    if not args.no_shapes:
-        # the other two forward workloads, timed the same way with fewer steps
-        out["shapes"] = {}
-        for name, nsets in (("l125m_bf16", 3), ("long16k_bf16", 2)):
-            if name == args.workload:
-                continue
-            c2 = si.CONFIGS[name]
-            s2, _ = make_sets(c2, c2.chunk, nsets)
-            tm2 = time_forward(s2, max(10, K // 4), 5, args.repeats)
-            _, summ = shape_summary(c2, c2.chunk, tm2)
-            summ["workload"] = WORKLOAD_NAMES[name]
-            summ["config"] = {"batch": c2.batch, "seqlen": c2.seqlen, "nheads": c2.nheads, "headdim": c2.headdim,
-                              "dstate": c2.dstate, "ngroups": c2.ngroups, "chunk": c2.chunk}
-            out["shapes"][name] = summ
-            del s2
-        torch.cuda.empty_cache()
-
-    if not args.no_decode:
-        dc = si.DECODE
-        d = si.make_decode_inputs(dc)
-        state = up(d["state0"])
-        A_d, D_d = up(d["A"]), up(d["D"])
-        dsets = [{k: up(v) for k, v in s.items() if not k.endswith("32")} for s in d["sets"]]
-        y = torch.empty_like(dsets[0]["x"])
-        dcode = ssd.SSD_BF16
-        dargs = [(state.data_ptr(), s["x"].data_ptr(), s["dt"].data_ptr(), A_d.data_ptr(),
-                  s["B"].data_ptr(), s["C"].data_ptr(), D_d.data_ptr(), y.data_ptr(), dc.batch,
-                  dc.nheads, dc.headdim, dc.dstate, dc.ngroups, dcode, sptr) for s in dsets]
-        for i in range(10):
-            lib.ssd_step(*dargs[i % len(dargs)])
-        torch.cuda.synchronize()
-        ds, de = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ds.record(stream)
-        for i in range(args.decode_steps):
-            if lib.ssd_step(*dargs[i % len(dargs)]):
-                raise RuntimeError("ssd_step failed")
-        de.record(stream)
-        torch.cuda.synchronize()
-        us = ds.elapsed_time(de) * 1e3 / args.decode_steps
-        dacc = decode_accounting(dc)
-        gbs = dacc["bytes"] / (us / 1e6) / 1e9
-        out["decode"] = {"workload": "ssd_step batch 256, 64 heads, P 64, N 128, fp32 state",
-                         "steps": args.decode_steps, "us_per_step": us, "GB/s": gbs,
-                         "hbm_frac": gbs / HBM_PEAK_GBS, "bytes_per_step": dacc["bytes"],
-                         "kernel": "k_step"}
-        del state, dsets
-
-    if not args.no_fused:
-        # the forward with the layer's fused prologue and epilogue (causal conv1d +
-        # SiLU on X, softplus(dt + bias), Y * SiLU(z)) on the same workload. The
-        # step sizes arrive before their activation: raw N(0, 1) with bias -4,
-        # so softplus(raw + bias) has the plain workload's distribution.
-        t = sets[0]
-        rng = np.random.default_rng(8)
-        cw = up((0.5 * rng.standard_normal((H * P, 4))).astype(np.float32))
-        cb = up((0.1 * rng.standard_normal(H * P)).astype(np.float32))
-        dtb = up(np.full(H, -4.0, dtype=np.float32))
-        dt_raw = up(si.bf16_round_bits(rng.standard_normal((Bz, T, H)).astype(np.float32)))
-        zz = torch.empty_like(t["X"]).normal_()
-        Yf = torch.empty_like(t["X"])
-        Ff = torch.empty((Bz, H, P, N), dtype=torch.float32, device=dev)
-        # arguments marshalled once, as for the forward: the timed loop is C calls only
-        fargs = (t["X"].data_ptr(), cw.data_ptr(), cb.data_ptr(), dt_raw.data_ptr(), dtb.data_ptr(), 1,
-                 t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(), t["D"].data_ptr(), zz.data_ptr(), chunk,
-                 Yf.data_ptr(), Ff.data_ptr(), Bz, T, H, P, N, G, code, t["W"].data_ptr(), t["W"].numel(), sptr)
-
-        def fused():
-            st = lib.ssd_chunk_scan_fwd_fused(*fargs)
-            if st:
-                raise ssd.SSDError(st, "ssd_chunk_scan_fwd_fused")
-        for _ in range(5):
-            fused()
-        torch.cuda.synchronize()
-        fs, fe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fs.record(stream)
-        for _ in range(50):
-            fused()
-        fe.record(stream)
-        torch.cuda.synchronize()
-        ms_f = fs.elapsed_time(fe) / 50
-        es = 2 if cfg.dtype == "bf16" else 4
-        fbytes = fwd_accounting(cfg, chunk)["bytes"] + Bz * T * H * P * es  # plus z
-        out["fused"] = {"workload": out["config"]["workload"] + ", conv1d(4)+SiLU on X, softplus(dt+bias) with "
-                                    "raw dt ~ N(0,1) and bias -4, Y*SiLU(z)", "ms_per_call": ms_f,
-                        "tokens_per_s": Bz * T / (ms_f / 1e3), "vs_plain_forward": ms_f / ms_step,
-                        "algorithmic_bytes": fbytes, "hbm_frac": fbytes / (ms_f / 1e3) / 1e9 / HBM_PEAK_GBS}
-        del zz, Yf, Ff, dt_raw
-
-    bwd_ok = not args.no_backward and cfg.dtype == "bf16"
-    if bwd_ok:
-        try:
-            ssd.ssd_chunk_scan_bwd_workspace_bytes(Bz, T, H, P, N, G, chunk, code)
-        except ssd.SSDError:
-            bwd_ok = False  # no backward kernel for this shape (e.g. N 256)
-            out["backward"] = None
-    def time_backward(bcfg, t, bchunk, steps):
-        """ssd_chunk_scan_bwd on input set t of workload bcfg: `steps` calls
-        between two events, after 3 untimed ones (arguments marshalled once)."""
-        bcode = ssd.SSD_BF16 if bcfg.dtype == "bf16" else ssd.SSD_F32
-        b_, t_, h_, p_, n_, g_ = bcfg.batch, bcfg.seqlen, bcfg.nheads, bcfg.headdim, bcfg.dstate, bcfg.ngroups
-        rng = np.random.default_rng(7)
-        dY = up(si.bf16_round_bits(rng.standard_normal((b_, t_, h_, p_)).astype(np.float32)))
-        nb = ssd.ssd_chunk_scan_bwd_workspace_bytes(b_, t_, h_, p_, n_, g_, bchunk, bcode)
-        bws = torch.empty(nb, dtype=torch.uint8, device=dev)
-        g = {"dX": torch.empty_like(t["X"]), "ddt": torch.empty_like(t["dt"]), "dB": torch.empty_like(t["B"]),
-             "dC": torch.empty_like(t["C"]), "dA": torch.empty_like(t["A"]), "dD": torch.empty_like(t["D"])}
-        bargs = (t["X"].data_ptr(), t["dt"].data_ptr(), t["A"].data_ptr(), t["B"].data_ptr(), t["C"].data_ptr(),
-                 t["D"].data_ptr(), bchunk, None, dY.data_ptr(), None, g["dX"].data_ptr(), g["ddt"].data_ptr(),
-                 g["dA"].data_ptr(), g["dB"].data_ptr(), g["dC"].data_ptr(), g["dD"].data_ptr(), None,
-                 b_, t_, h_, p_, n_, g_, bcode, bws.data_ptr(), nb, sptr)
-
-        def bwd():
-            st = lib.ssd_chunk_scan_bwd(*bargs)
-            if st:
-                raise ssd.SSDError(st, "ssd_chunk_scan_bwd")
-        for _ in range(3):
-            bwd()
-        torch.cuda.synchronize()
-        bs, be = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        bs.record(stream)
-        for _ in range(steps):
-            bwd()
-        be.record(stream)
-        torch.cuda.synchronize()
-        ms_b = bs.elapsed_time(be) / steps
-        bbytes = bwd_accounting(bcfg)
-        del bws, dY, g
-        return {"workload": WORKLOAD_NAMES.get(bcfg.name, bcfg.name), "ms_per_call": ms_b, "tokens_per_s": b_ * t_ / (ms_b / 1e3),
-                "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
-                "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS}
-
-    if bwd_ok:
-        # one backward (ssd_chunk_scan_bwd) of the same workload; its states per
-        # 64-token tile (2 x 134 MB at the 1.3B shape) already exceed the cache
-        out["backward"] = time_backward(cfg, sets[0], chunk, args.backward_steps)
-        out["backward"]["kernels"] = ("k_state_passes (both state passes, one launch), k_bwd_tile, k_bwd_fin, "
-                                      "k_bwd_heads, k_bwd_sum_bc (+ k_prepare; k_bwd_dx where the n axis is split)")
-        if not args.no_shapes and args.workload != "long16k_bf16":
-            # the 16K-token workload's backward (N 256: the tile kernel takes the n axis in 2 slices)
-            c3 = si.CONFIGS["long16k_bf16"]
-            s3, _ = make_sets(c3, c3.chunk, 1)
-            out["backward"]["long16k_bf16"] = time_backward(c3, s3[0], c3.chunk, max(5, args.backward_steps // 4))
-            del s3
-            torch.cuda.empty_cache()
+    out.update(sections)
+    if "fused" in out:
+        out["fused"]["vs_plain_forward"] = out["fused"]["ms_per_call"] / ms_step
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(first_inp, cfg)
