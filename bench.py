@@ -13,15 +13,16 @@ steps, the K timed steps run back to back between two events; events at the
 boundaries of R equal sub-blocks give the median per-step time beside the
 mean.
 
-The other measurements run before the forward's: the 125M-layer and 16K-token
-forwards (timed like the main one, fewer steps, under "shapes"), 50 forwards
+The other measurements run before the forward's, in this order: 50 forwards
 with the fused layer prologue / epilogue (ssd_chunk_scan_fwd_fused), 20
 backward passes (ssd_chunk_scan_bwd) of the forward workload (and 5 of the
-16K-token one) and 1000 ssd_step calls on the 256 x 64 x 64 x 128 fp32 state
-(decode). The forward is timed last, straight after the decode steps, so that
-it runs on a GPU whose clocks have left their idle state: from idle the same
-forward takes ~10% longer for the first few tens of milliseconds, longer than a
-short timed run lasts.
+16K-token one), the 125M-layer and 16K-token forwards (timed like the main
+one, fewer steps, under "shapes") and 1000 ssd_step calls on the
+256 x 64 x 64 x 128 fp32 state (decode). Every input is made before the first
+of them, so the GPU work runs back to back, and the forward comes last,
+straight after the decode steps: from an idle GPU the same forward takes ~10%
+longer for the first few tens of milliseconds, longer than a short timed run
+lasts.
 Prints one JSON line.
 
 The oracle is timed beside the GPU on a bounded sample of the same workload
@@ -389,20 +390,14 @@ def main():
         dsets = [{k: up(v) for k, v in s.items() if not k.endswith("32")} for s in d["sets"]]
         y = torch.empty_like(dsets[0]["x"])
         del d
+    # the backward's output gradient dY ~ N(0, 1), rounded to bf16, per timed workload
+    bwd_dy = {}
+    if not args.no_backward and cfg.dtype == "bf16":
+        for bc in [cfg] + ([si.CONFIGS["long16k_bf16"]] if "long16k_bf16" in shape_names else []):
+            rng = np.random.default_rng(7)
+            bwd_dy[bc.name] = up(si.bf16_round_bits(
+                rng.standard_normal((bc.batch, bc.seqlen, bc.nheads, bc.headdim)).astype(np.float32)))
     torch.cuda.synchronize()
-
-    if shape_names:
-        # the other two forward workloads, timed the same way with fewer steps
-        sections["shapes"] = {}
-        for name in shape_names:
-            c2 = si.CONFIGS[name]
-            s2 = shape_sets[name]
-            tm2 = time_forward(s2, max(10, K // 4), 5, args.repeats)
-            _, summ = shape_summary(c2, c2.chunk, tm2)
-            summ["workload"] = WORKLOAD_NAMES[name]
-            summ["config"] = {"batch": c2.batch, "seqlen": c2.seqlen, "nheads": c2.nheads, "headdim": c2.headdim,
-                              "dstate": c2.dstate, "ngroups": c2.ngroups, "chunk": c2.chunk}
-            sections["shapes"][name] = summ
 
     if not args.no_fused:
         # the forward with the layer's fused prologue and epilogue (causal conv1d +
@@ -457,8 +452,7 @@ def main():
         between two events, after 3 untimed ones (arguments marshalled once)."""
         bcode = ssd.SSD_BF16 if bcfg.dtype == "bf16" else ssd.SSD_F32
         b_, t_, h_, p_, n_, g_ = bcfg.batch, bcfg.seqlen, bcfg.nheads, bcfg.headdim, bcfg.dstate, bcfg.ngroups
-        rng = np.random.default_rng(7)
-        dY = up(si.bf16_round_bits(rng.standard_normal((b_, t_, h_, p_)).astype(np.float32)))
+        dY = bwd_dy[bcfg.name]
         nb = ssd.ssd_chunk_scan_bwd_workspace_bytes(b_, t_, h_, p_, n_, g_, bchunk, bcode)
         bws = torch.empty(nb, dtype=torch.uint8, device=dev)
         g = {"dX": torch.empty_like(t["X"]), "ddt": torch.empty_like(t["dt"]), "dB": torch.empty_like(t["B"]),
@@ -483,7 +477,7 @@ def main():
         torch.cuda.synchronize()
         ms_b = bs.elapsed_time(be) / steps
         bbytes = bwd_accounting(bcfg)
-        del bws, dY, g
+        del bws, g
         return {"workload": WORKLOAD_NAMES.get(bcfg.name, bcfg.name), "ms_per_call": ms_b, "tokens_per_s": b_ * t_ / (ms_b / 1e3),
                 "algorithmic_bytes": bbytes, "GB/s": bbytes / (ms_b / 1e3) / 1e9,
                 "hbm_frac": bbytes / (ms_b / 1e3) / 1e9 / HBM_PEAK_GBS}
@@ -500,7 +494,21 @@ def main():
             s3 = shape_sets["long16k_bf16"]
             sections["backward"]["long16k_bf16"] = time_backward(c3, s3[0], c3.chunk, max(5, args.backward_steps // 4))
 
-    # the decode step last before the forward: 180 ms of back-to-back GPU work
+    # the other two forward shapes
+    if shape_names:
+        # the other two forward workloads, timed the same way with fewer steps
+        sections["shapes"] = {}
+        for name in shape_names:
+            c2 = si.CONFIGS[name]
+            s2 = shape_sets[name]
+            tm2 = time_forward(s2, max(10, K // 4), 5, args.repeats)
+            _, summ = shape_summary(c2, c2.chunk, tm2)
+            summ["workload"] = WORKLOAD_NAMES[name]
+            summ["config"] = {"batch": c2.batch, "seqlen": c2.seqlen, "nheads": c2.nheads, "headdim": c2.headdim,
+                              "dstate": c2.dstate, "ngroups": c2.ngroups, "chunk": c2.chunk}
+            sections["shapes"][name] = summ
+
+    # the decode steps straight before the forward: 180 ms of back-to-back GPU work
     if not args.no_decode:
         dcode = ssd.SSD_BF16
         dargs = [(state.data_ptr(), s["x"].data_ptr(), s["dt"].data_ptr(), A_d.data_ptr(),
