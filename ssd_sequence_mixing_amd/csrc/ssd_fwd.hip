@@ -1016,14 +1016,29 @@ static __global__ __launch_bounds__(256) void k_seg_scan(float *__restrict__ seg
     const int e = (int)(v - bhi * per);
     const float *cs = cs2 + bhi * Tpad;
     f32x4 *base = reinterpret_cast<f32x4 *>(seg + bhi * (int64_t)(S - 1) * PN) + e;
+    const int64_t stride = PN / 4;
     f32x4 E = base[0];
-    for (int s = 1; s < S - 1; ++s) {
-        float D = 0.f;
-        for (int c = s * cps; c < min((s + 1) * cps, nC); ++c) D += cs[c * Q + Q - 1];
-        const float a = fast_exp2(D);
-        f32x4 *slot = base + (int64_t)s * (PN / 4);
-        E = a * E + *slot;
-        *slot = E;
+    // four segments at a time: their states and total decays are loaded
+    // together, then chained (past the last segment a repeat, not stored)
+    for (int s0 = 1; s0 < S - 1; s0 += 4) {
+        f32x4 sl[4];
+        float D[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int s = min(s0 + k, S - 2);
+            sl[k] = base[(int64_t)s * stride];
+            float d = 0.f;
+#pragma unroll 8
+            for (int c = s * cps; c < min((s + 1) * cps, nC); ++c) d += cs[c * Q + Q - 1];
+            D[k] = d;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (s0 + k < S - 1) {
+                E = fast_exp2(D[k]) * E + sl[k];
+                base[(int64_t)(s0 + k) * stride] = E;
+            }
+        }
     }
 }
 
