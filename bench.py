@@ -17,7 +17,8 @@ The other measurements run before the forward's, in this order: 50 forwards
 with the fused layer prologue / epilogue (ssd_chunk_scan_fwd_fused), 20
 backward passes (ssd_chunk_scan_bwd) of the forward workload (and 5 of the
 16K-token one), the 125M-layer and 16K-token forwards (timed like the main
-one, fewer steps, under "shapes") and 1000 ssd_step calls on the
+one after 20 warmup steps, with a quarter of the steps, under "shapes") and
+1000 ssd_step calls on the
 256 x 64 x 64 x 128 fp32 state (decode). Every input is made before the first
 of them, so the GPU work runs back to back, and the forward comes last,
 straight after the decode steps: from an idle GPU the same forward takes ~10%
@@ -501,7 +502,7 @@ def main():
         for name in shape_names:
             c2 = si.CONFIGS[name]
             s2 = shape_sets[name]
-            tm2 = time_forward(s2, max(10, K // 4), 5, args.repeats)
+            tm2 = time_forward(s2, max(10, K // 4), 20, args.repeats)
             _, summ = shape_summary(c2, c2.chunk, tm2)
             summ["workload"] = WORKLOAD_NAMES[name]
             summ["config"] = {"batch": c2.batch, "seqlen": c2.seqlen, "nheads": c2.nheads, "headdim": c2.headdim,
